@@ -1,0 +1,190 @@
+"""Double-precision CPU oracle of the speculative-sampling verify step.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the library or its binding.  The C
+source (``specverify_oracle.c``) shares no code with the HIP path; this module
+only marshals numpy arrays into it with ctypes.
+
+What each function follows is cited in the C source.  Every function here is
+pinned by ``tests/test_oracle_pins.py`` except the zero-residual-mass fallback,
+which is "parity unpinned" (it can only be reached through rounding).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "specverify_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+ACCEPT = 0
+BONUS = 1
+
+ERR_TOKEN = 1
+ERR_TEMPERATURE = 2
+ERR_ROW = 4
+ERR_DRAFT_MASS = 8
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (strict IEEE double, OpenMP over sequences)."""
+    cmd = [
+        "gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+        "-fPIC", "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, u32, u64, f64 = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_uniform.argtypes = [u64, u32, u32, u32]
+    lib.oracle_uniform.restype = f64
+    lib.oracle_row_max.argtypes = [P, i32, i32]
+    lib.oracle_row_max.restype = f64
+    lib.oracle_row_argmax.argtypes = [P, i32, i32]
+    lib.oracle_row_argmax.restype = i32
+    lib.oracle_row_lognorm.argtypes = [P, i32, i32, f64]
+    lib.oracle_row_lognorm.restype = f64
+    lib.oracle_row_top4.argtypes = [P, i32, i32, P]
+    lib.oracle_row_top4.restype = i32
+    lib.oracle_draft_logprobs.argtypes = [P, i32, i32, f64, f64, P]
+    lib.oracle_draft_logprobs.restype = i32
+    lib.oracle_spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f64,
+                                       P, P, P, P, P, P, P, P, i32]
+    lib.oracle_spec_verify.restype = i32
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_raw(logits: np.ndarray) -> tuple[np.ndarray, int]:
+    """Accept float32 arrays, or uint16 arrays holding bf16 bit patterns."""
+    if logits.dtype == np.float32:
+        return np.ascontiguousarray(logits), F32
+    if logits.dtype == np.uint16:
+        return np.ascontiguousarray(logits), BF16
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {logits.dtype}")
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    lib = _load()
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.zeros(4, dtype=np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform(seed: int, b: int, pos: int, purpose: int) -> float:
+    return float(_load().oracle_uniform(seed, b, pos, purpose))
+
+
+def row_max(row: np.ndarray) -> float:
+    raw, dt = _as_raw(row)
+    return float(_load().oracle_row_max(_ptr(raw), dt, raw.shape[-1]))
+
+
+def row_argmax(row: np.ndarray) -> int:
+    raw, dt = _as_raw(row)
+    return int(_load().oracle_row_argmax(_ptr(raw), dt, raw.shape[-1]))
+
+
+def row_lognorm(row: np.ndarray, T: float) -> float:
+    """log sum_v exp(z_v / T)."""
+    raw, dt = _as_raw(row)
+    return float(_load().oracle_row_lognorm(_ptr(raw), dt, raw.shape[-1], float(T)))
+
+
+def row_top4(row: np.ndarray) -> list[int]:
+    raw, dt = _as_raw(row)
+    idx = np.zeros(4, dtype=np.int32)
+    n = _load().oracle_row_top4(_ptr(raw), dt, raw.shape[-1], _ptr(idx))
+    return [int(i) for i in idx[:n]]
+
+
+def draft_logprobs(row: np.ndarray, T: float, beta: float) -> np.ndarray:
+    raw, dt = _as_raw(row)
+    out = np.zeros(raw.shape[-1], dtype=np.float64)
+    err = _load().oracle_draft_logprobs(_ptr(raw), dt, raw.shape[-1], float(T), float(beta),
+                                        _ptr(out))
+    if err:
+        raise ValueError(f"oracle_draft_logprobs error bits {err}")
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray, seed: int,
+                temperature, beta: float = 1.0, nthreads: int = 0) -> dict:
+    """Run the oracle on a whole batch.
+
+    target: [B, K+1, V] float32 or uint16 (bf16 bits); draft: [B, K, V] same
+    dtype, or None when every temperature is 0; tokens: [B, K] int32;
+    temperature: scalar or [B] float32.  Returns a dict of numpy arrays:
+    accepted_len [B], out_tokens [B, K+1], p_target / p_draft / margin_accept
+    [B, K], residual_mass / margin_bonus / seq_error [B], and error (int).
+    """
+    lib = _load()
+    t_raw, dt = _as_raw(target)
+    B, K1, V = t_raw.shape
+    K = K1 - 1
+    if draft is not None:
+        d_raw, dt2 = _as_raw(draft)
+        assert dt2 == dt and d_raw.shape == (B, K, V)
+    else:
+        d_raw = None
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    assert tok.shape == (B, K)
+    temp = np.asarray(temperature, dtype=np.float32)
+    if temp.ndim == 0:
+        temp = np.full(B, temp, dtype=np.float32)
+    temp = np.ascontiguousarray(temp)
+    assert temp.shape == (B,)
+    res = {
+        "accepted_len": np.zeros(B, dtype=np.int32),
+        "out_tokens": np.zeros((B, K + 1), dtype=np.int32),
+        "p_target": np.zeros((B, K), dtype=np.float64),
+        "p_draft": np.zeros((B, K), dtype=np.float64),
+        "residual_mass": np.zeros(B, dtype=np.float64),
+        "margin_accept": np.zeros((B, K), dtype=np.float64),
+        "margin_bonus": np.zeros(B, dtype=np.float64),
+        "seq_error": np.zeros(B, dtype=np.int32),
+    }
+    err = lib.oracle_spec_verify(
+        _ptr(t_raw), _ptr(d_raw), _ptr(tok), B, K, V, dt, int(seed) & (2**64 - 1), _ptr(temp),
+        float(beta), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["p_target"]),
+        _ptr(res["p_draft"]), _ptr(res["residual_mass"]), _ptr(res["margin_accept"]),
+        _ptr(res["margin_bonus"]), _ptr(res["seq_error"]), int(nthreads))
+    res["error"] = int(err)
+    return res

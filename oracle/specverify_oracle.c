@@ -1,0 +1,477 @@
+/*
+ * specverify_oracle.c -- plain, slow, double-precision CPU oracle of the
+ * speculative-sampling verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header or constant table with the HIP
+ * library: every step below is written out again from the method's definition.
+ *
+ * Sources (cited by page title and section):
+ *  - "Kangaroo: Self-Speculative Decoding via Shallow Sub-Networks",
+ *    section "3. Lossless Speculative Verification": accept draft token x_i
+ *    when a uniform r satisfies r <= min(1, p_i/q_i); at the first rejection
+ *    emit a sample of max(0, p_i - q_i) normalised over the vocabulary and
+ *    stop.  Its simulation listing counts one guaranteed extra (bonus) token.
+ *  - glossary "speculative decoding llm", sections "How Speculative Decoding
+ *    Works" and "Why It Produces Identical Outputs": same accept rule and
+ *    residual; the output law equals the target's.
+ *  - "Speculative Speculative Decoding", sections "Key claims" and "Method":
+ *    the bonus token comes from the residual max(p_t - p_d, 0); Saguaro
+ *    down-weights the most likely draft probabilities by a factor beta.
+ *  - "LayerSkip Guide: Early Exit & Self-Speculative Decoding", section
+ *    "2. The Drafting and Single-Pass Verification Pipeline": greedy mode
+ *    accepts drafts while they equal the target argmax, then emits the
+ *    target argmax.
+ *  - Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:
+ *    As Easy as 1, 2, 3", SC'11 (a published counter-based generator; the
+ *    pages only ask for reproducible uniforms).
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - accept iff u <= ratio (inclusive); u in (0,1] with 2^-24 resolution;
+ *  - the bonus after acceptance of all K drafts is drawn from target row K;
+ *  - the residual is clamped at zero; if its mass is exactly zero the bonus
+ *    is drawn from the target row of that position instead;
+ *  - inverse CDF in ascending token id: smallest v with C(v) >= u * Z;
+ *  - greedy ties go to the lowest token id;
+ *  - both softmaxes use the same per-sequence temperature T; T == 0 is greedy;
+ *  - beta multiplies the probabilities of the 4 largest draft logits (ties by
+ *    lower token id) and the draft law is renormalised; beta == 1 is off;
+ *  - a draft token outside [0, V) is rejected (ratio 0) and flagged.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_BF16 1
+
+#define OR_ACCEPT 0u
+#define OR_BONUS 1u
+
+#define OR_ERR_TOKEN 1       /* a draft token outside [0, V)              */
+#define OR_ERR_TEMPERATURE 2 /* T < 0, NaN or infinite                    */
+#define OR_ERR_ROW 4         /* a row whose maximum logit is not finite   */
+#define OR_ERR_DRAFT_MASS 8  /* beta re-weighting left zero draft mass    */
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (SC'11): 10 rounds of a multiply/xor S-box; the 2-word key
+ * advances by the Weyl constants before every round after the first.       */
+
+static void or_philox_round(uint32_t c[4], const uint32_t k[2])
+{
+    uint64_t prod0 = (uint64_t)0xD2511F53u * (uint64_t)c[0];
+    uint64_t prod1 = (uint64_t)0xCD9E8D57u * (uint64_t)c[2];
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c[1] ^ k[0];
+    uint32_t n2 = hi0 ^ c[3] ^ k[1];
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k[2] = {key[0], key[1]};
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k[0] += 0x9E3779B9u;
+            k[1] += 0xBB67AE85u;
+        }
+        or_philox_round(c, k);
+    }
+    out[0] = c[0];
+    out[1] = c[1];
+    out[2] = c[2];
+    out[3] = c[3];
+}
+
+/* Uniform keyed by (seed, sequence, position, purpose): key = seed split into
+ * low/high words, counter = (b, pos, purpose, 0), first output word mapped to
+ * ((w >> 8) + 1) * 2^-24, which lies in (0, 1] and is exact in float.      */
+double oracle_uniform(uint64_t seed, uint32_t b, uint32_t pos, uint32_t purpose)
+{
+    uint32_t ctr[4] = {b, pos, purpose, 0u};
+    uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return (double)((out[0] >> 8) + 1u) * (1.0 / 16777216.0);
+}
+
+/* ------------------------------------------------------------------ */
+/* Reading logits: bf16 and fp32 both convert to double exactly.             */
+
+static double or_logit(const void *base, int dtype, size_t idx)
+{
+    if (dtype == OR_F32) {
+        return (double)((const float *)base)[idx];
+    }
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Largest logit of a row (plain scan). */
+double oracle_row_max(const void *row, int dtype, int32_t V)
+{
+    double m = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+        double z = or_logit(row, dtype, (size_t)v);
+        if (z > m) m = z;
+    }
+    return m;
+}
+
+/* Index of the largest logit, lowest index on ties. */
+int32_t oracle_row_argmax(const void *row, int dtype, int32_t V)
+{
+    int32_t best = 0;
+    double bestz = or_logit(row, dtype, 0);
+    for (int32_t v = 1; v < V; ++v) {
+        double z = or_logit(row, dtype, (size_t)v);
+        if (z > bestz) {
+            bestz = z;
+            best = v;
+        }
+    }
+    return best;
+}
+
+/* L = log sum_v exp(z_v / T): the normaliser of softmax(z / T).
+ * ln p(v) = z_v / T - L.                                                     */
+double oracle_row_lognorm(const void *row, int dtype, int32_t V, double T)
+{
+    double m = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+        double a = or_logit(row, dtype, (size_t)v) / T;
+        if (a > m) m = a;
+    }
+    double s = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+        double a = or_logit(row, dtype, (size_t)v) / T;
+        s += exp(a - m);
+    }
+    return m + log(s);
+}
+
+/* The min(4, V) largest logits of a row, ordered by (logit descending,
+ * index ascending).  Plain repeated selection.                              */
+int32_t oracle_row_top4(const void *row, int dtype, int32_t V, int32_t idx[4])
+{
+    int32_t count = V < 4 ? V : 4;
+    for (int32_t j = 0; j < count; ++j) {
+        int32_t best = -1;
+        double bestz = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            int taken = 0;
+            for (int32_t q = 0; q < j; ++q)
+                if (idx[q] == v) taken = 1;
+            if (taken) continue;
+            double z = or_logit(row, dtype, (size_t)v);
+            if (best < 0 || z > bestz) {
+                best = v;
+                bestz = z;
+            }
+        }
+        idx[j] = best;
+    }
+    for (int32_t j = count; j < 4; ++j) idx[j] = -1;
+    return count;
+}
+
+/* A prepared row: its normaliser and, for a beta-weighted draft row, the
+ * down-weighted tokens and the renormalisation log N.                       */
+typedef struct {
+    const void *z;
+    int dtype;
+    int32_t V;
+    double T;
+    double L;          /* log sum exp(z / T)                                  */
+    int weighted;      /* beta re-weighting active                            */
+    double beta;
+    int32_t top[4];    /* down-weighted tokens                                */
+    int32_t ntop;
+    double logN;       /* log sum_v w(v) p(v)                                 */
+} or_row;
+
+static double or_weight(const or_row *r, int32_t v)
+{
+    if (!r->weighted) return 1.0;
+    for (int32_t j = 0; j < r->ntop; ++j)
+        if (r->top[j] == v) return r->beta;
+    return 1.0;
+}
+
+/* ln p(v) for a prepared row; for a weighted draft row this is
+ * ln w(v) + ln p(v) - ln N  (w(v) = beta on the top tokens, 1 elsewhere).   */
+static double or_logprob(const or_row *r, int32_t v)
+{
+    double lp = or_logit(r->z, r->dtype, (size_t)v) / r->T - r->L;
+    if (r->weighted) {
+        double w = or_weight(r, v);
+        lp += log(w) - r->logN; /* log(0) = -inf for beta == 0 */
+    }
+    return lp;
+}
+
+static int or_prepare(or_row *r, const void *z, int dtype, int32_t V, double T, int weighted,
+                      double beta)
+{
+    r->z = z;
+    r->dtype = dtype;
+    r->V = V;
+    r->T = T;
+    r->weighted = weighted;
+    r->beta = beta;
+    r->ntop = 0;
+    r->logN = 0.0;
+    double m = oracle_row_max(z, dtype, V);
+    if (!isfinite(m)) return OR_ERR_ROW;
+    r->L = oracle_row_lognorm(z, dtype, V, T);
+    if (weighted) {
+        r->ntop = oracle_row_top4(z, dtype, V, r->top);
+        /* N = sum_v w(v) p(v), summed over the whole vocabulary. */
+        double N = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            double p = exp(or_logit(z, dtype, (size_t)v) / T - r->L);
+            N += or_weight(r, v) * p;
+        }
+        if (!(N > 0.0)) return OR_ERR_DRAFT_MASS;
+        r->logN = log(N);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Full verify step for one sequence.                                        */
+
+typedef struct {
+    const void *target;   /* [B, K+1, V] */
+    const void *draft;    /* [B, K, V] (may be NULL when every T == 0) */
+    const int32_t *tokens;/* [B, K] */
+    int32_t B, K, V;
+    int dtype;
+    uint64_t seed;
+    const float *temperature; /* [B] */
+    double beta;
+    int32_t *accepted_len;    /* [B] */
+    int32_t *out_tokens;      /* [B, K+1] */
+    double *p_target;         /* [B, K]   or NULL */
+    double *p_draft;          /* [B, K]   or NULL */
+    double *residual_mass;    /* [B]      or NULL */
+    double *margin_accept;    /* [B, K]   or NULL */
+    double *margin_bonus;     /* [B]      or NULL */
+    int32_t *seq_error;       /* [B]      or NULL */
+} or_call;
+
+static const void *or_row_ptr(const void *base, int dtype, size_t row, int32_t V)
+{
+    size_t elt = dtype == OR_F32 ? 4u : 2u;
+    return (const char *)base + row * (size_t)V * elt;
+}
+
+static void or_fail_sequence(const or_call *c, int32_t b)
+{
+    c->accepted_len[b] = 0;
+    for (int32_t j = 0; j <= c->K; ++j) c->out_tokens[(size_t)b * (c->K + 1) + j] = -1;
+}
+
+static int or_verify_sequence(const or_call *c, int32_t b)
+{
+    const int32_t K = c->K, V = c->V;
+    int err = 0;
+    int32_t *out = c->out_tokens + (size_t)b * (K + 1);
+    const int32_t *x = c->tokens + (size_t)b * K;
+    const double nan = NAN;
+
+    for (int32_t j = 0; j <= K; ++j) out[j] = -1;
+    for (int32_t i = 0; i < K; ++i) {
+        if (c->p_target) c->p_target[(size_t)b * K + i] = nan;
+        if (c->p_draft) c->p_draft[(size_t)b * K + i] = nan;
+        if (c->margin_accept) c->margin_accept[(size_t)b * K + i] = nan;
+    }
+    if (c->residual_mass) c->residual_mass[b] = nan;
+    if (c->margin_bonus) c->margin_bonus[b] = nan;
+
+    double T = (double)c->temperature[b];
+    if (!(T >= 0.0) || isinf(T)) {
+        or_fail_sequence(c, b);
+        return OR_ERR_TEMPERATURE;
+    }
+
+    if (T == 0.0) {
+        /* Greedy: accept while the draft equals the target argmax; the first
+         * mismatch (or position K) emits the target argmax.                 */
+        int32_t n = K;
+        for (int32_t i = 0; i <= K; ++i) {
+            const void *row = or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + i, V);
+            if (!isfinite(oracle_row_max(row, c->dtype, V))) {
+                or_fail_sequence(c, b);
+                return err | OR_ERR_ROW;
+            }
+            int32_t a = oracle_row_argmax(row, c->dtype, V);
+            if (i < K && x[i] == a) {
+                out[i] = x[i];
+                continue;
+            }
+            if (i < K && (x[i] < 0 || x[i] >= V)) err |= OR_ERR_TOKEN;
+            out[i] = a;
+            n = i;
+            break;
+        }
+        c->accepted_len[b] = n;
+        return err;
+    }
+
+    /* Sampling: accept x_i iff u_i <= ratio_i = p_t(x_i) / p_d'(x_i). */
+    int weighted = c->beta < 1.0;
+    int32_t n = K;
+    or_row rt, rd;
+    for (int32_t i = 0; i < K; ++i) {
+        int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + i, V),
+                           c->dtype, V, T, 0, 1.0);
+        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * K + i, V), c->dtype, V,
+                        T, weighted, c->beta);
+        if (e) {
+            or_fail_sequence(c, b);
+            return err | e;
+        }
+        double ratio;
+        if (x[i] < 0 || x[i] >= V) {
+            err |= OR_ERR_TOKEN;
+            ratio = 0.0;
+        } else {
+            double lpt = or_logprob(&rt, x[i]);
+            double lpd = or_logprob(&rd, x[i]);
+            if (c->p_target) c->p_target[(size_t)b * K + i] = exp(lpt);
+            if (c->p_draft) c->p_draft[(size_t)b * K + i] = exp(lpd);
+            /* a draft token the draft law gives zero mass cannot be rejected */
+            ratio = (lpd == -INFINITY) ? INFINITY : exp(lpt - lpd);
+        }
+        double u = oracle_uniform(c->seed, (uint32_t)b, (uint32_t)i, OR_ACCEPT);
+        if (c->margin_accept) c->margin_accept[(size_t)b * K + i] = fabs(u - ratio);
+        if (u <= ratio) {
+            out[i] = x[i];
+            continue;
+        }
+        n = i;
+        break;
+    }
+
+    /* Residual law at position n: max(p_t - p_d', 0) after a rejection,
+     * the target row K itself after K acceptances.                        */
+    int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + n, V), c->dtype,
+                       V, T, 0, 1.0);
+    if (n < K)
+        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * K + n, V), c->dtype, V, T,
+                        weighted, c->beta);
+    if (e) {
+        or_fail_sequence(c, b);
+        return err | e;
+    }
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    double Z = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+        double pt = exp(or_logprob(&rt, v));
+        r[v] = pt;
+        if (n < K) {
+            double d = pt - exp(or_logprob(&rd, v));
+            r[v] = d > 0.0 ? d : 0.0;
+        }
+        Z += r[v];
+    }
+    if (Z == 0.0) {
+        /* zero residual mass can only come from rounding: use p_t instead */
+        Z = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            r[v] = exp(or_logprob(&rt, v));
+            Z += r[v];
+        }
+    }
+    /* Inverse CDF over ascending token ids: smallest v with C(v) >= u Z.
+     * C is the same running sum that produced Z, so C(V-1) == Z.          */
+    double uB = oracle_uniform(c->seed, (uint32_t)b, (uint32_t)n, OR_BONUS);
+    double thr = uB * Z;
+    double C = 0.0, Cprev = 0.0;
+    int32_t bonus = -1;
+    for (int32_t v = 0; v < V; ++v) {
+        Cprev = C;
+        C += r[v];
+        if (C >= thr) {
+            bonus = v;
+            break;
+        }
+    }
+    if (bonus < 0) { /* unreachable: C(V-1) == Z >= u Z */
+        for (int32_t v = V - 1; v >= 0; --v)
+            if (r[v] > 0.0) {
+                bonus = v;
+                break;
+            }
+        C = Z;
+    }
+    free(r);
+    out[n] = bonus;
+    c->accepted_len[b] = n;
+    if (c->residual_mass) c->residual_mass[b] = Z;
+    if (c->margin_bonus) {
+        double m1 = fabs(uB - Cprev / Z), m2 = fabs(uB - C / Z);
+        c->margin_bonus[b] = m1 < m2 ? m1 : m2;
+    }
+    return err;
+}
+
+/* Verify every sequence of a batch.  Returns the OR of the error bits.
+ * nthreads <= 0 uses the OpenMP default; sequences are independent, so the
+ * result does not depend on the thread count.                              */
+int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t *tokens,
+                           int32_t B, int32_t K, int32_t V, int32_t dtype, uint64_t seed,
+                           const float *temperature, double beta, int32_t *accepted_len,
+                           int32_t *out_tokens, double *p_target, double *p_draft,
+                           double *residual_mass, double *margin_accept, double *margin_bonus,
+                           int32_t *seq_error, int32_t nthreads)
+{
+    or_call c = {target, draft, tokens, B, K, V, dtype, seed, temperature, beta,
+                 accepted_len, out_tokens, p_target, p_draft, residual_mass,
+                 margin_accept, margin_bonus, seq_error};
+    int32_t all_err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : all_err)
+#endif
+    for (int32_t b = 0; b < B; ++b) {
+        int e = or_verify_sequence(&c, b);
+        if (seq_error) seq_error[b] = e;
+        all_err |= e;
+    }
+    return all_err;
+}
+
+/* Full draft log-law ln p_d'(v) of one row (for invariant checks). */
+int32_t oracle_draft_logprobs(const void *row, int32_t dtype, int32_t V, double T, double beta,
+                              double *out)
+{
+    or_row r;
+    int e = or_prepare(&r, row, dtype, V, T, beta < 1.0, beta);
+    if (e) return e;
+    for (int32_t v = 0; v < V; ++v) out[v] = or_logprob(&r, v);
+    return 0;
+}
+
+/* Number of threads an OpenMP parallel region would use by default. */
+int32_t oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
