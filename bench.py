@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-sampling verify step on one MI355X.
+
+A step is one spec_verify call (streaming pass, accept scan, residual and
+bonus draw) over one batch of synthetic logits already resident in HBM.  The
+input batch is replicated so that consecutive steps read different copies and
+the working set exceeds the 256 MB Infinity Cache: every step streams from HBM.
+
+Prints one JSON line:
+  value        verified logits per second, B*(K+1)*V per step / step time
+  roofline     algorithmic bytes per step / measured step time vs 8 TB/s
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MALL_BYTES = 256 * 2**20       # Infinity Cache
+DEFAULT_WORKLOAD = "C2"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("draft_token_verification_03_amd/csrc/specverify.hip",
+                "draft_token_verification_03_amd/csrc/sv_device.h", "include/specverify.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(tag: str) -> float | None:
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
+def cpu_baseline(inp, w, seconds: float) -> dict:
+    """Time the oracle as it stands on host cores over a bounded sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workload import to_numpy_inputs
+
+    nseq = min(w.B, 32)
+    ids = np.arange(nseq)
+    sub = {k: (v[:nseq] if torch.is_tensor(v) else v) for k, v in inp.items()}
+    h = to_numpy_inputs(sub)
+    if w.greedy:
+        h["draft"] = None
+    threads = max(1, min(len(os.sched_getaffinity(0)), oracle.max_threads()))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.spec_verify(h["target"], h["draft"], h["tokens"], 0, h["temperature"], h["beta"],
+                           nthreads=threads, seq_ids=ids)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or calls >= 1000:
+            break
+    logits = calls * nseq * (w.K + 1) * w.V
+    return {"value": logits / el, "unit": "logits/s", "cores": min(threads, nseq),
+            "kind": "oracle",
+            "sample": f"{nseq} of {w.B} sequences of {w.tag()}, {calls} calls in {el:.1f} s, "
+                      f"OpenMP over sequences with {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="instead, run torch copies of MB megabytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verify step is data-parallel over sequences and "
+              "this build runs on a single MI355X (see the sharding notes in DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import draft_token_verification_03_amd as sv
+    from workload import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "calls": args.steps}))
+        return 0
+
+    sv.load_library()
+    w = WORKLOADS[args.workload]
+    print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
+    base = make_inputs(w, seed=args.seed, device=dev)
+    alg_bytes = w.algorithmic_bytes()
+    reps = max(1, math.ceil(2 * MALL_BYTES / alg_bytes))
+    replicas = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                         for _ in range(reps - 1)]
+    draft_arg = [None if w.greedy else r["draft"] for r in replicas]
+    ws = sv.alloc_workspace(w.B, w.K, w.V, base["target"].dtype, dev)
+    acc = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(k: int) -> None:
+        r = replicas[k % reps]
+        sv.spec_verify(r["target"], draft_arg[k % reps], r["tokens"], args.seed + k,
+                       r["temperature"], r["beta"], workspace=ws, accepted_len=acc,
+                       out_tokens=out, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        step(args.warmup + k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    mean_acc = float(acc.float().mean().item())
+
+    logits_per_step = w.B * (w.K + 1) * w.V
+    value = logits_per_step / (ms * 1e-3)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    rec = {
+        "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
+        "value": value,
+        "unit": "logits/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.tag(), "B": w.B, "K": w.K, "V": w.V,
+                   "temperature": w.temperature if w.temperature is not None
+                   else f"U[{w.t_lo},{w.t_hi}] per sequence",
+                   "beta": w.beta, "replicas_rotated": reps,
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "rows_per_s": w.B * (w.K + 1) / (ms * 1e-3),
+                   "sequences_per_s": w.B / (ms * 1e-3),
+                   "mean_accepted_len": mean_acc,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "scope": "whole verify step (all launches of one call) per step time"},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(base, w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

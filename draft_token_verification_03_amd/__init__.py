@@ -1,0 +1,198 @@
+"""Python binding of libspecverify, the speculative-sampling verify step for
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the verify step runs in the HIP
+kernels of ``libspecverify.so`` (built in-tree by ``build.py``).  PyTorch is
+used for device memory and the current stream.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_F32 = 0
+SV_BF16 = 1
+SV_OK = 0
+SV_EINVAL = -1
+SV_EWORKSPACE = -2
+SV_EHIP = -3
+
+SV_ERR_TOKEN = 1
+SV_ERR_TEMPERATURE = 2
+SV_ERR_ROW = 4
+SV_ERR_DRAFT_MASS = 8
+SV_ERR_NO_DRAFT = 16
+
+EXPORTED = ("spec_verify", "spec_verify_workspace_size", "spec_verify_row_stats",
+            "spec_verify_uniforms", "spec_verify_status_str")
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+class _Aux(ctypes.Structure):
+    _fields_ = [("p_target", ctypes.c_void_p), ("p_draft", ctypes.c_void_p),
+                ("residual_mass", ctypes.c_void_p), ("error_word", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SpecVerifyError(
+            f"{path} is missing: build it with `python -m draft_token_verification_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_workspace_size.restype = sz
+    lib.spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f32, P, P, P, sz,
+                                ctypes.POINTER(_Aux), P]
+    lib.spec_verify.restype = i32
+    lib.spec_verify_row_stats.argtypes = [P, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.spec_verify_row_stats.restype = i32
+    lib.spec_verify_uniforms.argtypes = [u64, i32, i32, P, P]
+    lib.spec_verify_uniforms.restype = i32
+    lib.spec_verify_status_str.argtypes = [i32]
+    lib.spec_verify_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().spec_verify_status_str(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != SV_OK:
+        raise SpecVerifyError(status_str(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace_size(B: int, K: int, V: int, dtype: torch.dtype) -> int:
+    code = SV_F32 if dtype == torch.float32 else SV_BF16
+    return int(load_library().spec_verify_workspace_size(B, K, V, code))
+
+
+def alloc_workspace(B: int, K: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
+    n = workspace_size(B, K, V, dtype)
+    if n == 0:
+        raise SpecVerifyError("invalid sizes for a workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
+                seed: int, temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
+                accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
+                aux: bool = False, stream=None):
+    """Verify K drafted tokens per sequence.
+
+    target [B, K+1, V] and draft [B, K, V] (or None if every temperature is 0)
+    are float32 or bfloat16 CUDA tensors; tokens [B, K] int32; temperature a
+    float or a [B] float32 tensor (0 = greedy); beta in [0, 1].  Returns
+    (accepted_len [B] int32, out_tokens [B, K+1] int32), plus a dict of
+    diagnostics (p_target, p_draft, residual_mass, error_word) if aux=True.
+    The work is enqueued on `stream` (default: the current stream).
+    """
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    if not target.is_contiguous():
+        raise ValueError("target must be contiguous")
+    if draft is not None:
+        if draft.shape != (B, K, V) or draft.dtype != target.dtype or not draft.is_contiguous():
+            raise ValueError("draft must be a contiguous [B, K, V] tensor of the target's dtype")
+    if tokens.shape != (B, K) or tokens.dtype != torch.int32 or not tokens.is_contiguous():
+        raise ValueError("tokens must be a contiguous [B, K] int32 tensor")
+    if not torch.is_tensor(temperature):
+        temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
+    if temperature.shape != (B,) or temperature.dtype != torch.float32:
+        raise ValueError("temperature must be a [B] float32 tensor")
+    temperature = temperature.contiguous()
+    if workspace is None:
+        workspace = alloc_workspace(B, K, V, target.dtype, dev)
+    if accepted_len is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    aux_t = None
+    aux_s = None
+    if aux:
+        aux_t = {
+            "p_target": torch.empty((B, K), dtype=torch.float32, device=dev),
+            "p_draft": torch.empty((B, K), dtype=torch.float32, device=dev),
+            "residual_mass": torch.empty((B,), dtype=torch.float32, device=dev),
+            "error_word": torch.empty((1,), dtype=torch.int32, device=dev),
+        }
+        aux_s = _Aux(aux_t["p_target"].data_ptr(), aux_t["p_draft"].data_ptr(),
+                     aux_t["residual_mass"].data_ptr(), aux_t["error_word"].data_ptr())
+    status = load_library().spec_verify(
+        _ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code, int(seed) & (2**64 - 1),
+        _ptr(temperature), float(beta), _ptr(accepted_len), _ptr(out_tokens), _ptr(workspace),
+        workspace.numel(), ctypes.byref(aux_s) if aux_s is not None else None, _stream(stream))
+    _check(status)
+    if aux:
+        return accepted_len, out_tokens, aux_t
+    return accepted_len, out_tokens
+
+
+def row_stats(logits: torch.Tensor, temperature, *, stream=None):
+    """Streaming-pass statistics of each row of a [rows, V] tensor:
+    (max [rows] f32, ln sum exp((z - max)/T) [rows] f64, argmax [rows] i32);
+    rows with T == 0 get the argmax and a NaN log-sum."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, V] tensor")
+    rows, V = logits.shape
+    dev = logits.device
+    code = _dtype_code(logits)
+    if not torch.is_tensor(temperature):
+        temperature = torch.full((rows,), float(temperature), dtype=torch.float32, device=dev)
+    temperature = temperature.contiguous()
+    ws = alloc_workspace(max(rows, 1), 0, V, logits.dtype, dev)
+    mx = torch.empty(rows, dtype=torch.float32, device=dev)
+    ls = torch.empty(rows, dtype=torch.float64, device=dev)
+    am = torch.empty(rows, dtype=torch.int32, device=dev)
+    _check(load_library().spec_verify_row_stats(
+        _ptr(logits), rows, V, code, _ptr(temperature), _ptr(mx), _ptr(ls), _ptr(am), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return mx, ls, am
+
+
+def uniforms(seed: int, B: int, P: int, *, device="cuda", stream=None) -> torch.Tensor:
+    """u(b, pos, purpose) as a [B, P, 2] float32 tensor."""
+    out = torch.empty((B, P, 2), dtype=torch.float32, device=device)
+    _check(load_library().spec_verify_uniforms(int(seed) & (2**64 - 1), B, P, _ptr(out),
+                                               _stream(stream)))
+    return out

@@ -1,0 +1,387 @@
+// sv_device.h -- device-side building blocks of libspecverify (gfx950, wave64).
+//
+// Private to the library: row loading, wave/block reductions and scans, the
+// top-4 selection and the Philox4x32-10 counter generator.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+namespace sv {
+
+constexpr int kBlock = 256;            // threads per workgroup: four wave64s
+constexpr int kWaves = kBlock / 64;
+constexpr int kLoads = 4;              // 16-byte loads in flight per thread per step
+constexpr double kLog2e = 1.4426950408889634;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds, each
+// multiplying words 0 and 2 by fixed 32-bit constants (keeping both halves of
+// the 64-bit products) and xoring the high halves into words 1 and 3 together
+// with the key; the key advances by two Weyl increments between rounds.
+
+__device__ __forceinline__ uint32_t philox_word0(uint64_t seed, uint32_t c0, uint32_t c1,
+                                                 uint32_t c2, uint32_t c3)
+{
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo_a = 0xD2511F53u * c0, hi_a = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo_b = 0xCD9E8D57u * c2, hi_b = __umulhi(0xCD9E8D57u, c2);
+        c0 = hi_b ^ c1 ^ k0;
+        c1 = lo_b;
+        c2 = hi_a ^ c3 ^ k1;
+        c3 = lo_a;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+// Uniform in (0, 1] on a 2^-24 grid (exact in float) for counter (b, pos, purpose, 0).
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t b, uint32_t pos,
+                                                uint32_t purpose)
+{
+    const uint32_t w = philox_word0(seed, b, pos, purpose, 0u);
+    return (float)((w >> 8) + 1u) * 0x1p-24f;
+}
+
+// ---------------------------------------------------------------------------
+// Row loading.  A row of V logits is read as 16-byte vectors; vector q holds
+// elements [q*VEC, q*VEC + VEC).  The element-to-lane mapping depends only on
+// the element index, never on the row's address, so two rows with equal
+// values give bitwise-equal reductions wherever they sit in memory.
+
+template <int DT> struct Elt;
+template <> struct Elt<0> {  // fp32
+    static constexpr int kVec = 4;
+    static constexpr int kBytes = 4;
+    __device__ static __forceinline__ void unpack(uint4 r, float (&x)[4])
+    {
+        x[0] = __uint_as_float(r.x);
+        x[1] = __uint_as_float(r.y);
+        x[2] = __uint_as_float(r.z);
+        x[3] = __uint_as_float(r.w);
+    }
+    __device__ static __forceinline__ float scalar(const char *row, int64_t v)
+    {
+        return reinterpret_cast<const float *>(row)[v];
+    }
+};
+template <> struct Elt<1> {  // bf16: the upper 16 bits of a float
+    static constexpr int kVec = 8;
+    static constexpr int kBytes = 2;
+    __device__ static __forceinline__ void unpack(uint4 r, float (&x)[8])
+    {
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xffff0000u);
+        x[4] = __uint_as_float(r.z << 16);
+        x[5] = __uint_as_float(r.z & 0xffff0000u);
+        x[6] = __uint_as_float(r.w << 16);
+        x[7] = __uint_as_float(r.w & 0xffff0000u);
+    }
+    __device__ static __forceinline__ float scalar(const char *row, int64_t v)
+    {
+        const uint32_t bits = (uint32_t)reinterpret_cast<const uint16_t *>(row)[v] << 16;
+        return __uint_as_float(bits);
+    }
+};
+
+__device__ __forceinline__ uint32_t funnel_bytes(uint32_t lo, uint32_t hi, uint32_t r)
+{
+    return (uint32_t)((((uint64_t)hi << 32) | lo) >> (8u * r));
+}
+
+template <int W>
+__device__ __forceinline__ uint4 pick4(const uint32_t (&d)[8], uint32_t r)
+{
+    return make_uint4(funnel_bytes(d[W], d[W + 1], r), funnel_bytes(d[W + 1], d[W + 2], r),
+                      funnel_bytes(d[W + 2], d[W + 3], r), funnel_bytes(d[W + 3], d[W + 4], r));
+}
+
+// 16 bytes starting at a non-16-aligned address p, from the two aligned
+// 16-byte blocks that hold them.  The second block is only read when it holds
+// valid bytes (`need_second`), so no read leaves the pages the row lives in.
+__device__ __noinline__ uint4 load16_unaligned(const char *p, bool need_second)
+{
+    const uintptr_t a = (uintptr_t)p;
+    const uint4 *blk = reinterpret_cast<const uint4 *>(a & ~(uintptr_t)15);
+    const uint32_t sh = (uint32_t)(a & 15);
+    const uint4 x = blk[0];
+    const uint4 y = need_second ? blk[1] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t d[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    const uint32_t r = sh & 3u;
+    switch (sh >> 2) {
+    case 0: return pick4<0>(d, r);
+    case 1: return pick4<1>(d, r);
+    case 2: return pick4<2>(d, r);
+    default: return pick4<3>(d, r);
+    }
+}
+
+// Vector q of a row as floats; elements at or beyond V are -inf.
+template <int DT>
+__device__ __forceinline__ void load_vec(const char *row, bool aligned, int q, int V,
+                                         float (&x)[Elt<DT>::kVec])
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    const char *p = row + (size_t)q * 16;
+    uint4 raw;
+    const int first = q * VEC;
+    if (aligned) {
+        raw = *reinterpret_cast<const uint4 *>(p);
+    } else {
+        const int valid = min(VEC, V - first);
+        const uint32_t sh = (uint32_t)((uintptr_t)p & 15);
+        raw = load16_unaligned(p, sh + (uint32_t)valid * Elt<DT>::kBytes > 16u);
+    }
+    Elt<DT>::unpack(raw, x);
+    if (first + VEC > V) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k)
+            if (first + k >= V) x[k] = -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Exponent scale log2(e)/T split as c_hi + c_lo: c_hi is rounded toward zero
+// so c_lo >= 0, and c_lo is kept strictly positive so that -inf logits give
+// exp2(-inf) = 0 and never 0 * inf.
+
+struct ExpScale {
+    float hi, lo;
+    double c64;
+};
+
+__device__ __forceinline__ ExpScale make_scale(float T)
+{
+    ExpScale e;
+    e.c64 = kLog2e / (double)T;
+    e.hi = __double2float_rz(e.c64);
+    e.lo = (float)(e.c64 - (double)e.hi);
+    if (!(e.lo > 0.f)) e.lo = 1e-30f;
+    return e;
+}
+
+// 2^((x - m) * log2(e) / T) with the product carried to ~2^-48 relative.
+__device__ __forceinline__ float exp_scaled(float x, float m, const ExpScale &e)
+{
+    const float d = x - m;
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(d, e.hi, d * e.lo));
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 and workgroup reductions (fixed trees, so results are reproducible).
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// (value desc, index asc) order used for argmax and top-4.
+__device__ __forceinline__ bool better(float v, int i, float w, int j)
+{
+    return v > w || (v == w && i < j);
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, int &i)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float w = __shfl_xor(v, o, 64);
+        const int j = __shfl_xor(i, o, 64);
+        if (better(w, j, v, i)) {
+            v = w;
+            i = j;
+        }
+    }
+}
+
+__device__ __forceinline__ float block_max(float v, float *lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v);
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, double *lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    double r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += lds[w];
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int *lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_min_int(v);
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    int r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = min(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int block_max_int(int v, int *lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max_int(v);
+    if (lane == 0) lds[wave] = v;
+    __syncthreads();
+    int r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = max(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ void block_argmax(float &v, int &i, float *ldsv, int *ldsi)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wave_argmax(v, i);
+    if (lane == 0) {
+        ldsv[wave] = v;
+        ldsi[wave] = i;
+    }
+    __syncthreads();
+    v = ldsv[0];
+    i = ldsi[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        if (better(ldsv[w], ldsi[w], v, i)) {
+            v = ldsv[w];
+            i = ldsi[w];
+        }
+    __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup in thread order; `total` receives
+// the sum of all values.
+__device__ __forceinline__ double block_exclusive_scan(double v, double &total, double *lds)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    double exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = 0.0;
+    if (lane == 63) lds[wave] = inc;
+    __syncthreads();
+    double off = 0.0;
+    for (int w = 0; w < wave; ++w) off += lds[w];
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += lds[w];
+    __syncthreads();
+    total = tot;
+    return off + exc;
+}
+
+// ---------------------------------------------------------------------------
+// Top-4 lists kept sorted by (value desc, index asc); empty slots are
+// (-inf, INT_MAX).
+
+struct Top4 {
+    float v[4];
+    int i[4];
+};
+
+__device__ __forceinline__ void top_clear(Top4 &t)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        t.v[k] = -INFINITY;
+        t.i[k] = INT_MAX;
+    }
+}
+
+__device__ __forceinline__ void top_insert(Top4 &t, float v, int i)
+{
+    if (!better(v, i, t.v[3], t.i[3])) return;
+    t.v[3] = v;
+    t.i[3] = i;
+#pragma unroll
+    for (int k = 3; k > 0; --k) {
+        if (better(t.v[k], t.i[k], t.v[k - 1], t.i[k - 1])) {
+            const float tv = t.v[k];
+            const int ti = t.i[k];
+            t.v[k] = t.v[k - 1];
+            t.i[k] = t.i[k - 1];
+            t.v[k - 1] = tv;
+            t.i[k - 1] = ti;
+        }
+    }
+}
+
+// Merge the per-lane lists of a wave into the wave's top-4 (every lane gets it).
+__device__ __forceinline__ Top4 wave_top4(Top4 t)
+{
+    Top4 out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = t.v[0];
+        int i = t.i[0];
+        wave_argmax(v, i);
+        out.v[r] = v;
+        out.i[r] = i;
+        if (t.v[0] == v && t.i[0] == i && i != INT_MAX) {  // pop the winner's head
+            t.v[0] = t.v[1];
+            t.i[0] = t.i[1];
+            t.v[1] = t.v[2];
+            t.i[1] = t.i[2];
+            t.v[2] = t.v[3];
+            t.i[2] = t.i[3];
+            t.v[3] = -INFINITY;
+            t.i[3] = INT_MAX;
+        }
+    }
+    return out;
+}
+
+}  // namespace sv

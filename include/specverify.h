@@ -1,0 +1,142 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the speculative-sampling verify
+ * step for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *  - "Kangaroo: Self-Speculative Decoding via Shallow Sub-Networks",
+ *    "3. Lossless Speculative Verification": draft token x_i is accepted when
+ *    a uniform u satisfies u <= min(1, p_i(x_i) / q_i(x_i)); at the first
+ *    rejection one token is drawn from max(0, p_i - q_i) normalised over the
+ *    vocabulary and verification stops.  The simulation listing on the same
+ *    page counts one guaranteed bonus token per verification.
+ *  - glossary "speculative decoding llm", "How Speculative Decoding Works" and
+ *    "Why It Produces Identical Outputs": the same rule, whose output law is
+ *    exactly the target model's.
+ *  - "Speculative Speculative Decoding", "Method": the verification outcome
+ *    is (accepted prefix length, bonus token); the bonus comes from the
+ *    residual max(p_t - p_d, 0); Saguaro sampling down-weights the most
+ *    likely draft probabilities by a factor beta.
+ *  - "LayerSkip Guide: Early Exit & Self-Speculative Decoding", "2. The
+ *    Drafting and Single-Pass Verification Pipeline": greedy verification
+ *    accepts drafts while they equal the target argmax and replaces the first
+ *    mismatch by the target argmax.
+ *
+ * Per sequence b with temperature T = temperature[b] and K drafted tokens
+ * x_i = draft_tokens[b, i]:
+ *   p_i = softmax(target_logits[b, i, :] / T)   for i = 0..K,
+ *   q_i = softmax(draft_logits[b, i, :] / T)    for i = 0..K-1; when beta < 1
+ *         the probabilities of the 4 largest draft logits of the row (ties to
+ *         the lower token id) are multiplied by beta and q_i is renormalised.
+ *   For i = 0, 1, ...: accept x_i iff u(b, i, 0) <= p_i(x_i) / q_i(x_i).
+ *   n = index of the first rejection, or K if all are accepted.
+ *   The bonus token is the smallest v with C(v) >= u(b, n, 1) * C(V-1), where
+ *   C is the running sum in ascending token id of r(v) = max(p_n - q_n, 0)
+ *   (n < K) or r(v) = p_K(v) (n == K).  If r has zero mass the bonus is drawn
+ *   from p_n the same way.
+ *   T == 0 selects greedy mode for that sequence: n = first i with
+ *   x_i != argmax p_i (lowest token id on ties), else K; the bonus is the
+ *   argmax of target row n; draft logits and beta are not used.
+ *   u(b, pos, purpose) = ((w >> 8) + 1) * 2^-24 in (0, 1], where w is the
+ *   first output word of Philox4x32-10 (Salmon et al., SC'11) with key
+ *   (seed & 0xffffffff, seed >> 32) and counter (b, pos, purpose, 0).
+ *
+ * Memory and ownership: every array argument is a DEVICE pointer owned by the
+ * caller, unless noted.  Arrays are dense and row-major.  Logits are fp32 or
+ * bf16 (dtype) and must be aligned to their element size.  Logits may hold
+ * -inf (masked tokens); every row that is used needs a finite maximum; NaN or
+ * +inf logits give unspecified results.  The library never allocates device
+ * memory and never synchronises: all work is enqueued on `stream` (a
+ * hipStream_t; NULL is the default stream) and results are ready when the
+ * stream is synchronised.  Calls are re-entrant; concurrent calls need
+ * distinct workspaces.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Logit element types. */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* Status codes returned synchronously by the host entry points. */
+#define SV_OK 0
+#define SV_EINVAL (-1)      /* an argument is invalid; nothing was enqueued     */
+#define SV_EWORKSPACE (-2)  /* workspace NULL, misaligned or too small         */
+#define SV_EHIP (-3)        /* the HIP runtime reported an error on launch     */
+
+/* Bits of the device-side error word (see sv_aux.error_word). */
+#define SV_ERR_TOKEN 1          /* a draft token outside [0, V): treated as rejected    */
+#define SV_ERR_TEMPERATURE 2    /* T < 0, NaN or infinite: sequence outputs are -1      */
+#define SV_ERR_ROW 4            /* a used row has no finite maximum: outputs are -1     */
+#define SV_ERR_DRAFT_MASS 8     /* beta == 0 left a draft row with zero mass: outputs -1 */
+#define SV_ERR_NO_DRAFT 16      /* T > 0 but draft_logits is NULL: outputs are -1       */
+
+/* Optional per-call diagnostics; every field may be NULL. */
+typedef struct sv_aux {
+    float *p_target;      /* [B, K] p_i(x_i) at evaluated positions, NaN elsewhere and in greedy mode */
+    float *p_draft;       /* [B, K] q_i(x_i) (beta-weighted) at evaluated positions, else NaN         */
+    float *residual_mass; /* [B]    C(V-1) of the bonus draw; NaN in greedy mode                      */
+    int32_t *error_word;  /* [1]    OR of SV_ERR_* bits; cleared by the call before it is set        */
+} sv_aux;
+
+/*
+ * Bytes of device workspace spec_verify needs for these sizes (0 if the sizes
+ * are invalid).  Pure host function.
+ */
+size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype);
+
+/*
+ * The verify step.
+ *   target_logits  [B, K+1, V] dtype
+ *   draft_logits   [B, K, V]   dtype; may be NULL when every temperature is 0
+ *   draft_tokens   [B, K]      int32; may be NULL when K == 0
+ *   temperature    [B]         float; 0 = greedy for that sequence
+ *   beta           host float in [0, 1]; 1 = no draft re-weighting
+ *   accepted_len   [B]         int32 out: n in [0, K]
+ *   out_tokens     [B, K+1]    int32 out: x_0..x_{n-1}, the bonus token, then -1
+ *   workspace      device buffer of >= spec_verify_workspace_size(...) bytes,
+ *                  256-byte aligned; its contents on entry do not matter
+ *   aux            host pointer to an sv_aux, or NULL
+ * B == 0 is a no-op.  Returns SV_OK after enqueuing the work.
+ */
+int32_t spec_verify(const void *target_logits, const void *draft_logits,
+                    const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                    uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
+                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    const sv_aux *aux, void *stream);
+
+/*
+ * Per-row statistics of `rows` rows of V logits (the streaming pass of the
+ * verify step on its own, for parity checks of the row reduction):
+ *   row_max[r]    = max_v z[r, v]
+ *   row_logsum[r] = ln sum_v exp((z[r, v] - row_max[r]) / temperature[r]) when
+ *                   temperature[r] > 0, else NaN
+ *   row_argmax[r] = lowest v attaining row_max[r] when temperature[r] == 0, else -1
+ * All output pointers are device pointers and may not be NULL.
+ * Workspace: >= spec_verify_workspace_size(rows, 0, V, dtype) bytes.
+ */
+int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,
+                              const float *temperature, float *row_max, double *row_logsum,
+                              int32_t *row_argmax, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * The uniforms the verify step draws: out[(b * P + pos) * 2 + purpose] =
+ * u(b, pos, purpose) for b < B, pos < P, purpose in {0 (accept), 1 (bonus)}.
+ */
+int32_t spec_verify_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, void *stream);
+
+/* Static description of a status code. */
+const char *spec_verify_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

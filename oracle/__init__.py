@@ -30,6 +30,7 @@ ERR_TOKEN = 1
 ERR_TEMPERATURE = 2
 ERR_ROW = 4
 ERR_DRAFT_MASS = 8
+ERR_NO_DRAFT = 16
 
 _lib = None
 
@@ -71,7 +72,9 @@ def _load():
     lib.oracle_draft_logprobs.argtypes = [P, i32, i32, f64, f64, P]
     lib.oracle_draft_logprobs.restype = i32
     lib.oracle_spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f64,
-                                       P, P, P, P, P, P, P, P, i32]
+                                       P, P, P, P, P, P, P, P, P, i32]
+    lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
+    lib.oracle_uniforms.restype = None
     lib.oracle_spec_verify.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
@@ -106,6 +109,13 @@ def philox4x32_10(ctr, key) -> np.ndarray:
 
 def uniform(seed: int, b: int, pos: int, purpose: int) -> float:
     return float(_load().oracle_uniform(seed, b, pos, purpose))
+
+
+def uniforms(seed: int, B: int, P: int) -> np.ndarray:
+    """u(seed, b, pos, purpose) as a [B, P, 2] float64 array."""
+    out = np.zeros((B, P, 2), dtype=np.float64)
+    _load().oracle_uniforms(int(seed) & (2**64 - 1), B, P, _ptr(out))
+    return out
 
 
 def row_max(row: np.ndarray) -> float:
@@ -146,7 +156,8 @@ def max_threads() -> int:
 
 
 def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray, seed: int,
-                temperature, beta: float = 1.0, nthreads: int = 0) -> dict:
+                temperature, beta: float = 1.0, nthreads: int = 0,
+                seq_ids: np.ndarray | None = None) -> dict:
     """Run the oracle on a whole batch.
 
     target: [B, K+1, V] float32 or uint16 (bf16 bits); draft: [B, K, V] same
@@ -154,6 +165,8 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
     temperature: scalar or [B] float32.  Returns a dict of numpy arrays:
     accepted_len [B], out_tokens [B, K+1], p_target / p_draft / margin_accept
     [B, K], residual_mass / margin_bonus / seq_error [B], and error (int).
+    seq_ids [B] gives the global sequence index each row's uniforms are keyed
+    by (default 0..B-1), so a sample of a larger batch can be verified alone.
     """
     lib = _load()
     t_raw, dt = _as_raw(target)
@@ -164,13 +177,15 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
         assert dt2 == dt and d_raw.shape == (B, K, V)
     else:
         d_raw = None
-    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
-    assert tok.shape == (B, K)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(B, K))
     temp = np.asarray(temperature, dtype=np.float32)
     if temp.ndim == 0:
         temp = np.full(B, temp, dtype=np.float32)
     temp = np.ascontiguousarray(temp)
     assert temp.shape == (B,)
+    if seq_ids is not None:
+        seq_ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
+        assert seq_ids.shape == (B,)
     res = {
         "accepted_len": np.zeros(B, dtype=np.int32),
         "out_tokens": np.zeros((B, K + 1), dtype=np.int32),
@@ -185,6 +200,6 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
         _ptr(t_raw), _ptr(d_raw), _ptr(tok), B, K, V, dt, int(seed) & (2**64 - 1), _ptr(temp),
         float(beta), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["p_target"]),
         _ptr(res["p_draft"]), _ptr(res["residual_mass"]), _ptr(res["margin_accept"]),
-        _ptr(res["margin_bonus"]), _ptr(res["seq_error"]), int(nthreads))
+        _ptr(res["margin_bonus"]), _ptr(res["seq_error"]), _ptr(seq_ids), int(nthreads))
     res["error"] = int(err)
     return res

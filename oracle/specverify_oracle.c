@@ -57,6 +57,7 @@
 #define OR_ERR_TEMPERATURE 2 /* T < 0, NaN or infinite                    */
 #define OR_ERR_ROW 4         /* a row whose maximum logit is not finite   */
 #define OR_ERR_DRAFT_MASS 8  /* beta re-weighting left zero draft mass    */
+#define OR_ERR_NO_DRAFT 16   /* T > 0 and K > 0 but no draft logits given */
 
 /* ------------------------------------------------------------------ */
 /* Philox4x32-10 (SC'11): 10 rounds of a multiply/xor S-box; the 2-word key
@@ -270,6 +271,7 @@ typedef struct {
     double *margin_accept;    /* [B, K]   or NULL */
     double *margin_bonus;     /* [B]      or NULL */
     int32_t *seq_error;       /* [B]      or NULL */
+    const int32_t *seq_ids;   /* [B] global sequence index used by the uniforms, or NULL */
 } or_call;
 
 static const void *or_row_ptr(const void *base, int dtype, size_t row, int32_t V)
@@ -278,10 +280,19 @@ static const void *or_row_ptr(const void *base, int dtype, size_t row, int32_t V
     return (const char *)base + row * (size_t)V * elt;
 }
 
+/* A sequence that cannot be verified: no accepted drafts, every output
+ * token -1 and every diagnostic NaN. */
 static void or_fail_sequence(const or_call *c, int32_t b)
 {
     c->accepted_len[b] = 0;
     for (int32_t j = 0; j <= c->K; ++j) c->out_tokens[(size_t)b * (c->K + 1) + j] = -1;
+    for (int32_t i = 0; i < c->K; ++i) {
+        if (c->p_target) c->p_target[(size_t)b * c->K + i] = NAN;
+        if (c->p_draft) c->p_draft[(size_t)b * c->K + i] = NAN;
+        if (c->margin_accept) c->margin_accept[(size_t)b * c->K + i] = NAN;
+    }
+    if (c->residual_mass) c->residual_mass[b] = NAN;
+    if (c->margin_bonus) c->margin_bonus[b] = NAN;
 }
 
 static int or_verify_sequence(const or_call *c, int32_t b)
@@ -290,6 +301,7 @@ static int or_verify_sequence(const or_call *c, int32_t b)
     int err = 0;
     int32_t *out = c->out_tokens + (size_t)b * (K + 1);
     const int32_t *x = c->tokens + (size_t)b * K;
+    const uint32_t gb = c->seq_ids ? (uint32_t)c->seq_ids[b] : (uint32_t)b;
     const double nan = NAN;
 
     for (int32_t j = 0; j <= K; ++j) out[j] = -1;
@@ -331,6 +343,11 @@ static int or_verify_sequence(const or_call *c, int32_t b)
         return err;
     }
 
+    if (K > 0 && c->draft == NULL) {
+        or_fail_sequence(c, b);
+        return OR_ERR_NO_DRAFT;
+    }
+
     /* Sampling: accept x_i iff u_i <= ratio_i = p_t(x_i) / p_d'(x_i). */
     int weighted = c->beta < 1.0;
     int32_t n = K;
@@ -356,7 +373,7 @@ static int or_verify_sequence(const or_call *c, int32_t b)
             /* a draft token the draft law gives zero mass cannot be rejected */
             ratio = (lpd == -INFINITY) ? INFINITY : exp(lpt - lpd);
         }
-        double u = oracle_uniform(c->seed, (uint32_t)b, (uint32_t)i, OR_ACCEPT);
+        double u = oracle_uniform(c->seed, gb, (uint32_t)i, OR_ACCEPT);
         if (c->margin_accept) c->margin_accept[(size_t)b * K + i] = fabs(u - ratio);
         if (u <= ratio) {
             out[i] = x[i];
@@ -398,7 +415,7 @@ static int or_verify_sequence(const or_call *c, int32_t b)
     }
     /* Inverse CDF over ascending token ids: smallest v with C(v) >= u Z.
      * C is the same running sum that produced Z, so C(V-1) == Z.          */
-    double uB = oracle_uniform(c->seed, (uint32_t)b, (uint32_t)n, OR_BONUS);
+    double uB = oracle_uniform(c->seed, gb, (uint32_t)n, OR_BONUS);
     double thr = uB * Z;
     double C = 0.0, Cprev = 0.0;
     int32_t bonus = -1;
@@ -437,11 +454,11 @@ int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t 
                            const float *temperature, double beta, int32_t *accepted_len,
                            int32_t *out_tokens, double *p_target, double *p_draft,
                            double *residual_mass, double *margin_accept, double *margin_bonus,
-                           int32_t *seq_error, int32_t nthreads)
+                           int32_t *seq_error, const int32_t *seq_ids, int32_t nthreads)
 {
     or_call c = {target, draft, tokens, B, K, V, dtype, seed, temperature, beta,
                  accepted_len, out_tokens, p_target, p_draft, residual_mass,
-                 margin_accept, margin_bonus, seq_error};
+                 margin_accept, margin_bonus, seq_error, seq_ids};
     int32_t all_err = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -464,6 +481,17 @@ int32_t oracle_draft_logprobs(const void *row, int32_t dtype, int32_t V, double 
     if (e) return e;
     for (int32_t v = 0; v < V; ++v) out[v] = or_logprob(&r, v);
     return 0;
+}
+
+/* u(seed, b, pos, purpose) for b < B, pos < P, purpose in {0, 1}, laid out
+ * [B, P, 2]. */
+void oracle_uniforms(uint64_t seed, int32_t B, int32_t P, double *out)
+{
+    for (int32_t b = 0; b < B; ++b)
+        for (int32_t pos = 0; pos < P; ++pos)
+            for (uint32_t purpose = 0; purpose < 2; ++purpose)
+                out[((size_t)b * P + pos) * 2 + purpose] =
+                    oracle_uniform(seed, (uint32_t)b, (uint32_t)pos, purpose);
 }
 
 /* Number of threads an OpenMP parallel region would use by default. */

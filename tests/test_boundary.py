@@ -1,0 +1,140 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function
+include/*.h declares, sizes workspaces, and rejects invalid arguments with a
+status code before anything reaches the GPU (no compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import draft_token_verification_03_amd as sv
+    if not os.path.exists(sv.LIB_PATH):
+        from draft_token_verification_03_amd import build
+        build.build()
+    return sv.load_library()
+
+
+def declared_functions() -> set[str]:
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M):
+            name = m.group(1)
+            if name not in ("defined",):
+                names.add(name)
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"spec_verify", "spec_verify_workspace_size", "spec_verify_row_stats",
+            "spec_verify_uniforms", "spec_verify_status_str"} <= names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import draft_token_verification_03_amd as sv
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(sv.EXPORTED) <= declared_functions()
+
+
+def test_status_strings(lib):
+    import draft_token_verification_03_amd as sv
+    for code in (sv.SV_OK, sv.SV_EINVAL, sv.SV_EWORKSPACE, sv.SV_EHIP):
+        assert sv.status_str(code).startswith("SV_")
+    assert sv.status_str(12345) == "unknown status"
+
+
+def test_workspace_size(lib):
+    f = lib.spec_verify_workspace_size
+    assert f(8, 5, 128256, 1) > 0
+    assert f(8, 5, 128256, 1) % 256 == 0
+    assert f(512, 5, 128256, 0) >= f(8, 5, 128256, 0)
+    assert f(1, 0, 7, 0) > 0          # K = 0 (plain sampling) is allowed
+    assert f(-1, 5, 100, 0) == 0
+    assert f(1, -1, 100, 0) == 0
+    assert f(1, 129, 100, 0) == 0     # K above the documented maximum
+    assert f(1, 4, 0, 0) == 0
+    assert f(1, 4, 100, 7) == 0
+
+
+# fake but well-aligned device addresses: validation must reject before use
+A = 0x7F0000000000
+
+
+def _call(lib, **kw):
+    args = dict(target=A, draft=A + 0x100000, tokens=A + 0x200000, B=2, K=3, V=1000, dtype=1,
+                seed=0, temperature=A + 0x300000, beta=1.0, acc=A + 0x400000,
+                out=A + 0x500000, ws=A + 0x600000, wsbytes=1 << 30, aux=None, stream=None)
+    args.update(kw)
+    return lib.spec_verify(args["target"], args["draft"], args["tokens"], args["B"], args["K"],
+                           args["V"], args["dtype"], args["seed"], args["temperature"],
+                           args["beta"], args["acc"], args["out"], args["ws"], args["wsbytes"],
+                           args["aux"], args["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=-1), dict(K=-1), dict(K=129), dict(V=0), dict(V=-5), dict(dtype=2),
+    dict(beta=1.5), dict(beta=-0.1), dict(beta=float("nan")),
+    dict(target=None), dict(temperature=None), dict(acc=None), dict(out=None),
+    dict(tokens=None), dict(target=A + 1), dict(draft=A + 0x100001),
+    dict(target=A + 2, dtype=0),
+])
+def test_invalid_arguments_rejected(lib, bad):
+    import draft_token_verification_03_amd as sv
+    assert _call(lib, **bad) == sv.SV_EINVAL
+
+
+@pytest.mark.parametrize("bad", [dict(ws=None), dict(ws=A + 0x600010), dict(wsbytes=16)])
+def test_bad_workspace_rejected(lib, bad):
+    import draft_token_verification_03_amd as sv
+    assert _call(lib, **bad) == sv.SV_EWORKSPACE
+
+
+def test_empty_batch_is_a_noop(lib):
+    import draft_token_verification_03_amd as sv
+    # B == 0 returns before touching any pointer, even NULL ones
+    assert _call(lib, B=0, target=None, draft=None, tokens=None, temperature=None, acc=None,
+                 out=None, ws=None, wsbytes=0) == sv.SV_OK
+
+
+def test_tokens_may_be_null_when_no_drafts(lib):
+    import draft_token_verification_03_amd as sv
+    # K == 0 with NULL tokens passes validation up to the workspace check
+    assert _call(lib, K=0, tokens=None, draft=None, ws=None) == sv.SV_EWORKSPACE
+
+
+def test_row_stats_and_uniforms_validation(lib):
+    import draft_token_verification_03_amd as sv
+    P = ctypes.c_void_p
+    assert lib.spec_verify_row_stats(P(A), -1, 10, 0, P(A), P(A), P(A), P(A), P(A), 1 << 20,
+                                     None) == sv.SV_EINVAL
+    assert lib.spec_verify_row_stats(None, 4, 10, 0, P(A), P(A), P(A), P(A), P(A), 1 << 20,
+                                     None) == sv.SV_EINVAL
+    assert lib.spec_verify_row_stats(P(A), 4, 10, 0, P(A), P(A), P(A), P(A), None, 0,
+                                     None) == sv.SV_EWORKSPACE
+    assert lib.spec_verify_row_stats(P(A), 0, 10, 0, None, None, None, None, None, 0,
+                                     None) == sv.SV_OK
+    assert lib.spec_verify_uniforms(0, -1, 3, P(A), None) == sv.SV_EINVAL
+    assert lib.spec_verify_uniforms(0, 4, 3, None, None) == sv.SV_EINVAL
+    assert lib.spec_verify_uniforms(0, 0, 3, None, None) == sv.SV_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import draft_token_verification_03_amd as sv
+    saved = sv._lib
+    sv._lib = None
+    try:
+        with pytest.raises(sv.SpecVerifyError):
+            sv.load_library(str(tmp_path / "missing.so"))
+    finally:
+        sv._lib = saved
