@@ -31,8 +31,10 @@ DEFAULT_WORKLOAD = "C2"
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("draft_token_verification_03_amd/csrc/specverify.hip",
-                "draft_token_verification_03_amd/csrc/sv_device.h", "include/specverify.h"):
+    csrc = "draft_token_verification_03_amd/csrc/"
+    for rel in (csrc + "sv_api.hip", csrc + "sv_fused.hip", csrc + "sv_multipass.hip",
+                csrc + "sv_device.h", csrc + "sv_internal.h", csrc + "sv_accept.h",
+                "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -91,6 +93,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("default", "multipass"), default="default",
+                    help="spec_verify (default) or spec_verify_multipass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="instead, run torch copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -137,7 +141,7 @@ def main() -> int:
         r = replicas[k % reps]
         sv.spec_verify(r["target"], draft_arg[k % reps], r["tokens"], args.seed + k,
                        r["temperature"], r["beta"], workspace=ws, accepted_len=acc,
-                       out_tokens=out, stream=stream)
+                       out_tokens=out, stream=stream, multipass=args.path == "multipass")
 
     for k in range(args.warmup):
         step(k)
@@ -177,6 +181,8 @@ def main() -> int:
                    "rows_per_s": w.B * (w.K + 1) / (ms * 1e-3),
                    "sequences_per_s": w.B / (ms * 1e-3),
                    "mean_accepted_len": mean_acc,
+                   "entry_point": "spec_verify_multipass" if args.path == "multipass"
+                   else "spec_verify",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

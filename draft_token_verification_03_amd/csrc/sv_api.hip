@@ -1,0 +1,292 @@
+// sv_api.hip -- the C ABI of libspecverify: argument validation, the launch
+// plan and the choice between the fused single-launch path and the
+// multi-pass path.  The operation is specified in include/specverify.h.
+#include <algorithm>
+#include <cstdint>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
+{
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return false;
+    *p = Plan{};
+    p->B = B;
+    p->K = K;
+    p->V = V;
+    p->dtype = dtype;
+    const int elt = dtype == SV_F32 ? 4 : 2;
+    p->vec = 16 / elt;
+    p->R = 2 * K + 1;
+    p->row_bytes = (int64_t)V * elt;
+    p->nvec = (int32_t)(((int64_t)V + p->vec - 1) / p->vec);
+
+    // multi-pass: enough workgroups to fill the chip, >= one vector per thread
+    const int64_t rows = std::max<int64_t>(1, (int64_t)B * p->R);
+    int64_t nc = (kFillBlocks + rows - 1) / rows;
+    const int64_t nc_max = std::max<int64_t>(1, p->nvec / kBlock);
+    nc = std::min<int64_t>(std::min<int64_t>(nc, nc_max), kMaxChunks);
+    p->cvec = (int32_t)((p->nvec + nc - 1) / nc);
+    p->nc = (p->nvec + p->cvec - 1) / p->cvec;
+    const int64_t ncr_want = (kFillBlocks + std::max(B, 1) - 1) / std::max(B, 1);
+    int64_t rvec = (p->nvec + ncr_want - 1) / ncr_want;
+    rvec = std::max<int64_t>(rvec, kBlock);
+    rvec = std::min<int64_t>(rvec, (int64_t)kBlock * kLoads);
+    p->rvec = (int32_t)rvec;
+    p->ncr = (int32_t)((p->nvec + rvec - 1) / rvec);
+    if ((int64_t)B * p->R * p->nc >= ((int64_t)1 << 31) || (int64_t)B * p->ncr >= ((int64_t)1 << 31))
+        return false;
+    size_t off = align256(kPersistBytes);
+    p->off_part = off;
+    off = align256(off + sizeof(RowPart) * (size_t)B * p->R * p->nc);
+    p->off_top = off;
+    off = align256(off + sizeof(Top4) * (size_t)B * K * p->nc);
+    p->off_seq = off;
+    off = align256(off + sizeof(SeqState) * (size_t)B);
+    p->off_res = off;
+    off = align256(off + sizeof(double) * (size_t)B * p->ncr);
+    p->mp_bytes = off;
+
+    // fused: chunks of kBlock * kFusedU vectors, one launch per kMaxSeqPerLaunch sequences
+    p->fu = kFusedU;
+    const int64_t cvf = (int64_t)kBlock * kFusedU;
+    p->fchunks = (int32_t)((p->nvec + cvf - 1) / cvf);
+    p->fB = std::min(std::max(B, 1), kMaxSeqPerLaunch);
+    // streaming chunks: as long as possible while the grid keeps ~kFusedFill items
+    const int64_t slots = (int64_t)p->fB * (K + 1);
+    int64_t sch = std::min<int64_t>(std::max<int64_t>(1, (kFusedFill + slots - 1) / slots), p->fchunks);
+    p->fspan = (int32_t)((p->fchunks + sch - 1) / sch);
+    p->fschunks = (p->fchunks + p->fspan - 1) / p->fspan;
+    p->fitems = (K + 1) * p->fschunks;
+    const int64_t parts = (int64_t)(2 * K + 1) * p->fschunks;
+    const int64_t tops = (int64_t)K * p->fschunks;
+    p->fused_shape_ok = K <= kFusedMaxK && parts <= 4 * kBlock && tops <= 2 * kBlock &&
+                        parts * (int64_t)sizeof(RowPart) + tops * (int64_t)sizeof(Top4) <= kStageBytes &&
+                        (int64_t)p->fB * (p->fitems + p->fchunks) < ((int64_t)1 << 31);
+    off = align256(kPersistBytes);
+    p->foff_part = off;
+    off = align256(off + sizeof(RowPart) * (size_t)p->fB * parts);
+    p->foff_top = off;
+    off = align256(off + sizeof(Top4) * (size_t)p->fB * tops);
+    p->foff_state = off;
+    off = align256(off + sizeof(SeqState) * (size_t)p->fB);
+    p->foff_res = off;
+    off = align256(off + sizeof(double) * (size_t)p->fB * p->fchunks);
+    p->foff_zx = off;
+    off = align256(off + sizeof(float2) * (size_t)p->fB * K);
+    p->f_bytes = p->fused_shape_ok ? off : 0;
+
+    p->bytes = std::max(p->mp_bytes, p->f_bytes);
+    return true;
+}
+
+static Args base_args(const Plan &p, void *ws)
+{
+    Args a = {};
+    char *w = static_cast<char *>(ws);
+    a.B = p.B;
+    a.K = p.K;
+    a.V = p.V;
+    a.R = p.R;
+    a.nvec = p.nvec;
+    a.nc = p.nc;
+    a.cvec = p.cvec;
+    a.ncr = p.ncr;
+    a.rvec = p.rvec;
+    a.dtype = p.dtype;
+    a.row_bytes = p.row_bytes;
+    a.part = reinterpret_cast<RowPart *>(w + p.off_part);
+    a.top = reinterpret_cast<Top4 *>(w + p.off_top);
+    a.seq = reinterpret_cast<SeqState *>(w + p.off_seq);
+    a.res = reinterpret_cast<double *>(w + p.off_res);
+    return a;
+}
+
+// Checks shared by the verify entry points; SV_OK means "go on".
+static int32_t validate(const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                        const float *temperature, float beta, int32_t *accepted_len,
+                        int32_t *out_tokens)
+{
+    if (B < 0 || K < 0 || K > kMaxK || V < 1) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (!(beta >= 0.f && beta <= 1.f)) return SV_EINVAL;
+    if ((int64_t)B * (K + 1) * (int64_t)V > ((int64_t)1 << 40)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !temperature || !accepted_len || !out_tokens) return SV_EINVAL;
+    if (K > 0 && !draft_tokens) return SV_EINVAL;
+    const size_t elt = dtype == SV_F32 ? 4 : 2;
+    if (((uintptr_t)target_logits % elt) || (draft_logits && ((uintptr_t)draft_logits % elt)))
+        return SV_EINVAL;
+    return SV_OK;
+}
+
+static int32_t verify(const void *target_logits, const void *draft_logits,
+                      const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                      uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
+                      int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                      const sv_aux *aux, void *stream, bool allow_fused)
+{
+    const int32_t v = validate(target_logits, draft_logits, draft_tokens, B, K, V, dtype,
+                               temperature, beta, accepted_len, out_tokens);
+    if (v != SV_OK || B == 0) return v;
+    Plan p;
+    if (!make_plan(B, K, V, dtype, &p)) return SV_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
+        return SV_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool weighted = beta < 1.f && K > 0;
+    char *ws = static_cast<char *>(workspace);
+
+    if (allow_fused && p.fused_shape_ok && fused_capacity_ok(p, weighted)) {
+        for (int32_t b0 = 0; b0 < B; b0 += p.fB) {
+            const int32_t nb = std::min(p.fB, B - b0);
+            FusedArgs a = {};
+            a.target = static_cast<const char *>(target_logits) + (int64_t)b0 * (K + 1) * p.row_bytes;
+            a.draft = draft_logits
+                          ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
+                          : nullptr;
+            a.tokens = draft_tokens ? draft_tokens + (int64_t)b0 * K : nullptr;
+            a.temperature = temperature + b0;
+            a.B = nb;
+            a.K = K;
+            a.V = V;
+            a.nvec = p.nvec;
+            a.chunks = p.fchunks;
+            a.sspan = p.fspan;
+            a.schunks = p.fschunks;
+            a.stream_items = nb * p.fitems;
+            a.b0 = b0;
+            a.row_bytes = p.row_bytes;
+            a.seed = seed;
+            a.beta = beta;
+            a.weighted = weighted ? 1 : 0;
+            a.spin_limit = 1u << 20;
+            a.accepted_len = accepted_len + b0;
+            a.out_tokens = out_tokens + (int64_t)b0 * (K + 1);
+            if (aux) {
+                a.aux_pt = aux->p_target ? aux->p_target + (int64_t)b0 * K : nullptr;
+                a.aux_pd = aux->p_draft ? aux->p_draft + (int64_t)b0 * K : nullptr;
+                a.aux_z = aux->residual_mass ? aux->residual_mass + b0 : nullptr;
+                a.error_word = aux->error_word;
+            }
+            a.seqctl = reinterpret_cast<SeqCtl *>(ws);
+            a.part = reinterpret_cast<RowPart *>(ws + p.foff_part);
+            a.top = reinterpret_cast<Top4 *>(ws + p.foff_top);
+            a.state = reinterpret_cast<SeqState *>(ws + p.foff_state);
+            a.res = reinterpret_cast<double *>(ws + p.foff_res);
+            a.zx = reinterpret_cast<float2 *>(ws + p.foff_zx);
+            launch_fused(a, p, s);
+        }
+    } else {
+        Args a = base_args(p, workspace);
+        a.target = static_cast<const char *>(target_logits);
+        a.draft = static_cast<const char *>(draft_logits);
+        a.tokens = draft_tokens;
+        a.temperature = temperature;
+        a.seed = seed;
+        a.beta = beta;
+        a.weighted = weighted ? 1 : 0;
+        a.accepted_len = accepted_len;
+        a.out_tokens = out_tokens;
+        if (aux) {
+            a.aux_pt = aux->p_target;
+            a.aux_pd = aux->p_draft;
+            a.aux_z = aux->residual_mass;
+            a.error_word = aux->error_word;
+        }
+        // With no draft logits every sequence is greedy or fails; nothing to draw.
+        const bool draw = !(K > 0 && draft_logits == nullptr);
+        launch_multipass(a, p, s, draw);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype)
+{
+    sv::Plan p;
+    if (B < 0 || !sv::make_plan(B, K, V, dtype, &p)) return 0;
+    return p.bytes;
+}
+
+int32_t spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < sv::kPersistBytes)
+        return SV_EWORKSPACE;
+    sv::launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+int32_t spec_verify(const void *target_logits, const void *draft_logits,
+                    const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                    uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
+                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    const sv_aux *aux, void *stream)
+{
+    return sv::verify(target_logits, draft_logits, draft_tokens, B, K, V, dtype, seed, temperature,
+                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream, true);
+}
+
+int32_t spec_verify_multipass(const void *target_logits, const void *draft_logits,
+                              const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
+                              int32_t dtype, uint64_t seed, const float *temperature, float beta,
+                              int32_t *accepted_len, int32_t *out_tokens, void *workspace,
+                              size_t workspace_bytes, const sv_aux *aux, void *stream)
+{
+    return sv::verify(target_logits, draft_logits, draft_tokens, B, K, V, dtype, seed, temperature,
+                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream, false);
+}
+
+int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,
+                              const float *temperature, float *row_max, double *row_logsum,
+                              int32_t *row_argmax, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    if (rows < 0 || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return SV_EINVAL;
+    if (rows == 0) return SV_OK;
+    if (!logits || !temperature || !row_max || !row_logsum || !row_argmax) return SV_EINVAL;
+    const size_t elt = dtype == SV_F32 ? 4 : 2;
+    if ((uintptr_t)logits % elt) return SV_EINVAL;
+    sv::Plan p;
+    if (!sv::make_plan(rows, 0, V, dtype, &p)) return SV_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
+        return SV_EWORKSPACE;
+    sv::Args a = sv::base_args(p, workspace);
+    a.target = static_cast<const char *>(logits);
+    a.temperature = temperature;
+    a.rs_max = row_max;
+    a.rs_logsum = row_logsum;
+    a.rs_argmax = row_argmax;
+    sv::launch_rowstats(a, p, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+int32_t spec_verify_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, void *stream)
+{
+    if (B < 0 || P < 0) return SV_EINVAL;
+    const int64_t total = (int64_t)B * P * 2;
+    if (total == 0) return SV_OK;
+    if (!out || total > ((int64_t)1 << 31)) return SV_EINVAL;
+    sv::launch_uniforms(seed, B, P, out, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+const char *spec_verify_status_str(int32_t status)
+{
+    switch (status) {
+    case SV_OK: return "SV_OK: success";
+    case SV_EINVAL: return "SV_EINVAL: invalid argument (nothing enqueued)";
+    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
+    case SV_EHIP: return "SV_EHIP: HIP runtime error on launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -108,7 +108,7 @@ __device__ __forceinline__ uint4 pick4(const uint32_t (&d)[8], uint32_t r)
 // 16 bytes starting at a non-16-aligned address p, from the two aligned
 // 16-byte blocks that hold them.  The second block is only read when it holds
 // valid bytes (`need_second`), so no read leaves the pages the row lives in.
-__device__ __noinline__ uint4 load16_unaligned(const char *p, bool need_second)
+__device__ __forceinline__ uint4 load16_unaligned(const char *p, bool need_second)
 {
     const uintptr_t a = (uintptr_t)p;
     const uint4 *blk = reinterpret_cast<const uint4 *>(a & ~(uintptr_t)15);
@@ -125,8 +125,18 @@ __device__ __noinline__ uint4 load16_unaligned(const char *p, bool need_second)
     }
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the nontemporal hint: logits are streamed once, and on
+// MI355X the hinted loads sustain ~7.1 TB/s against ~6.3 TB/s without it.
+__device__ __forceinline__ uint4 load16_stream(const char *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Vector q of a row as floats; elements at or beyond V are -inf.
-template <int DT>
+template <int DT, bool STREAM = false>
 __device__ __forceinline__ void load_vec(const char *row, bool aligned, int q, int V,
                                          float (&x)[Elt<DT>::kVec])
 {
@@ -135,7 +145,7 @@ __device__ __forceinline__ void load_vec(const char *row, bool aligned, int q, i
     uint4 raw;
     const int first = q * VEC;
     if (aligned) {
-        raw = *reinterpret_cast<const uint4 *>(p);
+        raw = STREAM ? load16_stream(p) : *reinterpret_cast<const uint4 *>(p);
     } else {
         const int valid = min(VEC, V - first);
         const uint32_t sh = (uint32_t)((uintptr_t)p & 15);
@@ -147,6 +157,58 @@ __device__ __forceinline__ void load_vec(const char *row, bool aligned, int q, i
         for (int k = 0; k < VEC; ++k)
             if (first + k >= V) x[k] = -INFINITY;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Data handed between workgroups.  The L2 caches of the XCDs are not coherent
+// with each other, and the fences that would make plain stores visible write
+// back or invalidate a whole L2, which serialises workgroups.  Instead every
+// word another workgroup reads is stored and loaded as a relaxed agent-scope
+// atomic (coherent across XCDs), and a producer drains its outstanding memory
+// operations before the counter update that publishes them.
+
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
+{
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_agent16(void *p, uint4 v)
+{
+    unsigned long long *q = reinterpret_cast<unsigned long long *>(p);
+    __hip_atomic_store(q, ((unsigned long long)v.y << 32) | v.x, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, ((unsigned long long)v.w << 32) | v.z, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint4 ld_agent16(const void *p)
+{
+    unsigned long long *q = reinterpret_cast<unsigned long long *>(const_cast<void *>(p));
+    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+
+template <class T>
+__device__ __forceinline__ void st_agent_obj(T *dst, const T &v)
+{
+    static_assert(sizeof(T) % 16 == 0, "16-byte granules");
+    const uint4 *src = reinterpret_cast<const uint4 *>(&v);
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 16); ++k) st_agent16(reinterpret_cast<uint4 *>(dst) + k, src[k]);
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void drain_memory()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ---------------------------------------------------------------------------

@@ -47,8 +47,14 @@
  * +inf logits give unspecified results.  The library never allocates device
  * memory and never synchronises: all work is enqueued on `stream` (a
  * hipStream_t; NULL is the default stream) and results are ready when the
- * stream is synchronised.  Calls are re-entrant; concurrent calls need
- * distinct workspaces.
+ * stream is synchronised.  Calls are re-entrant; calls that may overlap in
+ * time need distinct workspaces.
+ *
+ * Workspace: a caller-owned device buffer of spec_verify_workspace_size()
+ * bytes, 256-byte aligned.  Its first 1 MiB holds per-sequence control words
+ * that must be zero before its first use (spec_verify_workspace_init, or any
+ * zero fill) and that every completed call leaves zero again; the rest is
+ * scratch.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -76,13 +82,15 @@ extern "C" {
 #define SV_ERR_ROW 4            /* a used row has no finite maximum: outputs are -1     */
 #define SV_ERR_DRAFT_MASS 8     /* beta == 0 left a draft row with zero mass: outputs -1 */
 #define SV_ERR_NO_DRAFT 16      /* T > 0 but draft_logits is NULL: outputs are -1       */
+#define SV_ERR_TIMEOUT 32       /* an internal wait gave up (another kernel held the
+                                   GPU's workgroup slots); some bonus tokens are -1  */
 
 /* Optional per-call diagnostics; every field may be NULL. */
 typedef struct sv_aux {
     float *p_target;      /* [B, K] p_i(x_i) at evaluated positions, NaN elsewhere and in greedy mode */
     float *p_draft;       /* [B, K] q_i(x_i) (beta-weighted) at evaluated positions, else NaN         */
     float *residual_mass; /* [B]    C(V-1) of the bonus draw; NaN in greedy mode                      */
-    int32_t *error_word;  /* [1]    OR of SV_ERR_* bits; cleared by the call before it is set        */
+    int32_t *error_word;  /* [1]    SV_ERR_* bits are OR-ed in: zero it before the call           */
 } sv_aux;
 
 /*
@@ -90,6 +98,13 @@ typedef struct sv_aux {
  * are invalid).  Pure host function.
  */
 size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype);
+
+/*
+ * Zero a workspace on `stream` (needed once, before its first use).
+ * Returns SV_EWORKSPACE if it is NULL, not 256-byte aligned or smaller than
+ * the control words.
+ */
+int32_t spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The verify step.
@@ -100,16 +115,30 @@ size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype
  *   beta           host float in [0, 1]; 1 = no draft re-weighting
  *   accepted_len   [B]         int32 out: n in [0, K]
  *   out_tokens     [B, K+1]    int32 out: x_0..x_{n-1}, the bonus token, then -1
- *   workspace      device buffer of >= spec_verify_workspace_size(...) bytes,
- *                  256-byte aligned; its contents on entry do not matter
+ *   workspace      device buffer of >= spec_verify_workspace_size(...) bytes
+ *                  (see "Workspace" above)
  *   aux            host pointer to an sv_aux, or NULL
- * B == 0 is a no-op.  Returns SV_OK after enqueuing the work.
+ * B == 0 is a no-op.  Returns SV_OK after enqueuing the work.  Shapes with
+ * K <= 16 and rows short enough for one sequence's partials to fit on chip
+ * run as a single launch; others take the multi-pass path below.
  */
 int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
                     uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_aux *aux, void *stream);
+
+/*
+ * The same operation, same arguments and same results, always computed by
+ * the four-launch path (streaming pass, accept scan, residual sums, bonus
+ * draw) that spec_verify falls back to.  It never touches the workspace's
+ * control words.
+ */
+int32_t spec_verify_multipass(const void *target_logits, const void *draft_logits,
+                              const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
+                              int32_t dtype, uint64_t seed, const float *temperature, float beta,
+                              int32_t *accepted_len, int32_t *out_tokens, void *workspace,
+                              size_t workspace_bytes, const sv_aux *aux, void *stream);
 
 /*
  * Per-row statistics of `rows` rows of V logits (the streaming pass of the
