@@ -32,8 +32,8 @@ DEFAULT_WORKLOAD = "C2"
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = "draft_token_verification_03_amd/csrc/"
-    for rel in (csrc + "sv_api.hip", csrc + "sv_fused.hip", csrc + "sv_multipass.hip",
-                csrc + "sv_device.h", csrc + "sv_internal.h", csrc + "sv_accept.h",
+    for rel in (csrc + "sv_api.hip", csrc + "sv_verify.hip",
+                csrc + "sv_device.h", csrc + "sv_internal.h", csrc + "sv_accept.h", csrc + "sv_tile.h",
                 "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
@@ -93,8 +93,6 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("default", "multipass"), default="default",
-                    help="spec_verify (default) or spec_verify_multipass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="instead, run torch copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -141,7 +139,7 @@ def main() -> int:
         r = replicas[k % reps]
         sv.spec_verify(r["target"], draft_arg[k % reps], r["tokens"], args.seed + k,
                        r["temperature"], r["beta"], workspace=ws, accepted_len=acc,
-                       out_tokens=out, stream=stream, multipass=args.path == "multipass")
+                       out_tokens=out, stream=stream)
 
     for k in range(args.warmup):
         step(k)
@@ -181,8 +179,6 @@ def main() -> int:
                    "rows_per_s": w.B * (w.K + 1) / (ms * 1e-3),
                    "sequences_per_s": w.B / (ms * 1e-3),
                    "mean_accepted_len": mean_acc,
-                   "entry_point": "spec_verify_multipass" if args.path == "multipass"
-                   else "spec_verify",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

@@ -28,11 +28,9 @@ SV_ERR_TEMPERATURE = 2
 SV_ERR_ROW = 4
 SV_ERR_DRAFT_MASS = 8
 SV_ERR_NO_DRAFT = 16
-SV_ERR_TIMEOUT = 32
 
-EXPORTED = ("spec_verify", "spec_verify_multipass", "spec_verify_workspace_size",
-            "spec_verify_workspace_init", "spec_verify_row_stats", "spec_verify_uniforms",
-            "spec_verify_status_str")
+EXPORTED = ("spec_verify", "spec_verify_workspace_size", "spec_verify_row_stats",
+            "spec_verify_uniforms", "spec_verify_status_str")
 
 
 class SpecVerifyError(RuntimeError):
@@ -60,13 +58,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             ctypes.c_size_t)
     lib.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.spec_verify_workspace_size.restype = sz
-    for name in ("spec_verify", "spec_verify_multipass"):
-        fn = getattr(lib, name)
-        fn.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f32, P, P, P, sz,
-                       ctypes.POINTER(_Aux), P]
-        fn.restype = i32
-    lib.spec_verify_workspace_init.argtypes = [P, sz, P]
-    lib.spec_verify_workspace_init.restype = i32
+    lib.spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f32, P, P, P, sz,
+                                ctypes.POINTER(_Aux), P]
+    lib.spec_verify.restype = i32
     lib.spec_verify_row_stats.argtypes = [P, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.spec_verify_row_stats.restype = i32
     lib.spec_verify_uniforms.argtypes = [u64, i32, i32, P, P]
@@ -109,20 +103,18 @@ def workspace_size(B: int, K: int, V: int, dtype: torch.dtype) -> int:
     return int(load_library().spec_verify_workspace_size(B, K, V, code))
 
 
-def alloc_workspace(B: int, K: int, V: int, dtype: torch.dtype, device, stream=None) -> torch.Tensor:
-    """A workspace for these sizes, zero-initialised on `stream`."""
+def alloc_workspace(B: int, K: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """A workspace for these sizes (scratch: its contents do not matter)."""
     n = workspace_size(B, K, V, dtype)
     if n == 0:
         raise SpecVerifyError("invalid sizes for a workspace")
-    ws = torch.empty(n, dtype=torch.uint8, device=device)
-    _check(load_library().spec_verify_workspace_init(ws.data_ptr(), n, _stream(stream)))
-    return ws
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
                 seed: int, temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
                 accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
-                aux: bool = False, stream=None, multipass: bool = False):
+                aux: bool = False, stream=None):
     """Verify K drafted tokens per sequence.
 
     target [B, K+1, V] and draft [B, K, V] (or None if every temperature is 0)
@@ -130,9 +122,9 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
     float or a [B] float32 tensor (0 = greedy); beta in [0, 1].  Returns
     (accepted_len [B] int32, out_tokens [B, K+1] int32), plus a dict of
     diagnostics (p_target, p_draft, residual_mass, error_word) if aux=True.
-    The work is enqueued on `stream` (default: the current stream).  A
-    workspace passed in must come from alloc_workspace (or be zero-filled
-    once).  multipass=True forces the four-launch path.
+    The work is enqueued on `stream` (default: the current stream); a
+    workspace of at least workspace_size(B, K, V, dtype) bytes may be passed
+    in (e.g. from alloc_workspace) to avoid an allocation per call.
     """
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -153,7 +145,7 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
         raise ValueError("temperature must be a [B] float32 tensor")
     temperature = temperature.contiguous()
     if workspace is None:
-        workspace = alloc_workspace(B, K, V, target.dtype, dev, stream)
+        workspace = alloc_workspace(B, K, V, target.dtype, dev)
     if accepted_len is None:
         accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
     if out_tokens is None:
@@ -169,8 +161,7 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
         }
         aux_s = _Aux(aux_t["p_target"].data_ptr(), aux_t["p_draft"].data_ptr(),
                      aux_t["residual_mass"].data_ptr(), aux_t["error_word"].data_ptr())
-    fn = load_library().spec_verify_multipass if multipass else load_library().spec_verify
-    status = fn(
+    status = load_library().spec_verify(
         _ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code, int(seed) & (2**64 - 1),
         _ptr(temperature), float(beta), _ptr(accepted_len), _ptr(out_tokens), _ptr(workspace),
         workspace.numel(), ctypes.byref(aux_s) if aux_s is not None else None, _stream(stream))
@@ -192,7 +183,7 @@ def row_stats(logits: torch.Tensor, temperature, *, stream=None):
     if not torch.is_tensor(temperature):
         temperature = torch.full((rows,), float(temperature), dtype=torch.float32, device=dev)
     temperature = temperature.contiguous()
-    ws = alloc_workspace(max(rows, 1), 0, V, logits.dtype, dev, stream)
+    ws = alloc_workspace(max(rows, 1), 0, V, logits.dtype, dev)
     mx = torch.empty(rows, dtype=torch.float32, device=dev)
     ls = torch.empty(rows, dtype=torch.float64, device=dev)
     am = torch.empty(rows, dtype=torch.int32, device=dev)

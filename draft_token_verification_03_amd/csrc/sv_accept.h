@@ -1,5 +1,5 @@
 // sv_accept.h -- row merges, the accept decision and the residual, shared by
-// the fused and the multi-pass kernels.
+// the two-launch and the four-launch paths.
 #pragma once
 
 #include "sv_internal.h"
@@ -10,7 +10,7 @@ __device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T !
 
 // ---------------------------------------------------------------------------
 // Wave-level merges of one row's chunk partials `p[0..nc)` (lanes stride the
-// chunks).  The same code merges target and draft rows, so equal rows merge to
+// chunks; the accept kernel stages them in LDS).  The same code merges target and draft rows, so equal rows merge to
 // bitwise-equal statistics.
 
 __device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, float &M, double &S)
@@ -43,11 +43,6 @@ __device__ __forceinline__ void merge_argmax(const RowPart *p, int nc, float &M,
     wave_argmax(v, i);
     M = v;
     I = i;
-}
-
-__device__ __forceinline__ bool top_has(const Top4 &t, int i)
-{
-    return i != INT_MAX && (t.i[0] == i || t.i[1] == i || t.i[2] == i || t.i[3] == i);
 }
 
 // A beta-weighted draft row.  Partials carry, per chunk, the chunk's top-4 and

@@ -1,6 +1,5 @@
 // sv_api.hip -- the C ABI of libspecverify: argument validation, the launch
-// plan and the choice between the fused single-launch path and the
-// multi-pass path.  The operation is specified in include/specverify.h.
+// plan, the workspace layout and the split into sub-batches.  The operation is specified in include/specverify.h.
 #include <algorithm>
 #include <cstdint>
 
@@ -21,73 +20,50 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     const int elt = dtype == SV_F32 ? 4 : 2;
     p->vec = 16 / elt;
     p->R = 2 * K + 1;
+    p->sB = std::min(std::max(B, 1), kMaxSeqPerLaunch);
     p->row_bytes = (int64_t)V * elt;
     p->nvec = (int32_t)(((int64_t)V + p->vec - 1) / p->vec);
 
-    // multi-pass: enough workgroups to fill the chip, >= one vector per thread
-    const int64_t rows = std::max<int64_t>(1, (int64_t)B * p->R);
+    // streaming: ~kFillBlocks workgroups per sub-batch, >= one vector per
+    // thread, and one sequence's partials and top-4 lists within the accept
+    // kernel's LDS staging
+    const int64_t rows = (int64_t)p->sB * p->R;
     int64_t nc = (kFillBlocks + rows - 1) / rows;
     const int64_t nc_max = std::max<int64_t>(1, p->nvec / kBlock);
-    nc = std::min<int64_t>(std::min<int64_t>(nc, nc_max), kMaxChunks);
+    const int64_t nc_stage =
+        kStageBytes / ((int64_t)sizeof(RowPart) * p->R + (int64_t)sizeof(Top4) * K);
+    nc = std::min<int64_t>(std::min<int64_t>(nc, nc_max), std::min<int64_t>(kMaxChunks, nc_stage));
+    nc = std::max<int64_t>(nc, 1);
     p->cvec = (int32_t)((p->nvec + nc - 1) / nc);
     p->nc = (p->nvec + p->cvec - 1) / p->cvec;
-    const int64_t ncr_want = (kFillBlocks + std::max(B, 1) - 1) / std::max(B, 1);
+    // residual: chunks of kBlock..kBlock*kLoads vectors, ~kFillBlocks workgroups
+    const int64_t ncr_want = (kResFill + p->sB - 1) / p->sB;
     int64_t rvec = (p->nvec + ncr_want - 1) / ncr_want;
     rvec = std::max<int64_t>(rvec, kBlock);
     rvec = std::min<int64_t>(rvec, (int64_t)kBlock * kLoads);
     p->rvec = (int32_t)rvec;
     p->ncr = (int32_t)((p->nvec + rvec - 1) / rvec);
-    if ((int64_t)B * p->R * p->nc >= ((int64_t)1 << 31) || (int64_t)B * p->ncr >= ((int64_t)1 << 31))
+    if (rows * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ncr >= ((int64_t)1 << 31))
         return false;
-    size_t off = align256(kPersistBytes);
+    size_t off = 0;
     p->off_part = off;
-    off = align256(off + sizeof(RowPart) * (size_t)B * p->R * p->nc);
+    off = align256(off + sizeof(RowPart) * (size_t)rows * p->nc);
     p->off_top = off;
-    off = align256(off + sizeof(Top4) * (size_t)B * K * p->nc);
+    off = align256(off + sizeof(Top4) * (size_t)p->sB * K * p->nc);
     p->off_seq = off;
-    off = align256(off + sizeof(SeqState) * (size_t)B);
+    off = align256(off + sizeof(SeqState) * (size_t)p->sB);
     p->off_res = off;
-    off = align256(off + sizeof(double) * (size_t)B * p->ncr);
-    p->mp_bytes = off;
-
-    // fused: chunks of kBlock * kFusedU vectors, one launch per kMaxSeqPerLaunch sequences
-    p->fu = kFusedU;
-    const int64_t cvf = (int64_t)kBlock * kFusedU;
-    p->fchunks = (int32_t)((p->nvec + cvf - 1) / cvf);
-    p->fB = std::min(std::max(B, 1), kMaxSeqPerLaunch);
-    // streaming chunks: as long as possible while the grid keeps ~kFusedFill items
-    const int64_t slots = (int64_t)p->fB * (K + 1);
-    int64_t sch = std::min<int64_t>(std::max<int64_t>(1, (kFusedFill + slots - 1) / slots), p->fchunks);
-    p->fspan = (int32_t)((p->fchunks + sch - 1) / sch);
-    p->fschunks = (p->fchunks + p->fspan - 1) / p->fspan;
-    p->fitems = (K + 1) * p->fschunks;
-    const int64_t parts = (int64_t)(2 * K + 1) * p->fschunks;
-    const int64_t tops = (int64_t)K * p->fschunks;
-    p->fused_shape_ok = K <= kFusedMaxK && parts <= 4 * kBlock && tops <= 2 * kBlock &&
-                        parts * (int64_t)sizeof(RowPart) + tops * (int64_t)sizeof(Top4) <= kStageBytes &&
-                        (int64_t)p->fB * (p->fitems + p->fchunks) < ((int64_t)1 << 31);
-    off = align256(kPersistBytes);
-    p->foff_part = off;
-    off = align256(off + sizeof(RowPart) * (size_t)p->fB * parts);
-    p->foff_top = off;
-    off = align256(off + sizeof(Top4) * (size_t)p->fB * tops);
-    p->foff_state = off;
-    off = align256(off + sizeof(SeqState) * (size_t)p->fB);
-    p->foff_res = off;
-    off = align256(off + sizeof(double) * (size_t)p->fB * p->fchunks);
-    p->foff_zx = off;
-    off = align256(off + sizeof(float2) * (size_t)p->fB * K);
-    p->f_bytes = p->fused_shape_ok ? off : 0;
-
-    p->bytes = std::max(p->mp_bytes, p->f_bytes);
+    off = align256(off + sizeof(double) * (size_t)p->sB * p->ncr);
+    p->bytes = off;
     return true;
 }
 
-static Args base_args(const Plan &p, void *ws)
+// Arguments of the sub-batch of sequences [b0, b0 + nb).
+static Args sub_args(const Plan &p, void *ws, int32_t b0, int32_t nb)
 {
     Args a = {};
     char *w = static_cast<char *>(ws);
-    a.B = p.B;
+    a.B = nb;
     a.K = p.K;
     a.V = p.V;
     a.R = p.R;
@@ -97,6 +73,7 @@ static Args base_args(const Plan &p, void *ws)
     a.ncr = p.ncr;
     a.rvec = p.rvec;
     a.dtype = p.dtype;
+    a.b0 = b0;
     a.row_bytes = p.row_bytes;
     a.part = reinterpret_cast<RowPart *>(w + p.off_part);
     a.top = reinterpret_cast<Top4 *>(w + p.off_top);
@@ -128,7 +105,7 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
                       const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
                       uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                       int32_t *out_tokens, void *workspace, size_t workspace_bytes,
-                      const sv_aux *aux, void *stream, bool allow_fused)
+                      const sv_aux *aux, void *stream)
 {
     const int32_t v = validate(target_logits, draft_logits, draft_tokens, B, K, V, dtype,
                                temperature, beta, accepted_len, out_tokens);
@@ -138,69 +115,29 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
         return SV_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool weighted = beta < 1.f && K > 0;
-    char *ws = static_cast<char *>(workspace);
-
-    if (allow_fused && p.fused_shape_ok && fused_capacity_ok(p, weighted)) {
-        for (int32_t b0 = 0; b0 < B; b0 += p.fB) {
-            const int32_t nb = std::min(p.fB, B - b0);
-            FusedArgs a = {};
-            a.target = static_cast<const char *>(target_logits) + (int64_t)b0 * (K + 1) * p.row_bytes;
-            a.draft = draft_logits
-                          ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
-                          : nullptr;
-            a.tokens = draft_tokens ? draft_tokens + (int64_t)b0 * K : nullptr;
-            a.temperature = temperature + b0;
-            a.B = nb;
-            a.K = K;
-            a.V = V;
-            a.nvec = p.nvec;
-            a.chunks = p.fchunks;
-            a.sspan = p.fspan;
-            a.schunks = p.fschunks;
-            a.stream_items = nb * p.fitems;
-            a.b0 = b0;
-            a.row_bytes = p.row_bytes;
-            a.seed = seed;
-            a.beta = beta;
-            a.weighted = weighted ? 1 : 0;
-            a.spin_limit = 1u << 20;
-            a.accepted_len = accepted_len + b0;
-            a.out_tokens = out_tokens + (int64_t)b0 * (K + 1);
-            if (aux) {
-                a.aux_pt = aux->p_target ? aux->p_target + (int64_t)b0 * K : nullptr;
-                a.aux_pd = aux->p_draft ? aux->p_draft + (int64_t)b0 * K : nullptr;
-                a.aux_z = aux->residual_mass ? aux->residual_mass + b0 : nullptr;
-                a.error_word = aux->error_word;
-            }
-            a.seqctl = reinterpret_cast<SeqCtl *>(ws);
-            a.part = reinterpret_cast<RowPart *>(ws + p.foff_part);
-            a.top = reinterpret_cast<Top4 *>(ws + p.foff_top);
-            a.state = reinterpret_cast<SeqState *>(ws + p.foff_state);
-            a.res = reinterpret_cast<double *>(ws + p.foff_res);
-            a.zx = reinterpret_cast<float2 *>(ws + p.foff_zx);
-            launch_fused(a, p, s);
-        }
-    } else {
-        Args a = base_args(p, workspace);
-        a.target = static_cast<const char *>(target_logits);
-        a.draft = static_cast<const char *>(draft_logits);
-        a.tokens = draft_tokens;
-        a.temperature = temperature;
+    // With no draft logits every sequence is greedy or fails, unless K == 0,
+    // where sampling sequences draw from target row 0: draw only if needed.
+    const bool draw = !(K > 0 && draft_logits == nullptr);
+    for (int32_t b0 = 0; b0 < B; b0 += p.sB) {
+        const int32_t nb = std::min(p.sB, B - b0);
+        Args a = sub_args(p, workspace, b0, nb);
+        a.target = static_cast<const char *>(target_logits) + (int64_t)b0 * (K + 1) * p.row_bytes;
+        a.draft = draft_logits ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
+                               : nullptr;
+        a.tokens = draft_tokens ? draft_tokens + (int64_t)b0 * K : nullptr;
+        a.temperature = temperature + b0;
         a.seed = seed;
         a.beta = beta;
-        a.weighted = weighted ? 1 : 0;
-        a.accepted_len = accepted_len;
-        a.out_tokens = out_tokens;
+        a.weighted = (beta < 1.f && K > 0) ? 1 : 0;
+        a.accepted_len = accepted_len + b0;
+        a.out_tokens = out_tokens + (int64_t)b0 * (K + 1);
         if (aux) {
-            a.aux_pt = aux->p_target;
-            a.aux_pd = aux->p_draft;
-            a.aux_z = aux->residual_mass;
+            a.aux_pt = aux->p_target ? aux->p_target + (int64_t)b0 * K : nullptr;
+            a.aux_pd = aux->p_draft ? aux->p_draft + (int64_t)b0 * K : nullptr;
+            a.aux_z = aux->residual_mass ? aux->residual_mass + b0 : nullptr;
             a.error_word = aux->error_word;
         }
-        // With no draft logits every sequence is greedy or fails; nothing to draw.
-        const bool draw = !(K > 0 && draft_logits == nullptr);
-        launch_multipass(a, p, s, draw);
+        launch_verify(a, s, draw);
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -216,14 +153,6 @@ size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype
     return p.bytes;
 }
 
-int32_t spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream)
-{
-    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < sv::kPersistBytes)
-        return SV_EWORKSPACE;
-    sv::launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream));
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
-}
-
 int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
                     uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
@@ -231,17 +160,7 @@ int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     const sv_aux *aux, void *stream)
 {
     return sv::verify(target_logits, draft_logits, draft_tokens, B, K, V, dtype, seed, temperature,
-                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream, true);
-}
-
-int32_t spec_verify_multipass(const void *target_logits, const void *draft_logits,
-                              const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
-                              int32_t dtype, uint64_t seed, const float *temperature, float beta,
-                              int32_t *accepted_len, int32_t *out_tokens, void *workspace,
-                              size_t workspace_bytes, const sv_aux *aux, void *stream)
-{
-    return sv::verify(target_logits, draft_logits, draft_tokens, B, K, V, dtype, seed, temperature,
-                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream, false);
+                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream);
 }
 
 int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,
@@ -258,13 +177,16 @@ int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32
     if (!sv::make_plan(rows, 0, V, dtype, &p)) return SV_EINVAL;
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
         return SV_EWORKSPACE;
-    sv::Args a = sv::base_args(p, workspace);
-    a.target = static_cast<const char *>(logits);
-    a.temperature = temperature;
-    a.rs_max = row_max;
-    a.rs_logsum = row_logsum;
-    a.rs_argmax = row_argmax;
-    sv::launch_rowstats(a, p, static_cast<hipStream_t>(stream));
+    for (int32_t r0 = 0; r0 < rows; r0 += p.sB) {
+        const int32_t nr = std::min(p.sB, rows - r0);
+        sv::Args a = sv::sub_args(p, workspace, r0, nr);
+        a.target = static_cast<const char *>(logits) + (int64_t)r0 * p.row_bytes;
+        a.temperature = temperature + r0;
+        a.rs_max = row_max + r0;
+        a.rs_logsum = row_logsum + r0;
+        a.rs_argmax = row_argmax + r0;
+        sv::launch_rowstats(a, static_cast<hipStream_t>(stream));
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 

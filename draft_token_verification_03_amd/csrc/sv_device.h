@@ -421,6 +421,11 @@ __device__ __forceinline__ void top_insert(Top4 &t, float v, int i)
     }
 }
 
+__device__ __forceinline__ bool top_has(const Top4 &t, int i)
+{
+    return i != INT_MAX && (t.i[0] == i || t.i[1] == i || t.i[2] == i || t.i[3] == i);
+}
+
 // Merge the per-lane lists of a wave into the wave's top-4 (every lane gets it).
 __device__ __forceinline__ Top4 wave_top4(Top4 t)
 {

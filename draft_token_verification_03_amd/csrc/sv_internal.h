@@ -13,17 +13,12 @@ namespace sv {
 
 constexpr int kMaxK = 128;               // drafted positions per sequence
 constexpr int kMaxSlots = 2 * kMaxK + 1;
-constexpr int kMaxChunks = 1024;         // streaming chunks per row (multi-pass path)
-constexpr int kFillBlocks = 2048;        // workgroups a streaming grid aims for
-constexpr int kFusedFill = 8192;         // streaming items the fused grid aims for
-constexpr int kMaxSeqPerLaunch = 8192;   // sequences per fused launch
-constexpr int kFusedU = 4;               // fused path: 16-byte vectors per thread per row chunk
-constexpr int kFusedMaxK = 16;           // fused path: drafted positions per sequence
-constexpr int kStageBytes = 12 * 1024;   // fused path: LDS staging of one sequence's partials
+constexpr int kMaxChunks = 1024;         // streaming chunks per row
+constexpr int kFillBlocks = 2048;        // workgroups the streaming grid aims for
+constexpr int kResFill = 2048;           // workgroups the residual grid aims for
+constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
+constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials (accept)
 constexpr uint32_t kPurposeAccept = 0u, kPurposeBonus = 1u;
-
-// Error bit for a wait that exceeded its spin budget (fused path only).
-constexpr int kErrTimeout = 32;
 
 // One (row, chunk) partial of the streaming pass.
 struct RowPart {
@@ -49,101 +44,49 @@ struct SeqState {
 };
 static_assert(sizeof(SeqState) == 64, "SeqState layout");
 
-// Control words of one sequence on the fused path, one 128-byte line each so
-// that different sequences' atomics never share a line.  They are zero before
-// a launch and returned to zero by their last users.
-struct SeqCtl {
-    uint32_t count;   // streaming items of the sequence that have published
-    uint32_t rcount;  // draw items that have published a residual chunk sum
-    uint32_t dcount;  // draw items done
-    uint32_t flag;    // 1 once the accept scan of the sequence is done
-    uint32_t pad[28];
-};
-static_assert(sizeof(SeqCtl) == 128, "SeqCtl layout");
-constexpr size_t kPersistBytes = sizeof(SeqCtl) * (size_t)kMaxSeqPerLaunch;
-
+// Launch geometry and workspace layout for one sub-batch of sB sequences.
 struct Plan {
     int32_t B, K, V, dtype, vec, R;
+    int32_t sB;             // sequences per sub-batch: min(B, kMaxSeqPerLaunch)
     int32_t nvec;           // 16-byte vectors per row (the last may be partial)
     int64_t row_bytes;
-    // multi-pass path
     int32_t nc, cvec;       // streaming chunks per row, vectors per chunk
     int32_t ncr, rvec;      // residual chunks per sequence, vectors per residual chunk
-    size_t off_part, off_top, off_seq, off_res, mp_bytes;
-    // fused path (per launch of at most kMaxSeqPerLaunch sequences)
-    int32_t fu;             // 16-byte vectors per thread per sub-tile
-    int32_t fchunks;        // draw chunks (one sub-tile each) per row
-    int32_t fspan;          // sub-tiles per streaming chunk
-    int32_t fschunks;       // streaming chunks per row
-    int32_t fitems;         // streaming items per sequence: (K + 1) * fschunks
-    int32_t fB;             // sequences per launch
-    size_t foff_part, foff_top, foff_state, foff_res, foff_zx, f_bytes;
-    bool fused_shape_ok;
+    size_t off_part, off_top, off_seq, off_res;
     size_t bytes;           // total workspace
 };
 
 bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p);
 
 struct Args {
-    const char *target;
+    const char *target;     // the sub-batch's first target row
     const char *draft;
     const int32_t *tokens;
     const float *temperature;
     int32_t B, K, V, R, nvec, nc, cvec, ncr, rvec, dtype;
+    int32_t b0;             // index of the sub-batch's first sequence in the call
     int64_t row_bytes;
     uint64_t seed;
     float beta;
     int32_t weighted;
     int32_t *accepted_len;
     int32_t *out_tokens;
-    RowPart *part;
-    Top4 *top;
-    SeqState *seq;
-    double *res;
+    RowPart *part;          // [sB][R][nc]
+    Top4 *top;              // [sB][K][nc]
+    SeqState *seq;          // [sB]
+    double *res;            // [sB][ncr]
     float *aux_pt, *aux_pd, *aux_z;
-    int32_t *error_word;
+    int32_t *error_word;    // error bits are OR-ed in
     // row-statistics entry point outputs
     float *rs_max;
     double *rs_logsum;
     int32_t *rs_argmax;
 };
 
-struct FusedArgs {
-    const char *target;
-    const char *draft;
-    const int32_t *tokens;
-    const float *temperature;
-    int32_t B, K, V, nvec;
-    int32_t chunks;        // draw chunks per row (kBlock * U vectors each)
-    int32_t sspan;         // sub-tiles per streaming chunk
-    int32_t schunks;       // streaming chunks per row
-    int32_t stream_items, b0;
-    int64_t row_bytes;
-    uint64_t seed;
-    float beta;
-    int32_t weighted;
-    uint32_t spin_limit;
-    int32_t *accepted_len;
-    int32_t *out_tokens;
-    float *aux_pt, *aux_pd, *aux_z;
-    int32_t *error_word;   // error bits are OR-ed in
-    SeqCtl *seqctl;
-    RowPart *part;   // [B][2K+1][schunks]
-    Top4 *top;       // [B][K][schunks]
-    SeqState *state; // [B]
-    double *res;     // [B][chunks]
-    float2 *zx;      // [B][K]: (target, draft) logit of the drafted token
-};
-
-// Multi-pass path (any shape).
-void launch_multipass(const Args &a, const Plan &p, hipStream_t s, bool draw);
-void launch_rowstats(const Args &a, const Plan &p, hipStream_t s);
+// Launchers of one sub-batch: the verify step (`draw` false skips the residual
+// and bonus steps), the row-statistics entry point, the uniforms.
+void launch_verify(const Args &a, hipStream_t s, bool draw);
+void launch_rowstats(const Args &a, hipStream_t s);
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s);
-void launch_zero(void *ptr, size_t bytes, hipStream_t s);
-
-// Fused single-launch path: returns false (nothing enqueued) when the shape or
-// the device's resident-workgroup capacity does not allow it.
-bool fused_capacity_ok(const Plan &p, bool weighted);
-void launch_fused(const FusedArgs &a, const Plan &p, hipStream_t s);
 
 }  // namespace sv

@@ -51,10 +51,9 @@
  * time need distinct workspaces.
  *
  * Workspace: a caller-owned device buffer of spec_verify_workspace_size()
- * bytes, 256-byte aligned.  Its first 1 MiB holds per-sequence control words
- * that must be zero before its first use (spec_verify_workspace_init, or any
- * zero fill) and that every completed call leaves zero again; the rest is
- * scratch.
+ * bytes, 256-byte aligned, used as scratch (row partials, per-sequence state,
+ * residual chunk sums).  Its contents before a call do not matter; a call
+ * that is still running owns it.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -82,8 +81,6 @@ extern "C" {
 #define SV_ERR_ROW 4            /* a used row has no finite maximum: outputs are -1     */
 #define SV_ERR_DRAFT_MASS 8     /* beta == 0 left a draft row with zero mass: outputs -1 */
 #define SV_ERR_NO_DRAFT 16      /* T > 0 but draft_logits is NULL: outputs are -1       */
-#define SV_ERR_TIMEOUT 32       /* an internal wait gave up (another kernel held the
-                                   GPU's workgroup slots); some bonus tokens are -1  */
 
 /* Optional per-call diagnostics; every field may be NULL. */
 typedef struct sv_aux {
@@ -100,13 +97,6 @@ typedef struct sv_aux {
 size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype);
 
 /*
- * Zero a workspace on `stream` (needed once, before its first use).
- * Returns SV_EWORKSPACE if it is NULL, not 256-byte aligned or smaller than
- * the control words.
- */
-int32_t spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
-
-/*
  * The verify step.
  *   target_logits  [B, K+1, V] dtype
  *   draft_logits   [B, K, V]   dtype; may be NULL when every temperature is 0
@@ -118,27 +108,16 @@ int32_t spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void
  *   workspace      device buffer of >= spec_verify_workspace_size(...) bytes
  *                  (see "Workspace" above)
  *   aux            host pointer to an sv_aux, or NULL
- * B == 0 is a no-op.  Returns SV_OK after enqueuing the work.  Shapes with
- * K <= 16 and rows short enough for one sequence's partials to fit on chip
- * run as a single launch; others take the multi-pass path below.
+ * B == 0 is a no-op.  Returns SV_OK after enqueuing the work: four kernel
+ * launches per sub-batch of at most 8192 sequences (streaming pass, accept
+ * scan, residual chunk sums, bonus draw), the last two skipped when
+ * draft_logits is NULL and K > 0.
  */
 int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
                     uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_aux *aux, void *stream);
-
-/*
- * The same operation, same arguments and same results, always computed by
- * the four-launch path (streaming pass, accept scan, residual sums, bonus
- * draw) that spec_verify falls back to.  It never touches the workspace's
- * control words.
- */
-int32_t spec_verify_multipass(const void *target_logits, const void *draft_logits,
-                              const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
-                              int32_t dtype, uint64_t seed, const float *temperature, float beta,
-                              int32_t *accepted_len, int32_t *out_tokens, void *workspace,
-                              size_t workspace_bytes, const sv_aux *aux, void *stream);
 
 /*
  * Per-row statistics of `rows` rows of V logits (the streaming pass of the

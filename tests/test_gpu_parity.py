@@ -37,14 +37,13 @@ def _say(msg: str) -> None:
     sys.stdout.flush()
 
 
-PATHS = ["fused", "multipass"]
 
 
-def run_gpu(sv, inp: dict, seed: int, draft_none: bool = False, path: str = "fused",
+def run_gpu(sv, inp: dict, seed: int, draft_none: bool = False,
             workspace=None) -> dict:
     acc, out, aux = sv.spec_verify(inp["target"], None if draft_none else inp["draft"],
                                    inp["tokens"], seed, inp["temperature"], inp["beta"], aux=True,
-                                   multipass=(path == "multipass"), workspace=workspace)
+                                   workspace=workspace)
     torch.cuda.synchronize()
     res = {"accepted_len": acc.cpu().numpy(), "out_tokens": out.cpu().numpy()}
     for k, v in aux.items():
@@ -53,9 +52,8 @@ def run_gpu(sv, inp: dict, seed: int, draft_none: bool = False, path: str = "fus
     return res
 
 
-def run_both(sv, oracle_mod, inp: dict, seed: int, ptol: float, draft_none: bool = False,
-             path: str = "fused") -> Report:
-    g = run_gpu(sv, inp, seed, draft_none, path)
+def run_both(sv, oracle_mod, inp: dict, seed: int, ptol: float, draft_none: bool = False) -> Report:
+    g = run_gpu(sv, inp, seed, draft_none)
     h = to_numpy_inputs(inp)
     if draft_none:
         h["draft"] = None
@@ -106,34 +104,32 @@ def test_row_stats_match_oracle(sv, oracle_mod, dtype):
                 assert abs(L_g - L_o) <= 1e-6 + 1e-12 * abs(L_o), (V, r, L_g, L_o)
 
 
-@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name,B,seeds", [
     ("C1", 1, 200), ("C2", 8, 25), ("C3", 64, 6), ("C4", 30, 4), ("C5", 24, 4),
 ])
-def test_workload_parity_reduced(sv, oracle_mod, name, B, seeds, path):
+def test_workload_parity_reduced(sv, oracle_mod, name, B, seeds):
     """Each named workload at full vocabulary and a batch the oracle finishes
     in seconds, over several input and Philox seeds."""
     w = WORKLOADS[name].sized(B=B)
     rep = Report()
     for s in range(seeds):
-        _say(f"parity {name} B={B} seed={s} path={path}")
+        _say(f"parity {name} B={B} seed={s}")
         inp = make_inputs(w, seed=100 + s, device="cuda")
         rep.merge(run_both(sv, oracle_mod, inp, seed=s, ptol=_ptol(w.dtype),
-                           draft_none=w.greedy, path=path))
+                           draft_none=w.greedy))
     _say(f"{name}: {rep.sequences} seqs {rep.decisions} decisions {rep.flips} flips "
          f"max|dp| {rep.max_p_err:.2e} max|dZ| {rep.max_z_err:.2e}")
     rep.check()
 
 
-@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5"])
-def test_workload_parity_full_size_sampled(sv, oracle_mod, name, path):
+def test_workload_parity_full_size_sampled(sv, oracle_mod, name):
     """Full-size batch, one launch as the benchmark times it; 16 sequences
     (with their global Philox index) are re-verified by the oracle."""
     w = WORKLOADS[name]
-    _say(f"full-size {name} {w.tag()} path={path}")
+    _say(f"full-size {name} {w.tag()}")
     inp = make_inputs(w, seed=7, device="cuda")
-    g = run_gpu(sv, inp, seed=3, draft_none=w.greedy, path=path)
+    g = run_gpu(sv, inp, seed=3, draft_none=w.greedy)
     rng = np.random.default_rng(11)
     ids = np.sort(rng.choice(w.B, size=min(16, w.B), replace=False))
     if w.identical_every:
@@ -206,10 +202,9 @@ def _random_case(rng, B, K, V, spread=3.0, noise=0.7, argmax_frac=0.5):
     return tgt, drf, tokens
 
 
-@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 9, 31, 257, 2049, 10007, 70001])
-def test_ragged_and_tiny_vocab(sv, oracle_mod, dtype, V, path):
+def test_ragged_and_tiny_vocab(sv, oracle_mod, dtype, V):
     rng = np.random.default_rng(V)
     B, K = 24, 3
     tgt, drf, tok = _random_case(rng, B, K, V)
@@ -217,27 +212,25 @@ def test_ragged_and_tiny_vocab(sv, oracle_mod, dtype, V, path):
     for beta in (1.0, 0.5, 0.0):
         if beta == 0.0 and V <= 4:
             continue  # every draft token down-weighted to zero: undefined draft law
-        _say(f"ragged dtype={dtype} V={V} beta={beta} path={path}")
+        _say(f"ragged dtype={dtype} V={V} beta={beta}")
         inp = _inputs_from_numpy(tgt, drf, tok, temps, beta, dtype)
-        run_both(sv, oracle_mod, inp, seed=V, ptol=_ptol(dtype), path=path).check()
+        run_both(sv, oracle_mod, inp, seed=V, ptol=_ptol(dtype)).check()
 
 
-@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("K", [0, 1, 2, 7, 16, 20])
-def test_draft_lengths(sv, oracle_mod, K, path):
+def test_draft_lengths(sv, oracle_mod, K):
     rng = np.random.default_rng(40 + K)
     B, V = 40, 3001
     tgt, drf, tok = _random_case(rng, B, K, V)
     temps = rng.uniform(0.5, 1.2, size=B).astype(np.float32)
     temps[::5] = 0.0
     for dtype in ("fp32", "bf16"):
-        _say(f"draft-length K={K} dtype={dtype} path={path}")
+        _say(f"draft-length K={K} dtype={dtype}")
         inp = _inputs_from_numpy(tgt, drf, tok, temps, 0.5, dtype)
-        run_both(sv, oracle_mod, inp, seed=K, ptol=_ptol(dtype), path=path).check()
+        run_both(sv, oracle_mod, inp, seed=K, ptol=_ptol(dtype)).check()
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod, path):
+def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod):
     rng = np.random.default_rng(3)
     B, K, V = 16, 5, 50000
     tgt = (rng.normal(size=(B, K + 1, V)) * 3).astype(np.float32)
@@ -245,15 +238,14 @@ def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod, path):
     drf = np.ascontiguousarray(tgt[:, :K])
     tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
     for dtype in ("fp32", "bf16"):
-        _say(f"identical rows dtype={dtype} path={path}")
+        _say(f"identical rows dtype={dtype}")
         inp = _inputs_from_numpy(tgt, drf, tok, np.full(B, 0.8, np.float32), 1.0, dtype)
-        g = run_gpu(sv, inp, seed=9, path=path)
+        g = run_gpu(sv, inp, seed=9)
         assert np.all(g["accepted_len"] == K)
-        run_both(sv, oracle_mod, inp, seed=9, ptol=_ptol(dtype), path=path).check()
+        run_both(sv, oracle_mod, inp, seed=9, ptol=_ptol(dtype)).check()
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_error_paths(sv, oracle_mod, path):
+def test_error_paths(sv, oracle_mod):
     rng = np.random.default_rng(5)
     B, K, V = 8, 3, 777
     tgt, drf, tok = _random_case(rng, B, K, V)
@@ -262,19 +254,18 @@ def test_error_paths(sv, oracle_mod, path):
     temps = np.array([1.0, 1.0, 1.0, -1.0, np.nan, np.inf, 0.0, 0.9], dtype=np.float32)
     tgt[7, 1, :] = -np.inf  # a row without a finite maximum
     for dtype in ("fp32", "bf16"):
-        _say(f"error paths dtype={dtype} path={path}")
+        _say(f"error paths dtype={dtype}")
         inp = _inputs_from_numpy(tgt, drf, tok, temps, 1.0, dtype)
-        rep = run_both(sv, oracle_mod, inp, seed=1, ptol=_ptol(dtype), path=path)
+        rep = run_both(sv, oracle_mod, inp, seed=1, ptol=_ptol(dtype))
         rep.check()
     # no draft logits while a sequence samples
     inp = _inputs_from_numpy(tgt, None, tok, np.array([0.0] * 7 + [1.0], np.float32), 1.0, "fp32")
-    g = run_gpu(sv, inp, seed=0, draft_none=True, path=path)
+    g = run_gpu(sv, inp, seed=0, draft_none=True)
     assert g["error_word"] & sv.SV_ERR_NO_DRAFT
     assert np.all(g["out_tokens"][7] == -1)
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_extreme_logits_and_unaligned_rows(sv, oracle_mod, path):
+def test_extreme_logits_and_unaligned_rows(sv, oracle_mod):
     # Logits spanning +-1600 (exp underflow everywhere but the top).  Drafts are
     # the draft argmax, i.e. draws from the near one-hot draft law: a token the
     # draft law gives ~0 mass would be rejected against a residual that is pure
@@ -285,21 +276,20 @@ def test_extreme_logits_and_unaligned_rows(sv, oracle_mod, path):
     tgt, drf, tok = _random_case(rng, B, K, V, spread=400.0, noise=30.0, argmax_frac=1.0)
     temps = rng.uniform(0.3, 2.0, size=B).astype(np.float32)
     for dtype in ("fp32", "bf16"):
-        _say(f"extreme/unaligned dtype={dtype} path={path}")
+        _say(f"extreme/unaligned dtype={dtype}")
         inp = _inputs_from_numpy(tgt, drf, tok, temps, 0.5, dtype)
-        run_both(sv, oracle_mod, inp, seed=2, ptol=_ptol(dtype), path=path).check()
+        run_both(sv, oracle_mod, inp, seed=2, ptol=_ptol(dtype)).check()
         # the same rows one element into a larger buffer: no row is 16-byte aligned
         for key in ("target", "draft"):
             t = inp[key]
             big = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
             big[1:].copy_(t.reshape(-1))
             inp[key] = big[1:].view(t.shape)
-        run_both(sv, oracle_mod, inp, seed=2, ptol=_ptol(dtype), path=path).check()
+        run_both(sv, oracle_mod, inp, seed=2, ptol=_ptol(dtype)).check()
 
 
-@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_small_residual_mass_is_accurate(sv, oracle_mod, dtype, path):
+def test_small_residual_mass_is_accurate(sv, oracle_mod, dtype):
     """Draft rows equal the target rows except that the drafted token x gets a
     draft probability ~1e-4 where the target gives it ~1e-9: x is rejected and
     the residual, p_t minus a draft law that differs from it by ~1e-4, has mass
@@ -315,9 +305,9 @@ def test_small_residual_mass_is_accurate(sv, oracle_mod, dtype, path):
     for b in range(B):
         for i in range(K):
             drf[b, i, x[b, i]] = np.float32(np.log(1e-4 * V * 1.65))  # q'(x) ~ 1e-4
-    _say(f"small residual mass dtype={dtype} path={path}")
+    _say(f"small residual mass dtype={dtype}")
     inp = _inputs_from_numpy(tgt, drf, x.astype(np.int32), np.full(B, 1.0, np.float32), 1.0, dtype)
-    g = run_gpu(sv, inp, seed=4, path=path)
+    g = run_gpu(sv, inp, seed=4)
     h = to_numpy_inputs(inp)
     o = oracle_mod.spec_verify(h["target"], h["draft"], h["tokens"], 4, h["temperature"], h["beta"])
     rej = o["accepted_len"] < K
@@ -329,44 +319,49 @@ def test_small_residual_mass_is_accurate(sv, oracle_mod, dtype, path):
             uniform=lambda b, pos, pur: oracle_mod.uniform(4, b, pos, pur)).check()
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_repeatable_and_scratch_contents_do_not_matter(sv, path):
-    """Repeated calls give identical outputs whatever the scratch part of the
-    workspace holds (its control words are left untouched)."""
+def test_repeatable_and_scratch_contents_do_not_matter(sv):
+    """Repeated calls give identical outputs whatever the workspace holds
+    before the call."""
     w = WORKLOADS["C5"].sized(B=64, V=20011)
     inp = make_inputs(w, seed=1, device="cuda")
     ws = sv.alloc_workspace(w.B, w.K, w.V, inp["target"].dtype, "cuda")
-    ctrl_bytes = 128 * 8192
     ref = None
     for rep in range(20):
-        ws[ctrl_bytes:].fill_(0xFF if rep % 2 else 0x00)
+        ws.fill_(0xFF if rep % 2 else 0x00)
         acc, out = sv.spec_verify(inp["target"], inp["draft"], inp["tokens"], 5,
-                                  inp["temperature"], inp["beta"], workspace=ws,
-                                  multipass=(path == "multipass"))
+                                  inp["temperature"], inp["beta"], workspace=ws)
         cur = (acc.cpu().numpy(), out.cpu().numpy())
         if ref is None:
             ref = cur
         assert np.array_equal(ref[0], cur[0]) and np.array_equal(ref[1], cur[1])
-    assert int(ws[:ctrl_bytes].count_nonzero()) == 0
 
 
-def test_fused_calls_leave_control_words_zero(sv, oracle_mod):
-    """Back-to-back single-launch calls of different batch sizes on one
-    workspace: every call returns the control words to zero, and each result
-    still matches the oracle."""
+def test_workspace_reused_across_batch_sizes(sv, oracle_mod):
+    """Back-to-back calls of different batch sizes on one workspace each match
+    the oracle."""
     w = WORKLOADS["C2"].sized(B=40, V=9001)
     ws = sv.alloc_workspace(w.B, w.K, w.V, torch.bfloat16, "cuda")
-    ctrl_bytes = 128 * 8192
     for i, B in enumerate((40, 3, 17, 40, 1)):
         inp = make_inputs(w.sized(B=B), seed=60 + i, device="cuda")
         g = run_gpu(sv, inp, seed=i, workspace=ws)
-        torch.cuda.synchronize()
-        assert int(ws[:ctrl_bytes].count_nonzero()) == 0
         h = to_numpy_inputs(inp)
         o = oracle_mod.spec_verify(h["target"], h["draft"], h["tokens"], i, h["temperature"],
                                    h["beta"])
         compare(g, o, h, i, ptol=2e-3,
                 uniform=lambda b, pos, pur, i=i: oracle_mod.uniform(i, b, pos, pur)).check()
+
+
+def test_batch_beyond_one_sub_batch(sv, oracle_mod):
+    """More sequences than one sub-batch of launches holds (8192): the call is
+    split into sub-batches that reuse the workspace; the uniforms stay keyed
+    on each sequence's index in the call."""
+    w = WORKLOADS["C5"].sized(B=9000, V=301)
+    inp = make_inputs(w, seed=71, device="cuda")
+    g = run_gpu(sv, inp, seed=5)
+    h = to_numpy_inputs(inp)
+    o = oracle_mod.spec_verify(h["target"], h["draft"], h["tokens"], 5, h["temperature"], h["beta"])
+    compare(g, o, h, 5, ptol=1e-5,
+            uniform=lambda b, pos, pur: oracle_mod.uniform(5, b, pos, pur)).check()
 
 
 def test_empty_batch(sv):
