@@ -39,7 +39,8 @@ class SpecVerifyError(RuntimeError):
 
 class _Aux(ctypes.Structure):
     _fields_ = [("p_target", ctypes.c_void_p), ("p_draft", ctypes.c_void_p),
-                ("residual_mass", ctypes.c_void_p), ("error_word", ctypes.c_void_p)]
+                ("residual_mass", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
+                ("pass_begin", ctypes.c_void_p), ("pass_end", ctypes.c_void_p)]
 
 
 _lib = None
@@ -111,64 +112,108 @@ def alloc_workspace(B: int, K: int, V: int, dtype: torch.dtype, device) -> torch
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+class Verifier:
+    """One verify step with its buffers bound once, for loops that run the
+    step repeatedly (a decode loop, a benchmark): each call only marshals the
+    seed and enqueues the kernels.
+
+    target [B, K+1, V] and draft [B, K, V] (or None if every temperature is 0)
+    are contiguous float32 or bfloat16 CUDA tensors; tokens [B, K] int32;
+    temperature a float or a [B] float32 tensor (0 = greedy); beta in [0, 1].
+    The outputs accepted_len [B] and out_tokens [B, K+1] (int32) are
+    allocated unless passed in, and so is the workspace.  With aux=True the
+    diagnostics p_target, p_draft, residual_mass and error_word are written
+    too (error_word is cleared before every call).
+    """
+
+    def __init__(self, target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
+                 temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
+                 accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
+                 aux: bool = False, stream=None):
+        if target.dim() != 3:
+            raise ValueError("target must be [B, K+1, V]")
+        B, K1, V = target.shape
+        K = K1 - 1
+        dev = target.device
+        code = _dtype_code(target)
+        if not target.is_contiguous():
+            raise ValueError("target must be contiguous")
+        if draft is not None:
+            if draft.shape != (B, K, V) or draft.dtype != target.dtype or not draft.is_contiguous():
+                raise ValueError("draft must be a contiguous [B, K, V] tensor of the target's dtype")
+        if tokens.shape != (B, K) or tokens.dtype != torch.int32 or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous [B, K] int32 tensor")
+        if not torch.is_tensor(temperature):
+            temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
+        if temperature.shape != (B,) or temperature.dtype != torch.float32:
+            raise ValueError("temperature must be a [B] float32 tensor")
+        temperature = temperature.contiguous()
+        if workspace is None:
+            workspace = alloc_workspace(B, K, V, target.dtype, dev)
+        if accepted_len is None:
+            accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        self.shape = (B, K, V)
+        self.accepted_len, self.out_tokens = accepted_len, out_tokens
+        # keep every buffer alive for as long as the bound call
+        self._keep = (target, draft, tokens, temperature, workspace)
+        self.aux = None
+        self._aux = _Aux()
+        if aux:
+            self.aux = {
+                "p_target": torch.empty((B, K), dtype=torch.float32, device=dev),
+                "p_draft": torch.empty((B, K), dtype=torch.float32, device=dev),
+                "residual_mass": torch.empty((B,), dtype=torch.float32, device=dev),
+                "error_word": torch.zeros((1,), dtype=torch.int32, device=dev),
+            }
+            self._aux.p_target = self.aux["p_target"].data_ptr()
+            self._aux.p_draft = self.aux["p_draft"].data_ptr()
+            self._aux.residual_mass = self.aux["residual_mass"].data_ptr()
+            self._aux.error_word = self.aux["error_word"].data_ptr()
+        self._fn = load_library().spec_verify
+        self._head = (_ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code)
+        self._mid = (_ptr(temperature), ctypes.c_float(float(beta)), _ptr(accepted_len),
+                     _ptr(out_tokens), _ptr(workspace), workspace.numel())
+        self._stream = _stream(stream)
+
+    def __call__(self, seed: int, pass_events=None):
+        """Enqueue one verify step with this Philox seed; returns
+        (accepted_len, out_tokens), plus the diagnostics dict when bound with
+        aux=True.  pass_events, a pair of torch.cuda.Event that have been
+        recorded once (so that they exist), are recorded on the stream right
+        before and after the streaming-pass launch."""
+        aux = self._aux
+        if self.aux is not None:
+            self.aux["error_word"].zero_()
+        if pass_events is not None:
+            aux.pass_begin = pass_events[0].cuda_event
+            aux.pass_end = pass_events[1].cuda_event
+        else:
+            aux.pass_begin = aux.pass_end = None
+        use_aux = self.aux is not None or pass_events is not None
+        _check(self._fn(*self._head, int(seed) & (2**64 - 1), *self._mid,
+                        ctypes.byref(aux) if use_aux else None, self._stream))
+        if self.aux is not None:
+            return self.accepted_len, self.out_tokens, self.aux
+        return self.accepted_len, self.out_tokens
+
+
 def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
                 seed: int, temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
                 accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
                 aux: bool = False, stream=None):
-    """Verify K drafted tokens per sequence.
+    """Verify K drafted tokens per sequence (one call of the C entry point).
 
-    target [B, K+1, V] and draft [B, K, V] (or None if every temperature is 0)
-    are float32 or bfloat16 CUDA tensors; tokens [B, K] int32; temperature a
-    float or a [B] float32 tensor (0 = greedy); beta in [0, 1].  Returns
-    (accepted_len [B] int32, out_tokens [B, K+1] int32), plus a dict of
-    diagnostics (p_target, p_draft, residual_mass, error_word) if aux=True.
-    The work is enqueued on `stream` (default: the current stream); a
-    workspace of at least workspace_size(B, K, V, dtype) bytes may be passed
-    in (e.g. from alloc_workspace) to avoid an allocation per call.
+    Arguments as for Verifier.  Returns (accepted_len [B] int32, out_tokens
+    [B, K+1] int32), plus a dict of diagnostics (p_target, p_draft,
+    residual_mass, error_word) if aux=True.  The work is enqueued on `stream`
+    (default: the current stream); a workspace of at least
+    workspace_size(B, K, V, dtype) bytes may be passed in (e.g. from
+    alloc_workspace) to avoid an allocation per call.
     """
-    if target.dim() != 3:
-        raise ValueError("target must be [B, K+1, V]")
-    B, K1, V = target.shape
-    K = K1 - 1
-    dev = target.device
-    code = _dtype_code(target)
-    if not target.is_contiguous():
-        raise ValueError("target must be contiguous")
-    if draft is not None:
-        if draft.shape != (B, K, V) or draft.dtype != target.dtype or not draft.is_contiguous():
-            raise ValueError("draft must be a contiguous [B, K, V] tensor of the target's dtype")
-    if tokens.shape != (B, K) or tokens.dtype != torch.int32 or not tokens.is_contiguous():
-        raise ValueError("tokens must be a contiguous [B, K] int32 tensor")
-    if not torch.is_tensor(temperature):
-        temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
-    if temperature.shape != (B,) or temperature.dtype != torch.float32:
-        raise ValueError("temperature must be a [B] float32 tensor")
-    temperature = temperature.contiguous()
-    if workspace is None:
-        workspace = alloc_workspace(B, K, V, target.dtype, dev)
-    if accepted_len is None:
-        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    aux_t = None
-    aux_s = None
-    if aux:
-        aux_t = {
-            "p_target": torch.empty((B, K), dtype=torch.float32, device=dev),
-            "p_draft": torch.empty((B, K), dtype=torch.float32, device=dev),
-            "residual_mass": torch.empty((B,), dtype=torch.float32, device=dev),
-            "error_word": torch.zeros((1,), dtype=torch.int32, device=dev),
-        }
-        aux_s = _Aux(aux_t["p_target"].data_ptr(), aux_t["p_draft"].data_ptr(),
-                     aux_t["residual_mass"].data_ptr(), aux_t["error_word"].data_ptr())
-    status = load_library().spec_verify(
-        _ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code, int(seed) & (2**64 - 1),
-        _ptr(temperature), float(beta), _ptr(accepted_len), _ptr(out_tokens), _ptr(workspace),
-        workspace.numel(), ctypes.byref(aux_s) if aux_s is not None else None, _stream(stream))
-    _check(status)
-    if aux:
-        return accepted_len, out_tokens, aux_t
-    return accepted_len, out_tokens
+    return Verifier(target, draft, tokens, temperature, beta, workspace=workspace,
+                    accepted_len=accepted_len, out_tokens=out_tokens, aux=aux, stream=stream)(seed)
 
 
 def row_stats(logits: torch.Tensor, temperature, *, stream=None):

@@ -1,5 +1,4 @@
-// sv_accept.h -- row merges, the accept decision and the residual, shared by
-// the two-launch and the four-launch paths.
+// sv_accept.h -- row merges, the accept decision and the residual element.
 #pragma once
 
 #include "sv_internal.h"
@@ -10,7 +9,7 @@ __device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T !
 
 // ---------------------------------------------------------------------------
 // Wave-level merges of one row's chunk partials `p[0..nc)` (lanes stride the
-// chunks; the accept kernel stages them in LDS).  The same code merges target and draft rows, so equal rows merge to
+// chunks; the tail kernel stages them in LDS).  The same code merges target and draft rows, so equal rows merge to
 // bitwise-equal statistics.
 
 __device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, float &M, double &S)
@@ -118,23 +117,67 @@ __device__ __forceinline__ bool decide(float T, float mt, double St, float md, d
 // Speculative Decoding", "Key claims", the residual max(p_t - p_d, 0)):
 // p_t in mode 2; in mode 1
 //   r(v) = max(p_t(v) - q'(v), 0) = p_t(v) * (1 - 2^d(v))  for d(v) < 0, else 0,
+// both returned times S_t (p_t(v) S_t = exp2((z_t(v) - m_t) log2e / T)): a
+// factor common to the whole row, which cancels in the inverse CDF;
 //   d(v) = log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) log2e / T + k2 (+ log2 beta),
-// with d formed in fp64 and 1 - 2^d by expm1, so r keeps its relative
-// accuracy when p_t and q' nearly cancel (small residual mass).  The
-// difference p_t - q' taken in fp32 would carry an absolute error of ~1e-7 of
-// p_t, which for a residual mass Z of 0.1 is already 1e-6 of Z.
+// so r keeps its relative accuracy when p_t and q' nearly cancel (small
+// residual mass), where p_t - q' taken in fp32 would carry an absolute error
+// of ~1e-7 of p_t.  d is formed in fp32 from constants split into hi + lo
+// parts: fma(delta, c_hi, k_hi) rounds once, so d carries an error of a few
+// ulp of d itself, not of its terms.
+
+struct ResidualScale {
+    float c_hi, c_lo;    // log2e / T
+    float k_hi, k_lo;    // k2
+    float kt_hi, kt_lo;  // k2 + log2 beta (draft top-4 tokens)
+};
+
+__device__ __forceinline__ ResidualScale make_residual_scale(const SeqState &st, const ExpScale &e)
+{
+    ResidualScale r;
+    r.c_hi = e.hi;
+    r.c_lo = e.lo;
+    r.k_hi = (float)st.k2;
+    r.k_lo = (float)(st.k2 - (double)r.k_hi);
+    const double kt = st.k2 + (double)st.lbeta;  // -inf when beta == 0
+    r.kt_hi = (float)kt;
+    r.kt_lo = isfinite(kt) ? (float)(kt - (double)r.kt_hi) : 0.f;
+    return r;
+}
+
+// 1 - 2^d for d < 0, to a few ulp: a degree-9 Taylor series of -expm1(d ln2)
+// for d > -1 (truncation below 1e-8 relative), 1 - exp2(d) below, where
+// 2^d <= 1/2 keeps the subtraction well conditioned.
+__device__ __forceinline__ float one_minus_exp2(float d)
+{
+    const float y = d * 0.693147180559945f;
+    float p = __builtin_fmaf(y, 1.f / 362880.f, 1.f / 40320.f);
+    p = __builtin_fmaf(y, p, 1.f / 5040.f);
+    p = __builtin_fmaf(y, p, 1.f / 720.f);
+    p = __builtin_fmaf(y, p, 1.f / 120.f);
+    p = __builtin_fmaf(y, p, 1.f / 24.f);
+    p = __builtin_fmaf(y, p, 1.f / 6.f);
+    p = __builtin_fmaf(y, p, 0.5f);
+    p = __builtin_fmaf(y, p, 1.f);
+    const float series = -(y * p);
+    const float direct = 1.f - __builtin_amdgcn_exp2f(d);
+    return d > -1.f ? series : direct;
+}
 
 template <bool TOP>
 __device__ __forceinline__ float residual_at(float zt, float zd, int v, const SeqState &st,
-                                             const ExpScale &e, int mode)
+                                             const ExpScale &e, const ResidualScale &rs, int mode)
 {
-    const float pt = exp_scaled(zt, st.m_t, e) * st.inv_st;
+    const float pt = exp_scaled(zt, st.m_t, e);  // p_t(v) * S_t
     if (mode == 2) return pt;
-    double d = ((double)zd - (double)zt) * e.c64 + st.k2;
-    if (TOP && (v == st.top[0] || v == st.top[1] || v == st.top[2] || v == st.top[3]))
-        d += (double)st.lbeta;
-    if (!(d < 0.0)) return 0.f;  // q' >= p_t, or a masked target token
-    return pt * -expm1f((float)d * 0.6931471805599453f);
+    const float delta = zd - zt;
+    bool top = false;
+    if (TOP) top = v == st.top[0] || v == st.top[1] || v == st.top[2] || v == st.top[3];
+    const float khi = top ? rs.kt_hi : rs.k_hi;
+    const float klo = top ? rs.kt_lo : rs.k_lo;
+    const float d = __builtin_fmaf(delta, rs.c_hi, khi) + __builtin_fmaf(delta, rs.c_lo, klo);
+    if (!(d < 0.f)) return 0.f;  // q' >= p_t, or a masked target token
+    return pt * one_minus_exp2(d);
 }
 
 }  // namespace sv

@@ -25,7 +25,7 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     p->nvec = (int32_t)(((int64_t)V + p->vec - 1) / p->vec);
 
     // streaming: ~kFillBlocks workgroups per sub-batch, >= one vector per
-    // thread, and one sequence's partials and top-4 lists within the accept
+    // thread, and one sequence's partials and top-4 lists within the tail
     // kernel's LDS staging
     const int64_t rows = (int64_t)p->sB * p->R;
     int64_t nc = (kFillBlocks + rows - 1) / rows;
@@ -36,14 +36,19 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     nc = std::max<int64_t>(nc, 1);
     p->cvec = (int32_t)((p->nvec + nc - 1) / nc);
     p->nc = (p->nvec + p->cvec - 1) / p->cvec;
-    // residual: chunks of kBlock..kBlock*kLoads vectors, ~kFillBlocks workgroups
-    const int64_t ncr_want = (kResFill + p->sB - 1) / p->sB;
-    int64_t rvec = (p->nvec + ncr_want - 1) / ncr_want;
-    rvec = std::max<int64_t>(rvec, kBlock);
-    rvec = std::min<int64_t>(rvec, (int64_t)kBlock * kLoads);
-    p->rvec = (int32_t)rvec;
-    p->ncr = (int32_t)((p->nvec + rvec - 1) / rvec);
-    if (rows * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ncr >= ((int64_t)1 << 31))
+    // residual: slots of gs units of kSlotVec vectors (kSlotUnits units, or
+    // single units when a small batch needs the finer split to fill the
+    // grid), at most kMaxResSlots per row; ~kResFill workgroups in all
+    const int64_t units = (p->nvec + kSlotVec - 1) / kSlotVec;
+    const int64_t ng_fill = (kResFill + p->sB - 1) / p->sB;
+    int64_t gs = (units / kSlotUnits >= ng_fill) ? kSlotUnits : 1;
+    gs = std::max<int64_t>(gs, (units + kMaxResSlots - 1) / kMaxResSlots);
+    p->gs = (int32_t)gs;
+    p->nslot = (int32_t)((units + gs - 1) / gs);
+    p->ng = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ng_fill, p->nslot));
+    p->spg = (p->nslot + p->ng - 1) / p->ng;
+    p->ng = (p->nslot + p->spg - 1) / p->spg;
+    if (rows * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ng >= ((int64_t)1 << 31))
         return false;
     size_t off = 0;
     p->off_part = off;
@@ -52,8 +57,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     off = align256(off + sizeof(Top4) * (size_t)p->sB * K * p->nc);
     p->off_seq = off;
     off = align256(off + sizeof(SeqState) * (size_t)p->sB);
-    p->off_res = off;
-    off = align256(off + sizeof(double) * (size_t)p->sB * p->ncr);
+    p->off_slot = off;
+    off = align256(off + sizeof(double) * (size_t)p->sB * p->nslot);
     p->bytes = off;
     return true;
 }
@@ -70,15 +75,17 @@ static Args sub_args(const Plan &p, void *ws, int32_t b0, int32_t nb)
     a.nvec = p.nvec;
     a.nc = p.nc;
     a.cvec = p.cvec;
-    a.ncr = p.ncr;
-    a.rvec = p.rvec;
+    a.nslot = p.nslot;
+    a.gs = p.gs;
+    a.ng = p.ng;
+    a.spg = p.spg;
     a.dtype = p.dtype;
     a.b0 = b0;
     a.row_bytes = p.row_bytes;
     a.part = reinterpret_cast<RowPart *>(w + p.off_part);
     a.top = reinterpret_cast<Top4 *>(w + p.off_top);
     a.seq = reinterpret_cast<SeqState *>(w + p.off_seq);
-    a.res = reinterpret_cast<double *>(w + p.off_res);
+    a.slot = reinterpret_cast<double *>(w + p.off_slot);
     return a;
 }
 
@@ -115,9 +122,6 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
         return SV_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // With no draft logits every sequence is greedy or fails, unless K == 0,
-    // where sampling sequences draw from target row 0: draw only if needed.
-    const bool draw = !(K > 0 && draft_logits == nullptr);
     for (int32_t b0 = 0; b0 < B; b0 += p.sB) {
         const int32_t nb = std::min(p.sB, B - b0);
         Args a = sub_args(p, workspace, b0, nb);
@@ -137,7 +141,12 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
             a.aux_z = aux->residual_mass ? aux->residual_mass + b0 : nullptr;
             a.error_word = aux->error_word;
         }
-        launch_verify(a, s, draw);
+        hipEvent_t begin = nullptr, end = nullptr;
+        if (aux && b0 == 0) {
+            begin = static_cast<hipEvent_t>(aux->pass_begin);
+            end = static_cast<hipEvent_t>(aux->pass_end);
+        }
+        launch_verify(a, s, begin, end);
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }

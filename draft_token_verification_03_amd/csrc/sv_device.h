@@ -135,82 +135,6 @@ __device__ __forceinline__ uint4 load16_stream(const char *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Vector q of a row as floats; elements at or beyond V are -inf.
-template <int DT, bool STREAM = false>
-__device__ __forceinline__ void load_vec(const char *row, bool aligned, int q, int V,
-                                         float (&x)[Elt<DT>::kVec])
-{
-    constexpr int VEC = Elt<DT>::kVec;
-    const char *p = row + (size_t)q * 16;
-    uint4 raw;
-    const int first = q * VEC;
-    if (aligned) {
-        raw = STREAM ? load16_stream(p) : *reinterpret_cast<const uint4 *>(p);
-    } else {
-        const int valid = min(VEC, V - first);
-        const uint32_t sh = (uint32_t)((uintptr_t)p & 15);
-        raw = load16_unaligned(p, sh + (uint32_t)valid * Elt<DT>::kBytes > 16u);
-    }
-    Elt<DT>::unpack(raw, x);
-    if (first + VEC > V) {
-#pragma unroll
-        for (int k = 0; k < VEC; ++k)
-            if (first + k >= V) x[k] = -INFINITY;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Data handed between workgroups.  The L2 caches of the XCDs are not coherent
-// with each other, and the fences that would make plain stores visible write
-// back or invalidate a whole L2, which serialises workgroups.  Instead every
-// word another workgroup reads is stored and loaded as a relaxed agent-scope
-// atomic (coherent across XCDs), and a producer drains its outstanding memory
-// operations before the counter update that publishes them.
-
-__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p)
-{
-    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void st_agent16(void *p, uint4 v)
-{
-    unsigned long long *q = reinterpret_cast<unsigned long long *>(p);
-    __hip_atomic_store(q, ((unsigned long long)v.y << 32) | v.x, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, ((unsigned long long)v.w << 32) | v.z, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint4 ld_agent16(const void *p)
-{
-    unsigned long long *q = reinterpret_cast<unsigned long long *>(const_cast<void *>(p));
-    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
-}
-
-template <class T>
-__device__ __forceinline__ void st_agent_obj(T *dst, const T &v)
-{
-    static_assert(sizeof(T) % 16 == 0, "16-byte granules");
-    const uint4 *src = reinterpret_cast<const uint4 *>(&v);
-#pragma unroll
-    for (int k = 0; k < (int)(sizeof(T) / 16); ++k) st_agent16(reinterpret_cast<uint4 *>(dst) + k, src[k]);
-}
-
-// Wait until every memory operation this wave issued has completed.
-__device__ __forceinline__ void drain_memory()
-{
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // ---------------------------------------------------------------------------
 // Exponent scale log2(e)/T split as c_hi + c_lo: c_hi is rounded toward zero
 // so c_lo >= 0, and c_lo is kept strictly positive so that -inf logits give
@@ -262,6 +186,13 @@ __device__ __forceinline__ int wave_min_int(int v)
     return v;
 }
 
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 __device__ __forceinline__ int wave_max_int(int v)
 {
 #pragma unroll
@@ -288,6 +219,7 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i)
     }
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -296,11 +228,12 @@ __device__ __forceinline__ float block_max(float v, float *lds)
     __syncthreads();
     float r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = fmaxf(r, lds[w]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ double block_sum(double v, double *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -309,11 +242,12 @@ __device__ __forceinline__ double block_sum(double v, double *lds)
     __syncthreads();
     double r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r += lds[w];
+    for (int w = 1; w < NW; ++w) r += lds[w];
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_min_int(int v, int *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -322,11 +256,12 @@ __device__ __forceinline__ int block_min_int(int v, int *lds)
     __syncthreads();
     int r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = min(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = min(r, lds[w]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_max_int(int v, int *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -335,11 +270,12 @@ __device__ __forceinline__ int block_max_int(int v, int *lds)
     __syncthreads();
     int r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = max(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = max(r, lds[w]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ void block_argmax(float &v, int &i, float *ldsv, int *ldsi)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -352,7 +288,7 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *ldsv, int 
     v = ldsv[0];
     i = ldsi[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
+    for (int w = 1; w < NW; ++w)
         if (better(ldsv[w], ldsi[w], v, i)) {
             v = ldsv[w];
             i = ldsi[w];
@@ -362,6 +298,7 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *ldsv, int 
 
 // Exclusive prefix sum over the workgroup in thread order; `total` receives
 // the sum of all values.
+template <int NW = kWaves>
 __device__ __forceinline__ double block_exclusive_scan(double v, double &total, double *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -379,7 +316,7 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double &total, 
     for (int w = 0; w < wave; ++w) off += lds[w];
     double tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += lds[w];
+    for (int w = 0; w < NW; ++w) tot += lds[w];
     __syncthreads();
     total = tot;
     return off + exc;

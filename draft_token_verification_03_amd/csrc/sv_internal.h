@@ -15,9 +15,12 @@ constexpr int kMaxK = 128;               // drafted positions per sequence
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kMaxChunks = 1024;         // streaming chunks per row
 constexpr int kFillBlocks = 2048;        // workgroups the streaming grid aims for
-constexpr int kResFill = 2048;           // workgroups the residual grid aims for
 constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
-constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials (accept)
+constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials
+constexpr int kResFill = 1024;           // workgroups the residual grid aims for (one round)
+constexpr int kSlotVec = 64;             // 16-byte vectors per residual slot unit (one per lane)
+constexpr int kSlotUnits = 4;            // units per slot when the batch alone fills the grid
+constexpr int kMaxResSlots = 4096;       // residual slots per row (coarser slots beyond)
 constexpr uint32_t kPurposeAccept = 0u, kPurposeBonus = 1u;
 
 // One (row, chunk) partial of the streaming pass.
@@ -28,19 +31,18 @@ struct RowPart {
                   // draft row, over the chunk's elements outside the chunk's top-4
 };
 
-// Per-sequence outcome of the accept scan, read by the residual and bonus steps.
+// Per-sequence outcome of the accept scan, handed to the bonus step.
 struct SeqState {
     int32_t n;     // accepted drafts
     int32_t mode;  // 0: nothing to draw, 1: residual max(p_t - q', 0), 2: p_t alone
     float m_t, m_d;
     double k2;     // log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) log2e / T + k2 (+ log2 beta on the top-4)
-    float inv_st;  // 1 / S_t
-    float inv_sd;  // 1 / (S_d * N): the weighted draft normaliser
-    float beta;
+    float inv_st;  // 1 / S_t: residual masses are summed relative to p_t * S_t
     float u_bonus;
     int32_t top[4];
     float T;
     float lbeta;   // log2(beta), -inf for beta == 0
+    int32_t pad[2];
 };
 static_assert(sizeof(SeqState) == 64, "SeqState layout");
 
@@ -51,8 +53,9 @@ struct Plan {
     int32_t nvec;           // 16-byte vectors per row (the last may be partial)
     int64_t row_bytes;
     int32_t nc, cvec;       // streaming chunks per row, vectors per chunk
-    int32_t ncr, rvec;      // residual chunks per sequence, vectors per residual chunk
-    size_t off_part, off_top, off_seq, off_res;
+    int32_t nslot, gs;      // residual slots per row, kSlotVec-vector units per slot
+    int32_t ng, spg;        // residual workgroups per sequence, slots per workgroup
+    size_t off_part, off_top, off_seq, off_slot;
     size_t bytes;           // total workspace
 };
 
@@ -63,7 +66,7 @@ struct Args {
     const char *draft;
     const int32_t *tokens;
     const float *temperature;
-    int32_t B, K, V, R, nvec, nc, cvec, ncr, rvec, dtype;
+    int32_t B, K, V, R, nvec, nc, cvec, nslot, gs, ng, spg, dtype;
     int32_t b0;             // index of the sub-batch's first sequence in the call
     int64_t row_bytes;
     uint64_t seed;
@@ -74,7 +77,7 @@ struct Args {
     RowPart *part;          // [sB][R][nc]
     Top4 *top;              // [sB][K][nc]
     SeqState *seq;          // [sB]
-    double *res;            // [sB][ncr]
+    double *slot;           // [sB][nslot] residual mass of each slot
     float *aux_pt, *aux_pd, *aux_z;
     int32_t *error_word;    // error bits are OR-ed in
     // row-statistics entry point outputs
@@ -83,9 +86,9 @@ struct Args {
     int32_t *rs_argmax;
 };
 
-// Launchers of one sub-batch: the verify step (`draw` false skips the residual
-// and bonus steps), the row-statistics entry point, the uniforms.
-void launch_verify(const Args &a, hipStream_t s, bool draw);
+// Launchers of one sub-batch: the verify step (non-null events are recorded
+// around the streaming launch), the row-statistics entry point, the uniforms.
+void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 void launch_rowstats(const Args &a, hipStream_t s);
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s);
 

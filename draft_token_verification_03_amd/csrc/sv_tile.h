@@ -42,6 +42,15 @@ __device__ __forceinline__ void mask_raw(uint4 &r, int keep)
     }
 }
 
+// Element k (run-time index) of a raw vector.
+template <int DT>
+__device__ __forceinline__ float elt_of(uint4 r, int k)
+{
+    if (DT == 0) return __uint_as_float(word_of(r, k));
+    const uint32_t w = word_of(r, k >> 1);
+    return __uint_as_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
 // Element index of value k of this thread's vector u.
 __device__ __forceinline__ int elem_index(int q0, int u, int k, int vec)
 {
@@ -108,36 +117,68 @@ __device__ __forceinline__ void run_sum_tile(const uint4 (&r)[U], const ExpScale
     }
 }
 
-// Beta-weighted draft row: as run_sum_tile, and the lane keeps its top-4 by
-// (value desc, index asc).  An element entering the lane's top-4 is left out
-// of the sum and the element it evicts is added, so the sum covers the
-// lane's elements outside its top-4.
+// Beta-weighted draft row: as run_sum_tile, and the wave keeps the top-4 W of
+// the elements it has seen, by (value desc, index asc), identical in every
+// lane; the lanes' sums cover the wave's elements outside W.  W's 4th entry
+// is a threshold no later element reaches in most tiles (after t tiles a new
+// tile holds a candidate with probability ~4/t), so most tiles take the plain
+// sum.  A tile with a few candidates inserts them one at a time, in a
+// wave-uniform loop; the first tile, or one with many candidates (rising
+// rows), merges per-lane lists instead.  Whatever drops out of W, or never
+// enters it, joins lane 0's sum.
+
+__device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &out_v, int &out_i)
+{
+    if (!better(v, i, t.v[3], t.i[3])) return false;
+    out_v = t.v[3];
+    out_i = t.i[3];
+    top_insert(t, v, i);
+    return true;
+}
+
+constexpr int kSerialCandidates = 16;
+
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
-                                                 const ExpScale &e, RowRun &run, Top4 &t4)
+                                                 const ExpScale &e, RowRun &run, Top4 &W)
 {
     constexpr int VEC = Elt<DT>::kVec;
-    run_raise(run, wave_max(tile_lane_max<DT, U>(r)), e);
+    const int lane = threadIdx.x & 63;
+    const float mx = tile_lane_max<DT, U>(r);
+    run_raise(run, wave_max(mx), e);
+    const bool have_m = run.m != -INFINITY;
+    const float thr_v = W.v[3];
+    const int thr_i = W.i[3];
+    if (__ballot(mx >= thr_v) == 0ull) {  // no element can enter W
+        if (!have_m) return;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[VEC], ev[VEC];
+            Elt<DT>::unpack(r[u], x);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.m, e);
+#pragma unroll
+            for (int w = VEC / 2; w > 0; w >>= 1)
+#pragma unroll
+                for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
+            run.s += (double)ev[0];
+        }
+        return;
+    }
+    // candidates: elements that beat W's 4th entry; the others join the sum
+    uint32_t cmask = 0;  // bit u * VEC + k
+    int ncand = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float x[VEC], ev[VEC];
         Elt<DT>::unpack(r[u], x);
-        float mx = x[0];
 #pragma unroll
-        for (int k = 1; k < VEC; ++k) mx = fmaxf(mx, x[k]);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) ev[k] = run.m == -INFINITY ? 0.f : exp_scaled(x[k], run.m, e);
-        if (mx > t4.v[3] || (mx == t4.v[3] && t4.i[3] == INT_MAX)) {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                const int idx = elem_index(q0, u, k, VEC);
-                if (idx < V && better(x[k], idx, t4.v[3], t4.i[3])) {
-                    const float out_v = t4.v[3];
-                    const int out_i = t4.i[3];
-                    top_insert(t4, x[k], idx);
-                    ev[k] = (run.m != -INFINITY && out_i != INT_MAX) ? exp_scaled(out_v, run.m, e) : 0.f;
-                }
-            }
+        for (int k = 0; k < VEC; ++k) {
+            const int idx = elem_index(q0, u, k, VEC);
+            const bool c = idx < V && better(x[k], idx, thr_v, thr_i);
+            cmask |= (c ? 1u : 0u) << (u * VEC + k);
+            ncand += c ? 1 : 0;
+            ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.m, e);
         }
 #pragma unroll
         for (int w = VEC / 2; w > 0; w >>= 1)
@@ -145,6 +186,55 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
             for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
         run.s += (double)ev[0];
     }
+    double lost = 0.0;  // mass of candidates that end outside W
+    if (W.i[3] != INT_MAX && wave_sum_int(ncand) <= kSerialCandidates) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[VEC];
+            Elt<DT>::unpack(r[u], x);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                uint64_t bits = __ballot((cmask >> (u * VEC + k)) & 1u);
+                while (bits) {
+                    const int src = __ffsll((unsigned long long)bits) - 1;
+                    bits &= bits - 1;
+                    const float v = __shfl(x[k], src, 64);
+                    const int idx = __shfl(elem_index(q0, u, k, VEC), src, 64);
+                    float ov = v;
+                    int oi = idx;
+                    top_insert_out(W, v, idx, ov, oi);  // on insertion (ov, oi) is the evicted entry
+                    if (lane == 0 && oi != INT_MAX && ov != -INFINITY && have_m)
+                        lost += (double)exp_scaled(ov, run.m, e);
+                }
+            }
+        }
+    } else {
+        // per-lane lists of the candidates (lane 0 also holds W), then the
+        // wave's top-4 of all of them
+        Top4 t;
+        top_clear(t);
+        if (lane == 0) t = W;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[VEC];
+            Elt<DT>::unpack(r[u], x);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                if (!((cmask >> (u * VEC + k)) & 1u)) continue;
+                float ov = x[k];
+                int oi = elem_index(q0, u, k, VEC);
+                top_insert_out(t, x[k], oi, ov, oi);
+                if (oi != INT_MAX && ov != -INFINITY && have_m) lost += (double)exp_scaled(ov, run.m, e);
+            }
+        }
+        const Top4 nw = wave_top4(t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (t.i[k] != INT_MAX && t.v[k] != -INFINITY && !top_has(nw, t.i[k]) && have_m)
+                lost += (double)exp_scaled(t.v[k], run.m, e);
+        W = nw;
+    }
+    run.s += lost;
 }
 
 // Greedy row: the lane's (max, lowest index).
@@ -184,20 +274,20 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
 }
 
 // Weighted draft row chunk: block max M, the chunk's top-4 and the mass
-// outside it (lane-top entries that miss the chunk top-4 join the sum).
-__device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &t4, const ExpScale &e,
+// outside it (entries of the waves' top-4 lists that miss the chunk top-4
+// join the sum).
+__device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &W, const ExpScale &e,
                                                float *lds_f, int *lds_i, double *lds_d, float &M,
                                                double &S_excl, Top4 &ct)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     M = block_max(run.m, lds_f);
     double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2(((double)run.m - (double)M) * e.c64);
-    const Top4 w = wave_top4(t4);
     if (lane == 0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            lds_f[4 + wave * 4 + k] = w.v[k];
-            lds_i[4 + wave * 4 + k] = w.i[k];
+            lds_f[4 + wave * 4 + k] = W.v[k];
+            lds_i[4 + wave * 4 + k] = W.i[k];
         }
     }
     __syncthreads();
@@ -224,10 +314,12 @@ __device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &t4
         ct.i[k] = lds_i[k];
     }
     __syncthreads();
+    if (lane == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (t4.i[k] != INT_MAX && t4.v[k] != -INFINITY && !top_has(ct, t4.i[k]))
-            sc += exp2(((double)t4.v[k] - (double)M) * e.c64);
+        for (int k = 0; k < 4; ++k)
+            if (W.i[k] != INT_MAX && W.v[k] != -INFINITY && !top_has(ct, W.i[k]))
+                sc += exp2(((double)W.v[k] - (double)M) * e.c64);
+    }
     S_excl = block_sum(sc, lds_d);
 }
 

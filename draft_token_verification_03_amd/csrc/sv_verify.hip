@@ -1,19 +1,22 @@
 // sv_verify.hip -- the kernels of the verify step and their launchers.
 //
-//   1. stats_kernel     streams every needed logit row once, one workgroup per
-//                       (row, chunk), and reduces it to a partial: (max, sum
-//                       of exp2((z - max) log2e / T)) for sampling rows, (max,
-//                       lowest argmax) for greedy rows, and for beta-weighted
-//                       draft rows the chunk top-4 with the mass outside it.
-//   2. accept           per sequence: merge its rows' partials in fp64, form
-//                       every accept ratio in the log domain, draw the Philox
-//                       uniforms and find the first rejection n.
-//   3. residual_kernel  re-reads target row n and draft row n (or target row K
-//                       after K acceptances) in chunks and sums the residual.
-//   4. bonus            per sequence: scan the chunk sums, then the selected
-//                       chunk, for the bonus token.
+//   1. stats_kernel  streams every needed logit row once, one workgroup per
+//                    (row, chunk), and reduces it to a partial: (max, sum of
+//                    exp2((z - max) log2e / T)) for sampling rows, (max,
+//                    lowest argmax) for greedy rows, and for beta-weighted
+//                    draft rows the chunk top-4 with the mass outside it.
+//   2. residual_kernel  several workgroups per sequence.  Each runs the
+//                    sequence's accept scan: merge its rows' partials in fp64,
+//                    form every accept ratio in the log domain, draw the
+//                    Philox uniforms and find the first rejection n (all of
+//                    them agree; the first publishes it).  Each then streams
+//                    its share of target row n and draft row n (or of target
+//                    row K after K acceptances) and writes the residual mass
+//                    of every 1 KiB slot of it.
+//   3. bonus_kernel  one workgroup per sequence: inverse CDF over the slot
+//                    masses, then over the elements of the selected slot.
 //
-// The four launches are stream-ordered; every kernel reads only what earlier
+// The three launches are stream-ordered; every kernel reads only what earlier
 // launches wrote, so no workgroup ever waits for another.
 #include <algorithm>
 
@@ -64,6 +67,57 @@ __device__ __forceinline__ void load_step(const char *row, bool aligned, bool st
     }
 }
 
+// Vector q of a row (q < nvec), with elements at or beyond V as -inf.
+template <int DT>
+__device__ __forceinline__ uint4 load_one(const char *row, bool aligned, int q, int nvec, int V)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    const char *p = row + (size_t)q * 16;
+    uint4 r;
+    if (aligned) {
+        r = *reinterpret_cast<const uint4 *>(p);
+    } else {
+        const int valid = min(VEC, V - q * VEC);
+        r = load16_unaligned(p, ((uint32_t)((uintptr_t)p & 15)) + (uint32_t)valid * Elt<DT>::kBytes > 16u);
+    }
+    if ((V % VEC) && q == nvec - 1) mask_raw<DT>(r, V - q * VEC);
+    return r;
+}
+
+// The vectors q[u] of a row for the lanes where live[u]; -inf elsewhere and at
+// or beyond V.  Aligned rows load every vector unconditionally (indices
+// clamped into the row), so all loads are in flight before any is used.
+template <int DT, int U>
+__device__ __forceinline__ void load_units(const char *row, bool aligned, const int (&q)[U],
+                                           const bool (&live)[U], int nvec, int V, uint4 (&r)[U])
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    if (aligned) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = *reinterpret_cast<const uint4 *>(row + (size_t)min(q[u], nvec - 1) * 16);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (!live[u]) r[u] = neg_inf_raw<DT>();
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (live[u]) {
+                const char *p = row + (size_t)q[u] * 16;
+                const int valid = min(VEC, V - q[u] * VEC);
+                r[u] = load16_unaligned(p, ((uint32_t)((uintptr_t)p & 15)) +
+                                               (uint32_t)valid * Elt<DT>::kBytes > 16u);
+            } else {
+                r[u] = neg_inf_raw<DT>();
+            }
+        }
+    }
+    if (V % VEC) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (live[u] && q[u] == nvec - 1) mask_raw<DT>(r[u], V - q[u] * VEC);
+    }
+}
+
 __device__ __forceinline__ const char *target_row(const Args &a, int b, int i)
 {
     return a.target + ((int64_t)b * (a.K + 1) + i) * a.row_bytes;
@@ -75,246 +129,16 @@ __device__ __forceinline__ const char *draft_row(const Args &a, int b, int i)
 }
 
 // ---------------------------------------------------------------------------
-// 2. Accept scan of sequence b by one workgroup ("Kangaroo: Self-Speculative
-// Decoding via Shallow Sub-Networks", "3. Lossless Speculative Verification";
-// greedy: "LayerSkip Guide: Early Exit & Self-Speculative Decoding", "2. The
-// Drafting and Single-Pass Verification Pipeline").  Every position's ratio is
-// formed in parallel; n is the first rejection.  C: the partials were
-// published in the same launch.
-
-struct AcceptLds {
-    float m[kMaxSlots];
-    double S[kMaxSlots];  // S_t, or the draft normaliser D
-    int idx[kMaxSlots];
-    Top4 top[kMaxK];
-    int acc[kMaxK];
-    int err[kMaxK];
-    float pt[kMaxK], pd[kMaxK];
-    int x[kMaxK];                // drafted tokens
-    float zt[kMaxK], zd[kMaxK];  // their logits
-};
-
-__global__ __launch_bounds__(kBlock) void accept_kernel(const Args a)
-{
-    __shared__ __align__(16) unsigned char stage[kStageBytes];
-    __shared__ AcceptLds L;
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = a.K, nc = a.nc;
-    const uint32_t gb = (uint32_t)(a.b0 + b);  // Philox keys on the sequence's index in the call
-    int32_t *out = a.out_tokens + (int64_t)b * (K + 1);
-    const float T = a.temperature[b];
-    const bool greedy = T == 0.f;
-    const bool weighted = a.weighted && !greedy;
-
-    int fail = 0;
-    if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
-    else if (!greedy && K > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
-
-    if (!fail) {
-        // One round trip: the sequence's partials and top-4 lists into LDS
-        // (16-byte granules, every load issued before any is stored) and the
-        // two logits of each drafted token.
-        const int nslots = greedy ? K + 1 : 2 * K + 1;
-        const int P = nslots * nc;
-        const int PT = weighted ? K * nc : 0;
-        const uint4 *gp = reinterpret_cast<const uint4 *>(a.part + (int64_t)b * a.R * nc);
-        const uint4 *gt = reinterpret_cast<const uint4 *>(a.top + (int64_t)b * K * nc);
-        uint4 *s4 = reinterpret_cast<uint4 *>(stage);
-        const int total4 = P + 2 * PT;  // a RowPart is one granule, a Top4 two
-        if (tid < K) {
-            const int x = a.tokens[(int64_t)b * K + tid];
-            L.x[tid] = x;
-            float zt = 0.f, zd = 0.f;
-            if (!greedy && x >= 0 && x < a.V) {
-                if (a.dtype == SV_F32) {
-                    zt = Elt<0>::scalar(target_row(a, b, tid), x);
-                    zd = Elt<0>::scalar(draft_row(a, b, tid), x);
-                } else {
-                    zt = Elt<1>::scalar(target_row(a, b, tid), x);
-                    zd = Elt<1>::scalar(draft_row(a, b, tid), x);
-                }
-            }
-            L.zt[tid] = zt;
-            L.zd[tid] = zd;
-        }
-        for (int base = 0; base < total4; base += 4 * kBlock) {
-            uint4 v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int jj = base + k * kBlock + tid;
-                if (jj < total4) v[k] = jj < P ? gp[jj] : gt[jj - P];
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int jj = base + k * kBlock + tid;
-                if (jj < total4) s4[jj] = v[k];
-            }
-        }
-        __syncthreads();
-
-        const RowPart *sp = reinterpret_cast<const RowPart *>(stage);
-        const Top4 *stp = reinterpret_cast<const Top4 *>(stage + sizeof(RowPart) * (size_t)P);
-        const double c64 = greedy ? 0.0 : kLog2e / (double)T;
-        for (int slot = wave; slot < nslots; slot += kWaves) {
-            const RowPart *p = sp + slot * nc;
-            if (greedy) {
-                float M;
-                int I;
-                merge_argmax(p, nc, M, I);
-                if (lane == 0) {
-                    L.m[slot] = M;
-                    L.idx[slot] = I;
-                }
-            } else if (weighted && slot > K) {
-                const int i = slot - (K + 1);
-                float M;
-                Top4 rt4;
-                double S_rest, S_top;
-                merge_weighted(p, stp + i * nc, nc, c64, M, rt4, S_rest, S_top);
-                if (lane == 0) {
-                    L.m[slot] = M;
-                    L.S[slot] = S_rest + (double)a.beta * S_top;
-                    L.top[i] = rt4;
-                }
-            } else {
-                float M;
-                double S;
-                merge_sum(p, nc, c64, M, S);
-                if (lane == 0) {
-                    L.m[slot] = M;
-                    L.S[slot] = S;
-                }
-            }
-        }
-        __syncthreads();
-
-        if (!greedy) {
-            for (int i = tid; i < K; i += kBlock) {
-                const float mt = L.m[i], md = L.m[K + 1 + i];
-                int err = 0;
-                if (!isfinite(mt)) err |= SV_ERR_ROW;
-                if (!isfinite(md)) err |= SV_ERR_ROW;
-                else if (!(L.S[K + 1 + i] > 0.0)) err |= SV_ERR_DRAFT_MASS;
-                const int x = L.x[i];
-                const bool x_ok = x >= 0 && x < a.V && err == 0;
-                const bool in_top = weighted && top_has(L.top[i], x);
-                const float u = philox_uniform(a.seed, gb, (uint32_t)i, kPurposeAccept);
-                float pt, pd;
-                L.acc[i] = decide(T, mt, L.S[i], md, L.S[K + 1 + i], in_top, a.beta, x_ok, L.zt[i],
-                                  L.zd[i], u, pt, pd)
-                               ? 1
-                               : 0;
-                L.err[i] = err;
-                L.pt[i] = pt;
-                L.pd[i] = pd;
-            }
-        }
-        __syncthreads();
-    }
-
-    if (tid != 0) return;
-
-    int n = K;
-    int err_bits = 0;
-    SeqState st = {};
-    st.mode = 0;
-    if (!fail && greedy) {
-        for (int i = 0; i <= K; ++i) {
-            if (!isfinite(L.m[i])) {
-                fail = SV_ERR_ROW;
-                break;
-            }
-            if (i < K && L.x[i] == L.idx[i]) continue;
-            n = i;
-            break;
-        }
-        if (!fail) {
-            for (int i = 0; i < n; ++i) out[i] = L.x[i];
-            if (n < K) {
-                const int x = L.x[n];
-                if (x < 0 || x >= a.V) err_bits |= SV_ERR_TOKEN;
-            }
-            out[n] = L.idx[n];
-            for (int i = n + 1; i <= K; ++i) out[i] = -1;
-            a.accepted_len[b] = n;
-            if (a.aux_pt)
-                for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
-            if (a.aux_pd)
-                for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
-            if (a.aux_z) a.aux_z[b] = NAN;
-        }
-    } else if (!fail) {
-        for (int i = 0; i < K; ++i) {
-            if (L.err[i]) {  // rows of this position are unusable and it is reached
-                fail = L.err[i];
-                break;
-            }
-            if (!L.acc[i]) {
-                n = i;
-                break;
-            }
-        }
-        if (!fail && n == K && !isfinite(L.m[K])) fail = SV_ERR_ROW;
-        if (!fail) {
-            for (int i = 0; i < n; ++i) out[i] = L.x[i];
-            for (int i = n + 1; i <= K; ++i) out[i] = -1;
-            out[n] = -1;  // the bonus step writes the drawn token
-            if (n < K) {
-                const int x = L.x[n];
-                if (x < 0 || x >= a.V) err_bits |= SV_ERR_TOKEN;
-            }
-            a.accepted_len[b] = n;
-            if (a.aux_pt)
-                for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = i <= n ? L.pt[i] : NAN;
-            if (a.aux_pd)
-                for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = i <= n ? L.pd[i] : NAN;
-            st.n = n;
-            st.mode = n < K ? 1 : 2;
-            st.m_t = L.m[n];
-            st.inv_st = (float)(1.0 / L.S[n]);
-            st.T = T;
-            st.beta = a.beta;
-            st.u_bonus = philox_uniform(a.seed, gb, (uint32_t)n, kPurposeBonus);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) st.top[k] = -1;
-            st.lbeta = (float)log2((double)a.beta);
-            if (n < K) {
-                st.m_d = L.m[K + 1 + n];
-                st.inv_sd = (float)(1.0 / L.S[K + 1 + n]);
-                st.k2 = ((double)L.m[n] - (double)L.m[K + 1 + n]) * (kLog2e / (double)T) +
-                        log2(L.S[n]) - log2(L.S[K + 1 + n]);
-                if (weighted) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) st.top[k] = L.top[n].i[k] == INT_MAX ? -1 : L.top[n].i[k];
-                }
-            }
-        }
-    }
-    if (fail) {
-        a.accepted_len[b] = 0;
-        for (int i = 0; i <= K; ++i) out[i] = -1;
-        if (a.aux_pt)
-            for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
-        if (a.aux_pd)
-            for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
-        if (a.aux_z) a.aux_z[b] = NAN;
-        st = SeqState{};
-        st.mode = 0;
-        err_bits |= fail;
-    }
-    a.seq[b] = st;
-    if (err_bits && a.error_word) atomicOr(a.error_word, err_bits);
-}
-
-// ---------------------------------------------------------------------------
 // 1. Streaming pass, one workgroup per (row, chunk), with the per-thread tile
 // reductions of sv_tile.h: a wave-uniform running max with per-lane fp64
 // sums, lanes visiting their elements in increasing index order (so argmax
 // and top-4 ties resolve to the lowest token id), and for a weighted draft row
-// the lane top-4 kept out of the sum.  Rows a sequence does not use (draft
-// rows in greedy mode or without draft logits, rows of a sequence with an
-// invalid temperature) publish nothing.
+// the wave's top-4 kept out of the sum.  The first tile is requested before
+// the sequence's temperature is known, so the row stream starts one memory
+// round trip earlier; a draft row of a greedy sequence (whose draft logits
+// were passed anyway) wastes that one tile.  Rows a sequence does not use
+// (draft rows in greedy mode or without draft logits, rows of a sequence with
+// an invalid temperature) publish nothing.
 
 template <int DT, bool TOP>
 __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
@@ -328,254 +152,569 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
     const int slot_row = blockIdx.x / a.nc;
     const int b = slot_row / a.R;
     const int j = slot_row - b * a.R;
-
-    const float T = a.temperature[b];
-    const bool greedy = T == 0.f;
     const bool is_draft = j > a.K;
-    const bool used = temperature_ok(T) && !(is_draft && (greedy || a.draft == nullptr));
+    if (is_draft && a.draft == nullptr) return;
+    const int i = is_draft ? j - (a.K + 1) : j;
+    const float T = a.temperature[b];
+    const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
+    const bool aligned = ((uintptr_t)row & 15) == 0;
+    const int q0 = chunk * a.cvec;
+    const int q1 = min(a.nvec, q0 + a.cvec);
+    uint4 r[kLoads];
+    load_step<DT>(row, aligned, true, q0, q1, a.V, r);
+
+    const bool greedy = T == 0.f;
+    if (!temperature_ok(T) || (is_draft && greedy)) return;
     RowPart part;
     Top4 ct;
     const bool track_top = TOP && is_draft;
-    if (used) {
-        const int i = is_draft ? j - (a.K + 1) : j;
-        const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
-        const bool aligned = ((uintptr_t)row & 15) == 0;
-        const int q0 = chunk * a.cvec;
-        const int q1 = min(a.nvec, q0 + a.cvec);
-        if (greedy) {
-            float best = -INFINITY;
-            int bi = INT_MAX;
-            for (int qb = q0; qb < q1; qb += kBlock * kLoads) {
-                uint4 r[kLoads];
-                load_step<DT>(row, aligned, true, qb, q1, a.V, r);
-                run_argmax_tile<DT, kLoads>(r, qb, best, bi);
-            }
-            block_argmax(best, bi, lds_f, lds_i);
-            part.m = best;
-            part.idx = bi;
-            part.s = 0.0;
-        } else {
-            const ExpScale e = make_scale(T);
-            RowRun run;
-            run_clear(run);
-            Top4 t4;
-            top_clear(t4);
-            for (int qb = q0; qb < q1; qb += kBlock * kLoads) {
-                uint4 r[kLoads];
-                load_step<DT>(row, aligned, true, qb, q1, a.V, r);
-                if (track_top) run_sum_top_tile<DT, kLoads>(r, qb, a.V, e, run, t4);
-                else run_sum_tile<DT, kLoads>(r, e, run);
-            }
-            if (track_top) run_finish_top(run, t4, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
-            else run_finish(run, e, lds_f, lds_d, part.m, part.s);
-            part.idx = -1;
+    if (greedy) {
+        float best = -INFINITY;
+        int bi = INT_MAX;
+        for (int qb = q0;;) {
+            run_argmax_tile<DT, kLoads>(r, qb, best, bi);
+            qb += kBlock * kLoads;
+            if (qb >= q1) break;
+            load_step<DT>(row, aligned, true, qb, q1, a.V, r);
         }
+        block_argmax(best, bi, lds_f, lds_i);
+        part.m = best;
+        part.idx = bi;
+        part.s = 0.0;
+    } else {
+        const ExpScale e = make_scale(T);
+        RowRun run;
+        run_clear(run);
+        Top4 t4;
+        top_clear(t4);
+        for (int qb = q0;;) {
+            if (track_top) run_sum_top_tile<DT, kLoads>(r, qb, a.V, e, run, t4);
+            else run_sum_tile<DT, kLoads>(r, e, run);
+            qb += kBlock * kLoads;
+            if (qb >= q1) break;
+            load_step<DT>(row, aligned, true, qb, q1, a.V, r);
+        }
+        if (track_top) run_finish_top(run, t4, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
+        else run_finish(run, e, lds_f, lds_d, part.m, part.s);
+        part.idx = -1;
     }
-    if (used && tid == 0) {
+    if (tid == 0) {
         a.part[(int64_t)slot_row * a.nc + chunk] = part;
-        if (track_top && !greedy) a.top[((int64_t)b * a.K + (j - (a.K + 1))) * a.nc + chunk] = ct;
+        if (track_top) a.top[((int64_t)b * a.K + i) * a.nc + chunk] = ct;
     }
 }
 
 // ---------------------------------------------------------------------------
-// 4. Bonus draw by inverse CDF in ascending token id: the smallest v with
-// C(v) >= u * Z, Z the total residual mass; zero mass falls back to p_t.
+// 2. Accept scan of one sequence ("Kangaroo: Self-Speculative Decoding via
+// Shallow Sub-Networks", "3. Lossless Speculative Verification"; greedy:
+// "LayerSkip Guide: Early Exit & Self-Speculative Decoding", "2. The Drafting
+// and Single-Pass Verification Pipeline"), run by every residual workgroup
+// of the sequence (all reach the same outcome; the first writes it).  The
+// LDS it uses is laid out by accept_lds(), sized from (R, K, nc) so that a
+// workgroup holds only what its sequence needs.
 
-// Scan the residual over vectors [q0, q1), at most kBlock * kLoads of them,
-// in token order, starting from `base`, for the first element whose running
-// sum reaches `thr`.  All loads are issued before the scan.  Returns that
-// element (or INT_MAX), the range total, and the last element with mass.
+struct AcceptLds {
+    RowPart *part;  // [R][nc] staged partials
+    Top4 *ptop;     // [K][nc] staged chunk top-4 lists (weighted draft rows)
+    double *S;      // [R] S_t, or the draft normaliser D
+    float *m;       // [R]
+    int *idx;       // [R]
+    Top4 *top;      // [K] row top-4 of each weighted draft row
+    int *x, *acc, *err;
+    float *pt, *pd;
+    SeqState *st;
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Offsets of the AcceptLds arrays from `base` (nullptr: sizes only); returns
+// the bytes used.
+__host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool weighted,
+                                                    unsigned char *base, AcceptLds *L)
+{
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align16(off + bytes);
+        return base ? base + o : nullptr;
+    };
+    unsigned char *p_part = take(sizeof(RowPart) * (size_t)R * nc);
+    unsigned char *p_ptop = take(weighted ? sizeof(Top4) * (size_t)K * nc : 0);
+    unsigned char *p_S = take(sizeof(double) * (size_t)R);
+    unsigned char *p_m = take(sizeof(float) * (size_t)R);
+    unsigned char *p_idx = take(sizeof(int) * (size_t)R);
+    unsigned char *p_top = take(sizeof(Top4) * (size_t)K);
+    unsigned char *p_x = take(sizeof(int) * (size_t)K);
+    unsigned char *p_acc = take(sizeof(int) * (size_t)K);
+    unsigned char *p_err = take(sizeof(int) * (size_t)K);
+    unsigned char *p_pt = take(sizeof(float) * (size_t)K);
+    unsigned char *p_pd = take(sizeof(float) * (size_t)K);
+    unsigned char *p_st = take(sizeof(SeqState));
+    if (L) {
+        L->part = reinterpret_cast<RowPart *>(p_part);
+        L->ptop = reinterpret_cast<Top4 *>(p_ptop);
+        L->S = reinterpret_cast<double *>(p_S);
+        L->m = reinterpret_cast<float *>(p_m);
+        L->idx = reinterpret_cast<int *>(p_idx);
+        L->top = reinterpret_cast<Top4 *>(p_top);
+        L->x = reinterpret_cast<int *>(p_x);
+        L->acc = reinterpret_cast<int *>(p_acc);
+        L->err = reinterpret_cast<int *>(p_err);
+        L->pt = reinterpret_cast<float *>(p_pt);
+        L->pd = reinterpret_cast<float *>(p_pd);
+        L->st = reinterpret_cast<SeqState *>(p_st);
+    }
+    return off;
+}
+
+// Round trip 1: the temperature, the drafted tokens, and the partials and
+// top-4 lists of all 2K + 1 rows into LDS in 16-byte granules (greedy
+// sequences use the first K + 1 rows).  Round trip 2 gathers the drafted
+// tokens' logits while the partials are merged.  Returns the outcome to
+// every thread; `publish` writes the sequence's outputs (all but the bonus
+// token of a sampling sequence) and its SeqState.
+template <int DT>
+__device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, nc = a.nc;
+    const uint32_t gb = (uint32_t)(a.b0 + b);  // Philox keys on the sequence's index in the call
+    int32_t *out = a.out_tokens + (int64_t)b * (K + 1);
+
+    const float T = a.temperature[b];
+    int x = -1;
+    if (tid < K) x = a.tokens[(int64_t)b * K + tid];
+    {
+        const int P = a.R * nc;
+        const int PT = a.weighted ? K * nc : 0;
+        const uint4 *gp = reinterpret_cast<const uint4 *>(a.part + (int64_t)b * a.R * nc);
+        const uint4 *gt = reinterpret_cast<const uint4 *>(a.top + (int64_t)b * K * nc);
+        uint4 *sp = reinterpret_cast<uint4 *>(L.part);
+        uint4 *st4 = reinterpret_cast<uint4 *>(L.ptop);
+        const int total4 = P + 2 * PT;  // a RowPart is one granule, a Top4 two
+        for (int base = 0; base < total4; base += 4 * kBlock) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int jj = base + k * kBlock + tid;
+                if (jj < total4) v[k] = jj < P ? gp[jj] : gt[jj - P];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int jj = base + k * kBlock + tid;
+                if (jj < P) sp[jj] = v[k];
+                else if (jj < total4) st4[jj - P] = v[k];
+            }
+        }
+    }
+    const bool greedy = T == 0.f;
+    const bool weighted = a.weighted && !greedy;
+    int fail = 0;
+    if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
+    else if (!greedy && K > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
+
+    const bool x_ok = x >= 0 && x < a.V;
+    float zt = 0.f, zd = 0.f;
+    if (tid < K) {
+        L.x[tid] = x;
+        if (!fail && !greedy && x_ok) {
+            zt = Elt<DT>::scalar(target_row(a, b, tid), x);
+            zd = Elt<DT>::scalar(draft_row(a, b, tid), x);
+        }
+    }
+    __syncthreads();
+
+    if (!fail) {
+        const int nrows = greedy ? K + 1 : 2 * K + 1;
+        const double c64 = greedy ? 0.0 : kLog2e / (double)T;
+        for (int r = wave; r < nrows; r += kWaves) {
+            const RowPart *p = L.part + r * nc;
+            if (greedy) {
+                float M;
+                int I;
+                merge_argmax(p, nc, M, I);
+                if (lane == 0) {
+                    L.m[r] = M;
+                    L.idx[r] = I;
+                }
+            } else if (weighted && r > K) {
+                const int i = r - (K + 1);
+                float M;
+                Top4 rt4;
+                double S_rest, S_top;
+                merge_weighted(p, L.ptop + i * nc, nc, c64, M, rt4, S_rest, S_top);
+                if (lane == 0) {
+                    L.m[r] = M;
+                    L.S[r] = S_rest + (double)a.beta * S_top;
+                    L.top[i] = rt4;
+                }
+            } else {
+                float M;
+                double S;
+                merge_sum(p, nc, c64, M, S);
+                if (lane == 0) {
+                    L.m[r] = M;
+                    L.S[r] = S;
+                }
+            }
+        }
+        __syncthreads();
+
+        if (!greedy && tid < K) {
+            const int i = tid;
+            const float mt = L.m[i], md = L.m[K + 1 + i];
+            int err = 0;
+            if (!isfinite(mt)) err |= SV_ERR_ROW;
+            if (!isfinite(md)) err |= SV_ERR_ROW;
+            else if (!(L.S[K + 1 + i] > 0.0)) err |= SV_ERR_DRAFT_MASS;
+            const bool in_top = weighted && top_has(L.top[i], x);
+            const float u = philox_uniform(a.seed, gb, (uint32_t)i, kPurposeAccept);
+            float pt, pd;
+            L.acc[i] = decide(T, mt, L.S[i], md, L.S[K + 1 + i], in_top, a.beta, x_ok && err == 0, zt,
+                              zd, u, pt, pd)
+                           ? 1
+                           : 0;
+            L.err[i] = err;
+            L.pt[i] = pt;
+            L.pd[i] = pd;
+        }
+        __syncthreads();
+    }
+
+    if (tid == 0) {
+        int n = K;
+        int err_bits = 0;
+        SeqState st = {};
+        st.mode = 0;
+        if (!fail && greedy) {
+            for (int i = 0; i <= K; ++i) {
+                if (!isfinite(L.m[i])) {
+                    fail = SV_ERR_ROW;
+                    break;
+                }
+                if (i < K && L.x[i] == L.idx[i]) continue;
+                n = i;
+                break;
+            }
+            if (!fail && publish) {
+                for (int i = 0; i < n; ++i) out[i] = L.x[i];
+                if (n < K) {
+                    const int xn = L.x[n];
+                    if (xn < 0 || xn >= a.V) err_bits |= SV_ERR_TOKEN;
+                }
+                out[n] = L.idx[n];
+                for (int i = n + 1; i <= K; ++i) out[i] = -1;
+                a.accepted_len[b] = n;
+                if (a.aux_pt)
+                    for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
+                if (a.aux_pd)
+                    for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
+                if (a.aux_z) a.aux_z[b] = NAN;
+            }
+        } else if (!fail) {
+            for (int i = 0; i < K; ++i) {
+                if (L.err[i]) {  // rows of this position are unusable and it is reached
+                    fail = L.err[i];
+                    break;
+                }
+                if (!L.acc[i]) {
+                    n = i;
+                    break;
+                }
+            }
+            if (!fail && n == K && !isfinite(L.m[K])) fail = SV_ERR_ROW;
+            if (!fail) {
+                if (publish) {
+                    for (int i = 0; i < n; ++i) out[i] = L.x[i];
+                    for (int i = n; i <= K; ++i) out[i] = -1;  // out[n]: the bonus step
+                    if (n < K) {
+                        const int xn = L.x[n];
+                        if (xn < 0 || xn >= a.V) err_bits |= SV_ERR_TOKEN;
+                    }
+                    a.accepted_len[b] = n;
+                    if (a.aux_pt)
+                        for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = i <= n ? L.pt[i] : NAN;
+                    if (a.aux_pd)
+                        for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = i <= n ? L.pd[i] : NAN;
+                }
+                st.n = n;
+                st.mode = n < K ? 1 : 2;
+                st.m_t = L.m[n];
+                st.inv_st = (float)(1.0 / L.S[n]);
+                st.T = T;
+                st.u_bonus = philox_uniform(a.seed, gb, (uint32_t)n, kPurposeBonus);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) st.top[k] = -1;
+                st.lbeta = (float)log2((double)a.beta);
+                if (n < K) {
+                    st.m_d = L.m[K + 1 + n];
+                    st.k2 = ((double)L.m[n] - (double)L.m[K + 1 + n]) * (kLog2e / (double)T) +
+                            log2(L.S[n]) - log2(L.S[K + 1 + n]);
+                    if (weighted) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            st.top[k] = L.top[n].i[k] == INT_MAX ? -1 : L.top[n].i[k];
+                    }
+                }
+            }
+        }
+        if (fail) {
+            if (publish) {
+                a.accepted_len[b] = 0;
+                for (int i = 0; i <= K; ++i) out[i] = -1;
+                if (a.aux_pt)
+                    for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
+                if (a.aux_pd)
+                    for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
+                if (a.aux_z) a.aux_z[b] = NAN;
+            }
+            st = SeqState{};
+            st.mode = 0;
+            err_bits |= fail;
+        }
+        *L.st = st;
+        if (publish) {
+            a.seq[b] = st;
+            if (err_bits && a.error_word) atomicOr(a.error_word, err_bits);
+        }
+    }
+    __syncthreads();
+    return *L.st;
+}
+
+// ---------------------------------------------------------------------------
+// 3. Residual ("Kangaroo ...", "3. Lossless Speculative Verification";
+// "Speculative Speculative Decoding", "Method"): max(p_t - q', 0) over target
+// row n and draft row n, or p_t over target row K after K acceptances.
+
+// Residual of the elements of one 16-byte vector pair; returns the fp32
+// pairwise sum of the vector's values and fills r[].
 template <int DT, bool TOP>
-__device__ int scan_chunk(const Args &a, int b, const SeqState &st, int mode, const ExpScale &e,
-                          int q0, int q1, double base, double thr, double &total, int &last_pos,
-                          double *lds_d, int *lds_i)
+__device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, int mode, const SeqState &st,
+                                              const ExpScale &e, const ResidualScale &rs,
+                                              float (&r)[Elt<DT>::kVec])
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    float xt[VEC], xd[VEC];
+    Elt<DT>::unpack(rt, xt);
+    if (mode == 1) Elt<DT>::unpack(rd, xd);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k)
+        r[k] = residual_at<TOP>(xt[k], mode == 1 ? xd[k] : 0.f, q * VEC + k, st, e, rs, mode);
+    float s[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) s[k] = r[k];
+#pragma unroll
+    for (int w = VEC / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int k = 0; k < w; ++k) s[k] += s[k + w];
+    return s[0];
+}
+
+// Residual mass of the slots [s_begin, s_end) of the row pair into slot[].
+// Slot s covers the vectors [s*gs*kSlotVec, (s+1)*gs*kSlotVec); the NW waves
+// of the workgroup take the slots in turn, and a wave's 64 lanes read
+// kSlotVec consecutive vectors (1 KiB of each row) per load, kLoads units in
+// flight per lane.  Each slot is summed by one wave in a fixed order (fp32
+// within a vector, fp64 across vectors and lanes).
+template <int DT, bool TOP, int NW>
+__device__ void residual_slots(const char *trow, const char *drow, int mode, int V, int nvec,
+                               int s_begin, int s_end, int gs, const SeqState &st, const ExpScale &e,
+                               const ResidualScale &rs, double *slot)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool ta = ((uintptr_t)trow & 15) == 0, da = ((uintptr_t)drow & 15) == 0;
+    const int ns = s_end - s_begin;
+    const int my_slots = ns > wave ? (ns - wave + NW - 1) / NW : 0;
+    const int items = my_slots * gs;
+    double acc = 0.0;
+    // item f = t * gs + j is unit j of the wave's t-th slot, s_begin + wave + NW * t
+    int t = 0, j = 0;
+    for (int f0 = 0; f0 < items; f0 += kLoads) {
+        uint4 rt[kLoads], rd[kLoads];
+        int qv[kLoads], tv[kLoads];
+        bool endv[kLoads], live[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            const int s = s_begin + wave + NW * t;
+            const int q = (s * gs + j) * kSlotVec + lane;
+            qv[u] = q;
+            tv[u] = t;
+            endv[u] = j == gs - 1;
+            live[u] = f0 + u < items && q < nvec;
+            if (++j == gs) {
+                j = 0;
+                ++t;
+            }
+        }
+        load_units<DT, kLoads>(trow, ta, qv, live, nvec, V, rt);
+        if (mode == 1) load_units<DT, kLoads>(drow, da, qv, live, nvec, V, rd);
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) {
+            if (f0 + u >= items) break;
+            float r[Elt<DT>::kVec];
+            acc += (double)residual_vec<DT, TOP>(rt[u], rd[u], qv[u], mode, st, e, rs, r);
+            if (endv[u]) {
+                const double tot = wave_sum(acc);
+                if (lane == 0) slot[s_begin + wave + NW * tv[u]] = tot;
+                acc = 0.0;
+            }
+        }
+    }
+}
+
+// One workgroup per (sequence, group of a.spg slots): the accept scan, then
+// the group's slot masses.
+template <int DT, bool TOP>
+__global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
+{
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    const int b = blockIdx.x / a.ng;
+    const int g = blockIdx.x - b * a.ng;
+    AcceptLds L;
+    accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, dyn_lds, &L);
+    const SeqState st = accept_sequence<DT>(a, b, L, g == 0);
+    if (st.mode == 0) return;
+    const ExpScale e = make_scale(st.T);
+    const ResidualScale rs = make_residual_scale(st, e);
+    const char *trow = target_row(a, b, st.n);
+    const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
+    const int s0 = g * a.spg, s1 = min(a.nslot, s0 + a.spg);
+    residual_slots<DT, TOP, kWaves>(trow, drow, st.mode, a.V, a.nvec, s0, s1, a.gs, st, e, rs,
+                                    a.slot + (int64_t)b * a.nslot);
+}
+
+// ---------------------------------------------------------------------------
+// 4. Bonus draw by inverse CDF in ascending token id: the smallest v with
+// C(v) >= u * Z, Z the total residual mass, first over the slot masses, then
+// over the elements of the selected slot; zero mass (only through rounding)
+// falls back to p_t.
+
+// Ordered scan of the vectors [q0, q1) of the row pair, starting from `base`,
+// for the first element with mass whose running sum reaches `thr`.  Returns
+// that element, or INT_MAX when rounding leaves `thr` above the range; `last`
+// receives the last element of the range with positive mass.
+template <int DT, bool TOP>
+__device__ int scan_range(const char *trow, const char *drow, int mode, int V, int nvec, int q0,
+                          int q1, double base, double thr, const SeqState &st, const ExpScale &e,
+                          const ResidualScale &rs, int &last, double *lds_d, int *lds_i)
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int tid = threadIdx.x;
-    const char *trow = target_row(a, b, st.n);
-    const char *drow = mode == 1 ? draft_row(a, b, st.n) : trow;
     const bool ta = ((uintptr_t)trow & 15) == 0, da = ((uintptr_t)drow & 15) == 0;
-    uint4 rt[kLoads], rd[kLoads];
-    load_step<DT>(trow, ta, false, q0, q1, a.V, rt);
-    if (mode == 1) load_step<DT>(drow, da, false, q0, q1, a.V, rd);
-    double run = base;
-    int last = -1;
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-        float xt[VEC], xd[VEC];
-        Elt<DT>::unpack(rt[u], xt);
-        if (mode == 1) Elt<DT>::unpack(rd[u], xd);
+    last = -1;
+    for (int qb = q0; qb < q1; qb += kBlock) {
+        const int q = qb + tid;
+        const bool live = q < q1;
+        const uint4 rt = live ? load_one<DT>(trow, ta, q, nvec, V) : neg_inf_raw<DT>();
+        uint4 rd = neg_inf_raw<DT>();
+        if (mode == 1 && live) rd = load_one<DT>(drow, da, q, nvec, V);
+        float r[VEC];
+        residual_vec<DT, TOP>(rt, rd, q, mode, st, e, rs, r);
         double pre[VEC];
         double acc = 0.0;
         int mylast = -1;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const int v = elem_index(q0, u, k, VEC);
-            const float r = residual_at<TOP>(xt[k], mode == 1 ? xd[k] : 0.f, v, st, e, mode);
-            acc += (double)r;
+            acc += (double)r[k];
             pre[k] = acc;
-            if (r > 0.f) mylast = v;
+            if (r[k] > 0.f) mylast = q * VEC + k;
         }
         double tile_total;
         const double exc = block_exclusive_scan(acc, tile_total, lds_d);
         int cand = INT_MAX;
 #pragma unroll
         for (int k = VEC - 1; k >= 0; --k)
-            if (run + exc + pre[k] >= thr) cand = elem_index(q0, u, k, VEC);
+            if (r[k] > 0.f && base + exc + pre[k] >= thr) cand = q * VEC + k;
         cand = block_min_int(cand, lds_i);
         last = max(last, block_max_int(mylast, lds_i));
-        if (cand != INT_MAX) {
-            total = run + tile_total;
-            last_pos = last;
-            return cand;
-        }
-        run += tile_total;
+        if (cand != INT_MAX) return cand;
+        base += tile_total;
     }
-    total = run;
-    last_pos = last;
     return INT_MAX;
 }
 
-// The whole row range [0, nvec) in chunks of kBlock * kLoads vectors.
+// Inverse CDF over the slot masses in slot[0..nslot): returns the token (-1
+// when the mass is 0) and Z, the total mass.
 template <int DT, bool TOP>
-__device__ int scan_row(const Args &a, int b, const SeqState &st, int mode, const ExpScale &e,
-                        double thr, double &total, int &last_pos, double *lds_d, int *lds_i)
+__device__ int draw_token(const char *trow, const char *drow, int mode, int V, int nvec, int nslot,
+                          int gs, float u, const SeqState &st, const ExpScale &e,
+                          const ResidualScale &rs, const double *slot, double &Z, double *lds_d,
+                          int *lds_i)
 {
-    double run = 0.0;
-    int last = -1;
-    for (int q0 = 0; q0 < a.nvec; q0 += kBlock * kLoads) {
-        double t;
-        int l;
-        const int v = scan_chunk<DT, TOP>(a, b, st, mode, e, q0, min(a.nvec, q0 + kBlock * kLoads),
-                                          run, thr, t, l, lds_d, lds_i);
-        run = t;
-        last = max(last, l);
-        if (v != INT_MAX) {
-            total = run;
-            last_pos = last;
-            return v;
+    const int tid = threadIdx.x;
+    const int per = (nslot + kBlock - 1) / kBlock;
+    const int s0 = min(nslot, tid * per), s1 = min(nslot, s0 + per);
+    double loc = 0.0;
+    for (int s = s0; s < s1; ++s) loc += slot[s];
+    double total;
+    const double exc = block_exclusive_scan(loc, total, lds_d);
+    Z = total;
+    if (!(total > 0.0)) return -1;
+    const double thr = (double)u * total;
+    // the first slot with mass whose inclusive prefix reaches thr, else (by
+    // rounding between summation orders) the last slot with mass
+    int cand = INT_MAX, lastpos = -1;
+    double cbase = 0.0, lbase = 0.0, run = exc;
+    for (int s = s0; s < s1; ++s) {
+        const double v = slot[s];
+        if (v > 0.0) {
+            if (cand == INT_MAX && run + v >= thr) {
+                cand = s;
+                cbase = run;
+            }
+            lastpos = s;
+            lbase = run;
         }
+        run += v;
     }
-    total = run;
-    last_pos = last;
-    return INT_MAX;
+    const int c = block_min_int(cand, lds_i);
+    const int lp = block_max_int(lastpos, lds_i);
+    const int sel = c != INT_MAX ? c : lp;
+    if (sel < 0) return -1;  // no slot with mass: only NaN masses get here
+    if (sel >= s0 && sel < s1) lds_d[kWaves] = (c != INT_MAX) ? cbase : lbase;
+    __syncthreads();
+    const double base = lds_d[kWaves];
+    __syncthreads();
+    const int q0 = sel * gs * kSlotVec, q1 = min(nvec, q0 + gs * kSlotVec);
+    int last;
+    const int tok = scan_range<DT, TOP>(trow, drow, mode, V, nvec, q0, q1, base, thr, st, e, rs, last,
+                                        lds_d, lds_i);
+    return tok != INT_MAX ? tok : last;
 }
 
 template <int DT, bool TOP>
 __global__ __launch_bounds__(kBlock) void bonus_kernel(const Args a)
 {
-    __shared__ double lds_d[kWaves];
+    __shared__ double slot[kMaxResSlots];
+    __shared__ double lds_d[kWaves + 1];
     __shared__ int lds_i[kWaves];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    // the slot masses are requested together with the sequence's state
+    const double *gslot = a.slot + (int64_t)b * a.nslot;
+    for (int s = tid; s < a.nslot; s += kBlock) slot[s] = gslot[s];
     const SeqState st = a.seq[b];
+    __syncthreads();
     if (st.mode == 0) return;
     const ExpScale e = make_scale(st.T);
-    const double *rs = a.res + (int64_t)b * a.ncr;
-
-    double Z = 0.0;
-    for (int c0 = 0; c0 < a.ncr; c0 += kBlock) {
-        const int c = c0 + tid;
-        double tot;
-        block_exclusive_scan(c < a.ncr ? rs[c] : 0.0, tot, lds_d);
-        Z += tot;
-    }
-    int token = -1;
-    double total;
-    int last;
-    if (Z > 0.0) {
-        const double thr = (double)st.u_bonus * Z;
-        double run = 0.0;
-        int cstar = INT_MAX, last_chunk = -1;
-        double cbase = 0.0, last_base = 0.0;
-        for (int c0 = 0; c0 < a.ncr && cstar == INT_MAX; c0 += kBlock) {
-            const int c = c0 + tid;
-            const double v = c < a.ncr ? rs[c] : 0.0;
-            double tot;
-            const double exc = block_exclusive_scan(v, tot, lds_d);
-            int cand = (c < a.ncr && run + exc + v >= thr) ? c : INT_MAX;
-            cand = block_min_int(cand, lds_i);
-            const int lastc = block_max_int(v > 0.0 ? c : -1, lds_i);
-            if (cand != INT_MAX || lastc > last_chunk) {
-                if (c == cand) lds_d[0] = run + exc;
-                if (c == lastc) lds_d[1] = run + exc;
-                __syncthreads();
-                if (cand != INT_MAX) cbase = lds_d[0];
-                if (lastc > last_chunk) last_base = lds_d[1];
-                __syncthreads();
-            }
-            if (cand != INT_MAX) cstar = cand;
-            if (lastc > last_chunk) last_chunk = lastc;
-            run += tot;
-        }
-        if (cstar == INT_MAX) {
-            // rounding between the two summation orders left u * Z above the last
-            // prefix: the draw falls in the last chunk that has mass
-            cstar = last_chunk;
-            cbase = last_base;
-        }
-        if (cstar >= 0) {
-            const int q0 = cstar * a.rvec, q1 = min(a.nvec, q0 + a.rvec);
-            token = scan_chunk<DT, TOP>(a, b, st, st.mode, e, q0, q1, cbase, thr, total, last, lds_d,
-                                        lds_i);
-            if (token == INT_MAX) token = last;  // same rounding inside the chunk
-        }
-    }
+    const ResidualScale rs = make_residual_scale(st, e);
+    const char *trow = target_row(a, b, st.n);
+    const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
+    double Z;
+    int token = draw_token<DT, TOP>(trow, drow, st.mode, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e,
+                                    rs, slot, Z, lds_d, lds_i);
     if (token < 0) {
-        // zero residual mass (only through rounding): draw from p_t instead
-        scan_row<DT, TOP>(a, b, st, 2, e, INFINITY, total, last, lds_d, lds_i);
-        Z = total;
-        token = scan_row<DT, TOP>(a, b, st, 2, e, (double)st.u_bonus * Z, total, last, lds_d, lds_i);
-        if (token == INT_MAX) token = last;
+        // zero residual mass: the slot masses of p_t, by this workgroup alone
+        residual_slots<DT, TOP, kWaves>(trow, trow, 2, a.V, a.nvec, 0, a.nslot, a.gs, st, e, rs, slot);
+        __syncthreads();
+        token = draw_token<DT, TOP>(trow, trow, 2, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e, rs,
+                                    slot, Z, lds_d, lds_i);
     }
     if (tid == 0) {
         a.out_tokens[(int64_t)b * (a.K + 1) + st.n] = token;
-        if (a.aux_z) a.aux_z[b] = (float)Z;
+        if (a.aux_z) a.aux_z[b] = (float)(Z * (double)st.inv_st);
     }
-}
-
-// ---------------------------------------------------------------------------
-// 3. Chunk sums of the residual: one workgroup per (sequence, chunk);
-// sequences with nothing to draw (greedy, failed) skip it.
-
-template <int DT, bool TOP>
-__global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
-{
-    constexpr int VEC = Elt<DT>::kVec;
-    __shared__ double lds_d[kWaves];
-    const int b = blockIdx.x / a.ncr;
-    const int chunk = blockIdx.x - b * a.ncr;
-    const SeqState st = a.seq[b];
-    if (st.mode == 0) return;
-    const ExpScale e = make_scale(st.T);
-    const char *trow = target_row(a, b, st.n);
-    const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
-    const bool ta = ((uintptr_t)trow & 15) == 0, da = ((uintptr_t)drow & 15) == 0;
-    const int q0 = chunk * a.rvec, q1 = min(a.nvec, q0 + a.rvec);
-    const int tid = threadIdx.x;
-    double s = 0.0;
-    for (int qb = q0; qb < q1; qb += kBlock * kLoads) {
-        uint4 rt[kLoads], rd[kLoads];
-        load_step<DT>(trow, ta, false, qb, q1, a.V, rt);
-        if (st.mode == 1) load_step<DT>(drow, da, false, qb, q1, a.V, rd);
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
-            float xt[VEC], xd[VEC], rv[VEC];
-            Elt<DT>::unpack(rt[u], xt);
-            if (st.mode == 1) Elt<DT>::unpack(rd[u], xd);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k)
-                rv[k] = residual_at<TOP>(xt[k], st.mode == 1 ? xd[k] : 0.f, elem_index(qb, u, k, VEC),
-                                         st, e, st.mode);
-#pragma unroll
-            for (int w = VEC / 2; w > 0; w >>= 1)
-#pragma unroll
-                for (int k = 0; k < w; ++k) rv[k] += rv[k + w];
-            s += (double)rv[0];
-        }
-    }
-    const double S = block_sum(s, lds_d);
-    if (tid == 0) a.res[(int64_t)b * a.ncr + chunk] = S;
 }
 
 // Row-statistics entry point: finish the merge of each row's partials.
@@ -630,24 +769,24 @@ __global__ void uniforms_kernel(uint64_t seed, int32_t B, int32_t P, float *out)
 // Host launchers (one sub-batch of at most kMaxSeqPerLaunch sequences).
 
 template <int DT, bool TOP>
-static void launch_all(const Args &a, hipStream_t s, bool draw)
+static void launch_all(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)
 {
+    if (begin) (void)hipEventRecord(begin, s);
     stats_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.R * a.nc), kBlock, 0, s>>>(a);
-    accept_kernel<<<(unsigned)a.B, kBlock, 0, s>>>(a);
-    if (draw) {
-        residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ncr), kBlock, 0, s>>>(a);
-        bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
-    }
+    if (end) (void)hipEventRecord(end, s);
+    const size_t lds = accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, nullptr, nullptr);
+    residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ng), kBlock, lds, s>>>(a);
+    bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
 }
 
-void launch_verify(const Args &a, hipStream_t s, bool draw)
+void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)
 {
     if (a.dtype == SV_F32) {
-        if (a.weighted) launch_all<0, true>(a, s, draw);
-        else launch_all<0, false>(a, s, draw);
+        if (a.weighted) launch_all<0, true>(a, s, begin, end);
+        else launch_all<0, false>(a, s, begin, end);
     } else {
-        if (a.weighted) launch_all<1, true>(a, s, draw);
-        else launch_all<1, false>(a, s, draw);
+        if (a.weighted) launch_all<1, true>(a, s, begin, end);
+        else launch_all<1, false>(a, s, begin, end);
     }
 }
 

@@ -88,6 +88,8 @@ typedef struct sv_aux {
     float *p_draft;       /* [B, K] q_i(x_i) (beta-weighted) at evaluated positions, else NaN         */
     float *residual_mass; /* [B]    C(V-1) of the bonus draw; NaN in greedy mode                      */
     int32_t *error_word;  /* [1]    SV_ERR_* bits are OR-ed in: zero it before the call           */
+    void *pass_begin;     /* hipEvent_t recorded on `stream` right before the streaming-pass launch */
+    void *pass_end;       /* and right after it (first sub-batch only): times the dominant kernel   */
 } sv_aux;
 
 /*

@@ -58,6 +58,11 @@ class Workload:
         small = 4 * (self.B * self.K + self.B + self.B + self.B * (self.K + 1))
         return rows * self.V * self.elt_bytes + small
 
+    def stream_bytes(self) -> int:
+        """Bytes the streaming pass must read once: the logit rows alone."""
+        rows = self.B * (self.K + 1) + (0 if self.greedy else self.B * self.K)
+        return rows * self.V * self.elt_bytes
+
     def tag(self) -> str:
         t = "Tgreedy" if self.greedy else (f"T{self.temperature:g}" if self.temperature
                                            else f"TU[{self.t_lo:g},{self.t_hi:g}]")
