@@ -14,6 +14,11 @@ __device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T !
 
 __device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, float &M, double &S)
 {
+    if (nc == 1) {  // a whole row per chunk: its partial is the row's statistic
+        M = p[0].m;
+        S = p[0].s;
+        return;
+    }
     const int lane = threadIdx.x & 63;
     float m = -INFINITY;
     for (int c = lane; c < nc; c += 64) m = fmaxf(m, p[c].m);
@@ -29,6 +34,11 @@ __device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, 
 
 __device__ __forceinline__ void merge_argmax(const RowPart *p, int nc, float &M, int &I)
 {
+    if (nc == 1) {
+        M = p[0].m;
+        I = p[0].idx;
+        return;
+    }
     const int lane = threadIdx.x & 63;
     float v = -INFINITY;
     int i = INT_MAX;
@@ -56,59 +66,72 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
     const int lane = threadIdx.x & 63;
     double s_excl;
     merge_sum(p, nc, c64, M, s_excl);
-    Top4 t;
-    top_clear(t);
-    for (int c = lane; c < nc; c += 64) {
-        const Top4 r = tp[c];
+    if (nc == 1) {  // the chunk's top-4 is the row's; nothing else to move
+        row_top = tp[0];
+        S_rest = s_excl;
+    } else {
+        Top4 t;
+        top_clear(t);
+        for (int c = lane; c < nc; c += 64) {
+            const Top4 r = tp[c];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) top_insert(t, r.v[k], r.i[k]);
-    }
-    row_top = wave_top4(t);
-    double extra = 0.0;
-    for (int c = lane; c < nc; c += 64) {
-        const Top4 r = tp[c];
+            for (int k = 0; k < 4; ++k) top_insert(t, r.v[k], r.i[k]);
+        }
+        row_top = wave_top4(t);
+        double extra = 0.0;
+        for (int c = lane; c < nc; c += 64) {
+            const Top4 r = tp[c];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
-                extra += exp2(((double)r.v[k] - (double)M) * c64);
+            for (int k = 0; k < 4; ++k)
+                if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
+                    extra += exp2(((double)r.v[k] - (double)M) * c64);
+        }
+        S_rest = s_excl + wave_sum(extra);
     }
-    S_rest = s_excl + wave_sum(extra);
+    // lane k < 4 adds the k-th entry of the row top-4
     double st = 0.0;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        if (row_top.i[k] != INT_MAX && row_top.v[k] != -INFINITY)
-            st += exp2(((double)row_top.v[k] - (double)M) * c64);
-    S_top = st;
+        if (lane == k && row_top.i[k] != INT_MAX && row_top.v[k] != -INFINITY)
+            st = exp2(((double)row_top.v[k] - (double)M) * c64);
+    S_top = wave_sum(st);
 }
 
 // ---------------------------------------------------------------------------
 // One accept test ("Kangaroo: Self-Speculative Decoding via Shallow
 // Sub-Networks", "3. Lossless Speculative Verification"; glossary
 // "speculative decoding llm", "Why It Produces Identical Outputs"): accept x
-// iff u <= p(x) / q'(x), formed in fp64 in the log domain,
-//   ln p(x)  = (z_t(x) - m_t) / T - ln S_t,
-//   ln q'(x) = (z_d(x) - m_d) / T + ln w(x) - ln D,
+// iff u <= p(x) / q'(x), with the ratio formed in fp64 in the log domain,
+//   ln r = [(z_t(x) - m_t) - (z_d(x) - m_d)] / T + ln(D / S_t) + ln w(x),
 // with D = S_d unweighted, or S_rest + beta * S_top for the Saguaro-style
-// draft ("Speculative Speculative Decoding", "Method"), w(x) = beta on the
-// draft's top-4 and 1 elsewhere.  A token the draft law gives no mass is
-// accepted (the ratio is +inf).
+// draft ("Speculative Speculative Decoding", "Method"), w(x) = 1/beta on the
+// draft's top-4 and 1 elsewhere (ln_beta = ln beta, from the host).  Only the
+// final exponential is fp32: rounding ln r to fp32 moves r by at most
+// r |ln r| 2^-24 <= 2.2e-8 where r <= 1, below the uniforms' 2^-24 grid.  A
+// token the draft law gives no mass is accepted (the ratio is +inf).  The
+// diagnostics p(x), q'(x) are only formed when asked for (fp32 logs: ~1e-6
+// relative).
 __device__ __forceinline__ bool decide(float T, float mt, double St, float md, double D,
-                                       bool weighted_top, float beta, bool x_ok, float zt, float zd,
-                                       float u, float &pt, float &pd)
+                                       bool weighted_top, double ln_beta, bool x_ok, float zt,
+                                       float zd, float u, bool want_p, float &pt, float &pd)
 {
-    const double Td = (double)T;
-    double ratio = 0.0;
     pt = NAN;
     pd = NAN;
-    if (x_ok) {
-        const double lpt = ((double)zt - (double)mt) / Td - log(St);
-        double lpd = ((double)zd - (double)md) / Td - log(D);
-        if (weighted_top) lpd += log((double)beta);
-        ratio = (lpd == -INFINITY) ? INFINITY : exp(lpt - lpd);
-        pt = (float)exp(lpt);
-        pd = (float)exp(lpd);
+    if (!x_ok) return false;
+    const double Td = (double)T;
+    const double dt = (double)zt - (double)mt, dd = (double)zd - (double)md;  // exact
+    const bool no_draft_mass = dd == -INFINITY || (weighted_top && ln_beta == -INFINITY);
+    double lr = (dt - dd) / Td + log(D / St);
+    if (weighted_top) lr -= ln_beta;
+    const bool accept = no_draft_mass || (double)u <= (double)__expf((float)lr);
+    if (want_p) {
+        const float lpt = (float)(dt / Td) - __logf((float)St);
+        float lpd = (float)(dd / Td) - __logf((float)D);
+        if (weighted_top) lpd += (float)ln_beta;
+        pt = __expf(lpt);
+        pd = __expf(lpd);
     }
-    return (double)u <= ratio;
+    return accept;
 }
 
 // ---------------------------------------------------------------------------
@@ -145,39 +168,37 @@ __device__ __forceinline__ ResidualScale make_residual_scale(const SeqState &st,
     return r;
 }
 
-// 1 - 2^d for d < 0, to a few ulp: a degree-9 Taylor series of -expm1(d ln2)
-// for d > -1 (truncation below 1e-8 relative), 1 - exp2(d) below, where
-// 2^d <= 1/2 keeps the subtraction well conditioned.
+// 1 - 2^d for d < 0, to ~2e-7 relative: -d * P(d) on [-1, 0), with P a
+// degree-5 fit of (2^d - 1)/d on that interval (fit error 1e-8, fp32 Horner
+// rounding ~1e-7), and 1 - exp2(d) below -1, where 2^d <= 1/2 keeps the
+// subtraction well conditioned.  d >= 0 gives a value <= 0 (callers clamp).
 __device__ __forceinline__ float one_minus_exp2(float d)
 {
-    const float y = d * 0.693147180559945f;
-    float p = __builtin_fmaf(y, 1.f / 362880.f, 1.f / 40320.f);
-    p = __builtin_fmaf(y, p, 1.f / 5040.f);
-    p = __builtin_fmaf(y, p, 1.f / 720.f);
-    p = __builtin_fmaf(y, p, 1.f / 120.f);
-    p = __builtin_fmaf(y, p, 1.f / 24.f);
-    p = __builtin_fmaf(y, p, 1.f / 6.f);
-    p = __builtin_fmaf(y, p, 0.5f);
-    p = __builtin_fmaf(y, p, 1.f);
-    const float series = -(y * p);
+    float p = __builtin_fmaf(d, 1.145800052e-04f, 1.290776301e-03f);
+    p = __builtin_fmaf(d, p, 9.596269578e-03f);
+    p = __builtin_fmaf(d, p, 5.549895018e-02f);
+    p = __builtin_fmaf(d, p, 2.402260602e-01f);
+    p = __builtin_fmaf(d, p, 6.931471825e-01f);
+    const float poly = -d * p;
     const float direct = 1.f - __builtin_amdgcn_exp2f(d);
-    return d > -1.f ? series : direct;
+    return d >= -1.f ? poly : direct;
 }
 
-template <bool TOP>
+// MODE 1: max(p_t - q', 0) * S_t; MODE 2: p_t * S_t.
+template <bool TOP, int MODE>
 __device__ __forceinline__ float residual_at(float zt, float zd, int v, const SeqState &st,
-                                             const ExpScale &e, const ResidualScale &rs, int mode)
+                                             const ExpScale &e, const ResidualScale &rs)
 {
     const float pt = exp_scaled(zt, st.m_t, e);  // p_t(v) * S_t
-    if (mode == 2) return pt;
+    if (MODE == 2) return pt;
     const float delta = zd - zt;
     bool top = false;
     if (TOP) top = v == st.top[0] || v == st.top[1] || v == st.top[2] || v == st.top[3];
     const float khi = top ? rs.kt_hi : rs.k_hi;
     const float klo = top ? rs.kt_lo : rs.k_lo;
     const float d = __builtin_fmaf(delta, rs.c_hi, khi) + __builtin_fmaf(delta, rs.c_lo, klo);
-    if (!(d < 0.f)) return 0.f;  // q' >= p_t, or a masked target token
-    return pt * one_minus_exp2(d);
+    const float om = one_minus_exp2(d);
+    return om > 0.f ? pt * om : 0.f;  // q' >= p_t, a masked target token, or NaN: no mass
 }
 
 }  // namespace sv

@@ -1,6 +1,7 @@
 // sv_api.hip -- the C ABI of libspecverify: argument validation, the launch
 // plan, the workspace layout and the split into sub-batches.  The operation is specified in include/specverify.h.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 
 #include "sv_internal.h"
@@ -132,6 +133,8 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
         a.temperature = temperature + b0;
         a.seed = seed;
         a.beta = beta;
+        a.ln_beta = std::log((double)beta);
+        a.log2_beta = std::log2((double)beta);
         a.weighted = (beta < 1.f && K > 0) ? 1 : 0;
         a.accepted_len = accepted_len + b0;
         a.out_tokens = out_tokens + (int64_t)b0 * (K + 1);

@@ -163,41 +163,124 @@ __device__ __forceinline__ float exp_scaled(float x, float m, const ExpScale &e)
 }
 
 // ---------------------------------------------------------------------------
-// Wave64 and workgroup reductions (fixed trees, so results are reproducible).
+// Wave64 all-reductions without LDS: DPP within each 16-lane row (quad
+// butterflies, then the half-row and row mirrors; after each step every lane
+// of the group holds the group's value), then v_permlane16_swap and
+// v_permlane32_swap across rows.  A swap of a register with itself returns
+// the two halves being combined, so op(first, second) is the butterfly
+// result on every lane.  Fixed trees: results are reproducible, and equal in
+// every lane.  Callers run them with all 64 lanes active.
+
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_float(float v)
+{
+    return __int_as_float(dpp_int<CTRL>(__float_as_int(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_double(double v)
+{
+    const int lo = dpp_int<CTRL>(__double2loint(v));
+    const int hi = dpp_int<CTRL>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+
+// The two halves a row-pair (16) or wave-half (32) butterfly combines.
+struct IntPair {
+    int a, b;
+};
+
+template <int SPAN>
+__device__ __forceinline__ IntPair swap_halves(int v)
+{
+    if (SPAN == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return {(int)p[0], (int)p[1]};
+    }
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return {(int)p[0], (int)p[1]};
+}
+
+template <int SPAN>
+__device__ __forceinline__ void swap_halves_float(float v, float &x, float &y)
+{
+    const IntPair p = swap_halves<SPAN>(__float_as_int(v));
+    x = __int_as_float(p.a);
+    y = __int_as_float(p.b);
+}
+
+template <int SPAN>
+__device__ __forceinline__ void swap_halves_double(double v, double &x, double &y)
+{
+    const IntPair lo = swap_halves<SPAN>(__double2loint(v));
+    const IntPair hi = swap_halves<SPAN>(__double2hiint(v));
+    x = __hiloint2double(hi.a, lo.a);
+    y = __hiloint2double(hi.b, lo.b);
+}
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_float<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_float<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_float<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_float<kDppRowMirror>(v));
+    float x, y;
+    swap_halves_float<16>(v, x, y);
+    v = fmaxf(x, y);
+    swap_halves_float<32>(v, x, y);
+    return fmaxf(x, y);
 }
 
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_double<kDppQuadXor1>(v);
+    v += dpp_double<kDppQuadXor2>(v);
+    v += dpp_double<kDppRowHalfMirror>(v);
+    v += dpp_double<kDppRowMirror>(v);
+    double x, y;
+    swap_halves_double<16>(v, x, y);
+    v = x + y;
+    swap_halves_double<32>(v, x, y);
+    return x + y;
+}
+
+template <class Op>
+__device__ __forceinline__ int wave_reduce_int(int v, Op op)
+{
+    v = op(v, dpp_int<kDppQuadXor1>(v));
+    v = op(v, dpp_int<kDppQuadXor2>(v));
+    v = op(v, dpp_int<kDppRowHalfMirror>(v));
+    v = op(v, dpp_int<kDppRowMirror>(v));
+    IntPair p = swap_halves<16>(v);
+    v = op(p.a, p.b);
+    p = swap_halves<32>(v);
+    return op(p.a, p.b);
 }
 
 __device__ __forceinline__ int wave_min_int(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce_int(v, [](int x, int y) { return min(x, y); });
 }
 
 __device__ __forceinline__ int wave_sum_int(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return wave_reduce_int(v, [](int x, int y) { return x + y; });
 }
 
 __device__ __forceinline__ int wave_max_int(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce_int(v, [](int x, int y) { return max(x, y); });
 }
 
 // (value desc, index asc) order used for argmax and top-4.
@@ -206,17 +289,41 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j)
     return v > w || (v == w && i < j);
 }
 
+__device__ __forceinline__ void argmax_step(float &v, int &i, float w, int j)
+{
+    if (better(w, j, v, i)) {
+        v = w;
+        i = j;
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &i)
+{
+    const float w = dpp_float<CTRL>(v);
+    const int j = dpp_int<CTRL>(i);
+    argmax_step(v, i, w, j);
+}
+
+template <int SPAN>
+__device__ __forceinline__ void argmax_swap(float &v, int &i)
+{
+    float x, y;
+    swap_halves_float<SPAN>(v, x, y);
+    const IntPair p = swap_halves<SPAN>(i);
+    v = x;
+    i = p.a;
+    argmax_step(v, i, y, p.b);
+}
+
 __device__ __forceinline__ void wave_argmax(float &v, int &i)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float w = __shfl_xor(v, o, 64);
-        const int j = __shfl_xor(i, o, 64);
-        if (better(w, j, v, i)) {
-            v = w;
-            i = j;
-        }
-    }
+    argmax_dpp<kDppQuadXor1>(v, i);
+    argmax_dpp<kDppQuadXor2>(v, i);
+    argmax_dpp<kDppRowHalfMirror>(v, i);
+    argmax_dpp<kDppRowMirror>(v, i);
+    argmax_swap<16>(v, i);
+    argmax_swap<32>(v, i);
 }
 
 template <int NW = kWaves>
@@ -296,20 +403,37 @@ __device__ __forceinline__ void block_argmax(float &v, int &i, float *ldsv, int 
     __syncthreads();
 }
 
+// Inclusive prefix sum over the wave in lane order: Hillis-Steele shifts of
+// 1, 2, 4, 8 lanes within each row (lanes without a source add 0), then the
+// last lane of row 0 (2) is broadcast into row 1 (3), and the last lane of
+// the lower half into rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_double_or0(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double wave_inclusive_scan(double v)
+{
+    v += dpp_double_or0<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_double_or0<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_double_or0<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_double_or0<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_double_or0<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_double_or0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // Exclusive prefix sum over the workgroup in thread order; `total` receives
 // the sum of all values.
 template <int NW = kWaves>
 __device__ __forceinline__ double block_exclusive_scan(double v, double &total, double *lds)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += y;
-    }
-    double exc = __shfl_up(inc, 1, 64);
-    if (lane == 0) exc = 0.0;
+    const double inc = wave_inclusive_scan(v);
+    const double exc = dpp_double_or0<0x138, 0xf>(inc);  // wave_shr:1, lane 0 gets 0
     if (lane == 63) lds[wave] = inc;
     __syncthreads();
     double off = 0.0;

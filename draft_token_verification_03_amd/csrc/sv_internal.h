@@ -18,6 +18,7 @@ constexpr int kFillBlocks = 2048;        // workgroups the streaming grid aims f
 constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
 constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials
 constexpr int kResFill = 1024;           // workgroups the residual grid aims for (one round)
+constexpr int kResLoads = 4;             // residual units in flight per lane (per row)
 constexpr int kSlotVec = 64;             // 16-byte vectors per residual slot unit (one per lane)
 constexpr int kSlotUnits = 4;            // units per slot when the batch alone fills the grid
 constexpr int kMaxResSlots = 4096;       // residual slots per row (coarser slots beyond)
@@ -71,6 +72,7 @@ struct Args {
     int64_t row_bytes;
     uint64_t seed;
     float beta;
+    double ln_beta, log2_beta;  // of beta, -inf for beta == 0
     int32_t weighted;
     int32_t *accepted_len;
     int32_t *out_tokens;

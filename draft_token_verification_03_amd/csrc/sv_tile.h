@@ -198,8 +198,8 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
                 while (bits) {
                     const int src = __ffsll((unsigned long long)bits) - 1;
                     bits &= bits - 1;
-                    const float v = __shfl(x[k], src, 64);
-                    const int idx = __shfl(elem_index(q0, u, k, VEC), src, 64);
+                    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), src));
+                    const int idx = __builtin_amdgcn_readlane(elem_index(q0, u, k, VEC), src);
                     float ov = v;
                     int oi = idx;
                     top_insert_out(W, v, idx, ov, oi);  // on insertion (ov, oi) is the evicted entry

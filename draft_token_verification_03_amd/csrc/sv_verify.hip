@@ -25,26 +25,25 @@
 
 namespace sv {
 
-// kLoads vectors q = qb + u*kBlock + tid of a row, all loads issued before use;
-// vectors at or beyond q1 and elements at or beyond V read as -inf.
-template <int DT>
-__device__ __forceinline__ void load_step(const char *row, bool aligned, bool stream, int qb, int q1,
-                                          int V, uint4 (&r)[kLoads])
+// Tiles of the streaming pass: kLoads vectors q = qb + u*kBlock + tid of a
+// row per thread.  issue_tile only requests the loads (aligned rows: indices
+// clamped into the chunk, so every load is unconditional); fix_tile, run by
+// the consumer on a chunk's last tile only, turns the vectors at or beyond q1
+// (re-reads of vector q1 - 1) and the elements at or beyond V into -inf.
+// Masking right after issuing would make each load wait before the next tile
+// could be requested.  Unaligned rows load through funnel shifts and are
+// masked as they are loaded.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void issue_tile(const char *row, int qb, int q1, int V, uint4 (&r)[kLoads])
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int tid = threadIdx.x;
-    if (aligned) {
-        // every load is issued before any is used: vectors at or beyond q1
-        // re-read vector q1 - 1 and are replaced by -inf afterwards
+    if (ALIGNED) {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
             const int q = min(qb + u * kBlock + tid, q1 - 1);
-            r[u] = stream ? load16_stream(row + (size_t)q * 16)
-                          : *reinterpret_cast<const uint4 *>(row + (size_t)q * 16);
+            r[u] = load16_stream(row + (size_t)q * 16);
         }
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u)
-            if (qb + u * kBlock + tid >= q1) r[u] = neg_inf_raw<DT>();
     } else {
 #pragma unroll
         for (int u = 0; u < kLoads; ++u) {
@@ -59,11 +58,47 @@ __device__ __forceinline__ void load_step(const char *row, bool aligned, bool st
             }
         }
     }
+}
+
+template <int DT>
+__device__ __forceinline__ void fix_tile(int qb, int q1, int V, uint4 (&r)[kLoads])
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+        if (qb + u * kBlock + tid >= q1) r[u] = neg_inf_raw<DT>();
     if (V % VEC) {
         const int last = (V - 1) / VEC;
 #pragma unroll
         for (int u = 0; u < kLoads; ++u)
             if (qb + u * kBlock + tid == last) mask_raw<DT>(r[u], V - last * VEC);
+    }
+}
+
+// Stream the chunk [q0, q1) of a row through consume(tile, qb), two tiles
+// in flight: the next tile is requested before the current one is consumed.
+// `ra` holds the (already requested) tile at q0.  The row's alignment is a
+// template parameter so that no loaded register passes a branch join (a
+// join copies registers, and a copy waits for its load).
+template <int DT, bool ALIGNED, class Consume>
+__device__ __forceinline__ void stream_chunk(const char *row, int q0, int q1, int V,
+                                             uint4 (&ra)[kLoads], Consume &&consume)
+{
+    constexpr int kStep = kBlock * kLoads;
+    uint4 rb[kLoads];
+    for (int qb = q0;;) {
+        const int qn = qb + kStep;
+        if (qn < q1) issue_tile<DT, ALIGNED>(row, qn, q1, V, rb);
+        if (qn >= q1) fix_tile<DT>(qb, q1, V, ra);
+        consume(ra, qb);
+        if (qn >= q1) return;
+        const int qn2 = qn + kStep;
+        if (qn2 < q1) issue_tile<DT, ALIGNED>(row, qn2, q1, V, ra);
+        if (qn2 >= q1) fix_tile<DT>(qn, q1, V, rb);
+        consume(rb, qn);
+        if (qn2 >= q1) return;
+        qb = qn2;
     }
 }
 
@@ -140,28 +175,19 @@ __device__ __forceinline__ const char *draft_row(const Args &a, int b, int i)
 // (draft rows in greedy mode or without draft logits, rows of a sequence with
 // an invalid temperature) publish nothing.
 
-template <int DT, bool TOP>
-__global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
+// One (row, chunk) of the streaming pass; the first tile is requested before
+// the temperature is looked at.
+template <int DT, bool TOP, bool ALIGNED>
+__device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int b, int i, bool is_draft,
+                                            int slot_row, int chunk, float T)
 {
     __shared__ float lds_f[4 + kWaves * 4];
     __shared__ int lds_i[4 + kWaves * 4];
     __shared__ double lds_d[kWaves];
-
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x % a.nc;
-    const int slot_row = blockIdx.x / a.nc;
-    const int b = slot_row / a.R;
-    const int j = slot_row - b * a.R;
-    const bool is_draft = j > a.K;
-    if (is_draft && a.draft == nullptr) return;
-    const int i = is_draft ? j - (a.K + 1) : j;
-    const float T = a.temperature[b];
-    const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
-    const bool aligned = ((uintptr_t)row & 15) == 0;
     const int q0 = chunk * a.cvec;
     const int q1 = min(a.nvec, q0 + a.cvec);
     uint4 r[kLoads];
-    load_step<DT>(row, aligned, true, q0, q1, a.V, r);
+    issue_tile<DT, ALIGNED>(row, q0, q1, a.V, r);
 
     const bool greedy = T == 0.f;
     if (!temperature_ok(T) || (is_draft && greedy)) return;
@@ -171,12 +197,9 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
     if (greedy) {
         float best = -INFINITY;
         int bi = INT_MAX;
-        for (int qb = q0;;) {
-            run_argmax_tile<DT, kLoads>(r, qb, best, bi);
-            qb += kBlock * kLoads;
-            if (qb >= q1) break;
-            load_step<DT>(row, aligned, true, qb, q1, a.V, r);
-        }
+        stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
+            run_argmax_tile<DT, kLoads>(t, qb, best, bi);
+        });
         block_argmax(best, bi, lds_f, lds_i);
         part.m = best;
         part.idx = bi;
@@ -187,21 +210,39 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
         run_clear(run);
         Top4 t4;
         top_clear(t4);
-        for (int qb = q0;;) {
-            if (track_top) run_sum_top_tile<DT, kLoads>(r, qb, a.V, e, run, t4);
-            else run_sum_tile<DT, kLoads>(r, e, run);
-            qb += kBlock * kLoads;
-            if (qb >= q1) break;
-            load_step<DT>(row, aligned, true, qb, q1, a.V, r);
+        if (track_top) {
+            stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
+                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, t4);
+            });
+            run_finish_top(run, t4, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
+        } else {
+            stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
+                run_sum_tile<DT, kLoads>(t, e, run);
+            });
+            run_finish(run, e, lds_f, lds_d, part.m, part.s);
         }
-        if (track_top) run_finish_top(run, t4, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
-        else run_finish(run, e, lds_f, lds_d, part.m, part.s);
         part.idx = -1;
     }
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
         a.part[(int64_t)slot_row * a.nc + chunk] = part;
         if (track_top) a.top[((int64_t)b * a.K + i) * a.nc + chunk] = ct;
     }
+}
+
+template <int DT, bool TOP>
+__global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
+{
+    const int chunk = blockIdx.x % a.nc;
+    const int slot_row = blockIdx.x / a.nc;
+    const int b = slot_row / a.R;
+    const int j = slot_row - b * a.R;
+    const bool is_draft = j > a.K;
+    if (is_draft && a.draft == nullptr) return;
+    const int i = is_draft ? j - (a.K + 1) : j;
+    const float T = a.temperature[b];
+    const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
+    if (((uintptr_t)row & 15) == 0) stats_chunk<DT, TOP, true>(a, row, b, i, is_draft, slot_row, chunk, T);
+    else stats_chunk<DT, TOP, false>(a, row, b, i, is_draft, slot_row, chunk, T);
 }
 
 // ---------------------------------------------------------------------------
@@ -238,8 +279,9 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
         off = align16(off + bytes);
         return base ? base + o : nullptr;
     };
-    unsigned char *p_part = take(sizeof(RowPart) * (size_t)R * nc);
-    unsigned char *p_ptop = take(weighted ? sizeof(Top4) * (size_t)K * nc : 0);
+    static_assert(sizeof(RowPart) == 16 && sizeof(Top4) == 32, "16-byte staging granules");
+    unsigned char *p_part = take(sizeof(RowPart) * (size_t)R * nc);  // ends on a granule:
+    unsigned char *p_ptop = take(weighted ? sizeof(Top4) * (size_t)K * nc : 0);  // contiguous
     unsigned char *p_S = take(sizeof(double) * (size_t)R);
     unsigned char *p_m = take(sizeof(float) * (size_t)R);
     unsigned char *p_idx = take(sizeof(int) * (size_t)R);
@@ -289,22 +331,15 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
         const int PT = a.weighted ? K * nc : 0;
         const uint4 *gp = reinterpret_cast<const uint4 *>(a.part + (int64_t)b * a.R * nc);
         const uint4 *gt = reinterpret_cast<const uint4 *>(a.top + (int64_t)b * K * nc);
-        uint4 *sp = reinterpret_cast<uint4 *>(L.part);
-        uint4 *st4 = reinterpret_cast<uint4 *>(L.ptop);
-        const int total4 = P + 2 * PT;  // a RowPart is one granule, a Top4 two
-        for (int base = 0; base < total4; base += 4 * kBlock) {
-            uint4 v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int jj = base + k * kBlock + tid;
-                if (jj < total4) v[k] = jj < P ? gp[jj] : gt[jj - P];
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int jj = base + k * kBlock + tid;
-                if (jj < P) sp[jj] = v[k];
-                else if (jj < total4) st4[jj - P] = v[k];
-            }
+        uint4 *s4 = reinterpret_cast<uint4 *>(L.part);  // the top-4 lists follow the partials
+        const int total4 = P + 2 * PT;                  // a RowPart is one granule, a Top4 two
+        for (int base = 0; base < total4; base += 2 * kBlock) {
+            const int j0 = base + tid, j1 = base + kBlock + tid;
+            uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+            if (j0 < total4) v0 = j0 < P ? gp[j0] : gt[j0 - P];
+            if (j1 < total4) v1 = j1 < P ? gp[j1] : gt[j1 - P];
+            if (j0 < total4) s4[j0] = v0;
+            if (j1 < total4) s4[j1] = v1;
         }
     }
     const bool greedy = T == 0.f;
@@ -370,8 +405,9 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
             const bool in_top = weighted && top_has(L.top[i], x);
             const float u = philox_uniform(a.seed, gb, (uint32_t)i, kPurposeAccept);
             float pt, pd;
-            L.acc[i] = decide(T, mt, L.S[i], md, L.S[K + 1 + i], in_top, a.beta, x_ok && err == 0, zt,
-                              zd, u, pt, pd)
+            const bool want_p = publish && (a.aux_pt != nullptr || a.aux_pd != nullptr);
+            L.acc[i] = decide(T, mt, L.S[i], md, L.S[K + 1 + i], in_top, a.ln_beta, x_ok && err == 0,
+                              zt, zd, u, want_p, pt, pd)
                            ? 1
                            : 0;
             L.err[i] = err;
@@ -445,11 +481,11 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
                 st.u_bonus = philox_uniform(a.seed, gb, (uint32_t)n, kPurposeBonus);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) st.top[k] = -1;
-                st.lbeta = (float)log2((double)a.beta);
+                st.lbeta = (float)a.log2_beta;
                 if (n < K) {
                     st.m_d = L.m[K + 1 + n];
                     st.k2 = ((double)L.m[n] - (double)L.m[K + 1 + n]) * (kLog2e / (double)T) +
-                            log2(L.S[n]) - log2(L.S[K + 1 + n]);
+                            log2(L.S[n] / L.S[K + 1 + n]);
                     if (weighted) {
 #pragma unroll
                         for (int k = 0; k < 4; ++k)
@@ -489,18 +525,18 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
 
 // Residual of the elements of one 16-byte vector pair; returns the fp32
 // pairwise sum of the vector's values and fills r[].
-template <int DT, bool TOP>
-__device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, int mode, const SeqState &st,
+template <int DT, bool TOP, int MODE>
+__device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, const SeqState &st,
                                               const ExpScale &e, const ResidualScale &rs,
                                               float (&r)[Elt<DT>::kVec])
 {
     constexpr int VEC = Elt<DT>::kVec;
     float xt[VEC], xd[VEC];
     Elt<DT>::unpack(rt, xt);
-    if (mode == 1) Elt<DT>::unpack(rd, xd);
+    if (MODE == 1) Elt<DT>::unpack(rd, xd);
 #pragma unroll
     for (int k = 0; k < VEC; ++k)
-        r[k] = residual_at<TOP>(xt[k], mode == 1 ? xd[k] : 0.f, q * VEC + k, st, e, rs, mode);
+        r[k] = residual_at<TOP, MODE>(xt[k], MODE == 1 ? xd[k] : 0.f, q * VEC + k, st, e, rs);
     float s[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) s[k] = r[k];
@@ -514,12 +550,12 @@ __device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, int mod
 // Residual mass of the slots [s_begin, s_end) of the row pair into slot[].
 // Slot s covers the vectors [s*gs*kSlotVec, (s+1)*gs*kSlotVec); the NW waves
 // of the workgroup take the slots in turn, and a wave's 64 lanes read
-// kSlotVec consecutive vectors (1 KiB of each row) per load, kLoads units in
+// kSlotVec consecutive vectors (1 KiB of each row) per load, kResLoads units in
 // flight per lane.  Each slot is summed by one wave in a fixed order (fp32
 // within a vector, fp64 across vectors and lanes).
-template <int DT, bool TOP, int NW>
-__device__ void residual_slots(const char *trow, const char *drow, int mode, int V, int nvec,
-                               int s_begin, int s_end, int gs, const SeqState &st, const ExpScale &e,
+template <int DT, bool TOP, int NW, int MODE>
+__device__ void residual_slots(const char *trow, const char *drow, int V, int nvec, int s_begin,
+                               int s_end, int gs, const SeqState &st, const ExpScale &e,
                                const ResidualScale &rs, double *slot)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -527,15 +563,16 @@ __device__ void residual_slots(const char *trow, const char *drow, int mode, int
     const int ns = s_end - s_begin;
     const int my_slots = ns > wave ? (ns - wave + NW - 1) / NW : 0;
     const int items = my_slots * gs;
+    const bool fast = ta && (MODE == 2 || da) && V % Elt<DT>::kVec == 0;
     double acc = 0.0;
     // item f = t * gs + j is unit j of the wave's t-th slot, s_begin + wave + NW * t
     int t = 0, j = 0;
-    for (int f0 = 0; f0 < items; f0 += kLoads) {
-        uint4 rt[kLoads], rd[kLoads];
-        int qv[kLoads], tv[kLoads];
-        bool endv[kLoads], live[kLoads];
+    for (int f0 = 0; f0 < items; f0 += kResLoads) {
+        uint4 rt[kResLoads], rd[kResLoads];
+        int qv[kResLoads], tv[kResLoads];
+        bool endv[kResLoads], live[kResLoads];
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
+        for (int u = 0; u < kResLoads; ++u) {
             const int s = s_begin + wave + NW * t;
             const int q = (s * gs + j) * kSlotVec + lane;
             qv[u] = q;
@@ -547,13 +584,28 @@ __device__ void residual_slots(const char *trow, const char *drow, int mode, int
                 ++t;
             }
         }
-        load_units<DT, kLoads>(trow, ta, qv, live, nvec, V, rt);
-        if (mode == 1) load_units<DT, kLoads>(drow, da, qv, live, nvec, V, rd);
+        if (fast) {
+            // aligned rows of whole vectors: unconditional loads (indices
+            // clamped into the row) with no mask to wait on; a unit that is
+            // not live adds nothing below
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) {
+            for (int u = 0; u < kResLoads; ++u)
+                rt[u] = *reinterpret_cast<const uint4 *>(trow + (size_t)min(qv[u], nvec - 1) * 16);
+            if (MODE == 1) {
+#pragma unroll
+                for (int u = 0; u < kResLoads; ++u)
+                    rd[u] = *reinterpret_cast<const uint4 *>(drow + (size_t)min(qv[u], nvec - 1) * 16);
+            }
+        } else {
+            load_units<DT, kResLoads>(trow, ta, qv, live, nvec, V, rt);
+            if (MODE == 1) load_units<DT, kResLoads>(drow, da, qv, live, nvec, V, rd);
+        }
+#pragma unroll
+        for (int u = 0; u < kResLoads; ++u) {
             if (f0 + u >= items) break;
             float r[Elt<DT>::kVec];
-            acc += (double)residual_vec<DT, TOP>(rt[u], rd[u], qv[u], mode, st, e, rs, r);
+            const float sum = residual_vec<DT, TOP, MODE>(rt[u], rd[u], qv[u], st, e, rs, r);
+            acc += live[u] ? (double)sum : 0.0;
             if (endv[u]) {
                 const double tot = wave_sum(acc);
                 if (lane == 0) slot[s_begin + wave + NW * tv[u]] = tot;
@@ -580,8 +632,11 @@ __global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
     const char *trow = target_row(a, b, st.n);
     const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
     const int s0 = g * a.spg, s1 = min(a.nslot, s0 + a.spg);
-    residual_slots<DT, TOP, kWaves>(trow, drow, st.mode, a.V, a.nvec, s0, s1, a.gs, st, e, rs,
-                                    a.slot + (int64_t)b * a.nslot);
+    double *slot = a.slot + (int64_t)b * a.nslot;
+    if (st.mode == 1)
+        residual_slots<DT, TOP, kWaves, 1>(trow, drow, a.V, a.nvec, s0, s1, a.gs, st, e, rs, slot);
+    else
+        residual_slots<DT, TOP, kWaves, 2>(trow, drow, a.V, a.nvec, s0, s1, a.gs, st, e, rs, slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -594,9 +649,9 @@ __global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
 // for the first element with mass whose running sum reaches `thr`.  Returns
 // that element, or INT_MAX when rounding leaves `thr` above the range; `last`
 // receives the last element of the range with positive mass.
-template <int DT, bool TOP>
-__device__ int scan_range(const char *trow, const char *drow, int mode, int V, int nvec, int q0,
-                          int q1, double base, double thr, const SeqState &st, const ExpScale &e,
+template <int DT, bool TOP, int MODE>
+__device__ int scan_range(const char *trow, const char *drow, int V, int nvec, int q0, int q1,
+                          double base, double thr, const SeqState &st, const ExpScale &e,
                           const ResidualScale &rs, int &last, double *lds_d, int *lds_i)
 {
     constexpr int VEC = Elt<DT>::kVec;
@@ -608,9 +663,9 @@ __device__ int scan_range(const char *trow, const char *drow, int mode, int V, i
         const bool live = q < q1;
         const uint4 rt = live ? load_one<DT>(trow, ta, q, nvec, V) : neg_inf_raw<DT>();
         uint4 rd = neg_inf_raw<DT>();
-        if (mode == 1 && live) rd = load_one<DT>(drow, da, q, nvec, V);
+        if (MODE == 1 && live) rd = load_one<DT>(drow, da, q, nvec, V);
         float r[VEC];
-        residual_vec<DT, TOP>(rt, rd, q, mode, st, e, rs, r);
+        residual_vec<DT, TOP, MODE>(rt, rd, q, st, e, rs, r);
         double pre[VEC];
         double acc = 0.0;
         int mylast = -1;
@@ -636,11 +691,10 @@ __device__ int scan_range(const char *trow, const char *drow, int mode, int V, i
 
 // Inverse CDF over the slot masses in slot[0..nslot): returns the token (-1
 // when the mass is 0) and Z, the total mass.
-template <int DT, bool TOP>
-__device__ int draw_token(const char *trow, const char *drow, int mode, int V, int nvec, int nslot,
-                          int gs, float u, const SeqState &st, const ExpScale &e,
-                          const ResidualScale &rs, const double *slot, double &Z, double *lds_d,
-                          int *lds_i)
+template <int DT, bool TOP, int MODE>
+__device__ int draw_token(const char *trow, const char *drow, int V, int nvec, int nslot, int gs,
+                          float u, const SeqState &st, const ExpScale &e, const ResidualScale &rs,
+                          const double *slot, double &Z, double *lds_d, int *lds_i)
 {
     const int tid = threadIdx.x;
     const int per = (nslot + kBlock - 1) / kBlock;
@@ -678,8 +732,8 @@ __device__ int draw_token(const char *trow, const char *drow, int mode, int V, i
     __syncthreads();
     const int q0 = sel * gs * kSlotVec, q1 = min(nvec, q0 + gs * kSlotVec);
     int last;
-    const int tok = scan_range<DT, TOP>(trow, drow, mode, V, nvec, q0, q1, base, thr, st, e, rs, last,
-                                        lds_d, lds_i);
+    const int tok = scan_range<DT, TOP, MODE>(trow, drow, V, nvec, q0, q1, base, thr, st, e, rs, last,
+                                              lds_d, lds_i);
     return tok != INT_MAX ? tok : last;
 }
 
@@ -702,14 +756,17 @@ __global__ __launch_bounds__(kBlock) void bonus_kernel(const Args a)
     const char *trow = target_row(a, b, st.n);
     const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
     double Z;
-    int token = draw_token<DT, TOP>(trow, drow, st.mode, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e,
-                                    rs, slot, Z, lds_d, lds_i);
+    int token = st.mode == 1
+                    ? draw_token<DT, TOP, 1>(trow, drow, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e, rs,
+                                             slot, Z, lds_d, lds_i)
+                    : draw_token<DT, TOP, 2>(trow, drow, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e, rs,
+                                             slot, Z, lds_d, lds_i);
     if (token < 0) {
         // zero residual mass: the slot masses of p_t, by this workgroup alone
-        residual_slots<DT, TOP, kWaves>(trow, trow, 2, a.V, a.nvec, 0, a.nslot, a.gs, st, e, rs, slot);
+        residual_slots<DT, TOP, kWaves, 2>(trow, trow, a.V, a.nvec, 0, a.nslot, a.gs, st, e, rs, slot);
         __syncthreads();
-        token = draw_token<DT, TOP>(trow, trow, 2, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e, rs,
-                                    slot, Z, lds_d, lds_i);
+        token = draw_token<DT, TOP, 2>(trow, trow, a.V, a.nvec, a.nslot, a.gs, st.u_bonus, st, e, rs, slot,
+                                       Z, lds_d, lds_i);
     }
     if (tid == 0) {
         a.out_tokens[(int64_t)b * (a.K + 1) + st.n] = token;
