@@ -130,7 +130,9 @@ def main() -> int:
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
     base = make_inputs(w, seed=args.seed, device=dev)
     alg_bytes = w.algorithmic_bytes()
-    reps = max(1, math.ceil(2 * MALL_BYTES / alg_bytes))
+    # at least two copies: consecutive steps never read the same bytes, so no
+    # step is served from what the previous one left in the Infinity Cache
+    reps = max(2, math.ceil(2 * MALL_BYTES / alg_bytes))
     replicas = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
                          for _ in range(reps - 1)]
     ws = sv.alloc_workspace(w.B, w.K, w.V, base["target"].dtype, dev)

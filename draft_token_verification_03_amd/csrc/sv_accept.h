@@ -9,10 +9,12 @@ __device__ __forceinline__ bool temperature_ok(float T) { return T >= 0.f && T !
 
 // ---------------------------------------------------------------------------
 // Wave-level merges of one row's chunk partials `p[0..nc)` (lanes stride the
-// chunks; the tail kernel stages them in LDS).  The same code merges target and draft rows, so equal rows merge to
-// bitwise-equal statistics.
+// chunks; the accept scan stages them in LDS).  A chunk's sum is relative to
+// its own offset fp32(m_c c); the merged sum S is relative to the row's,
+// fp32(M c).  The same code merges target and draft rows, so equal rows merge
+// to bitwise-equal statistics.
 
-__device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, float &M, double &S)
+__device__ __forceinline__ void merge_sum(const RowPart *p, int nc, const ExpScale &e, float &M, double &S)
 {
     if (nc == 1) {  // a whole row per chunk: its partial is the row's statistic
         M = p[0].m;
@@ -23,10 +25,11 @@ __device__ __forceinline__ void merge_sum(const RowPart *p, int nc, double c64, 
     float m = -INFINITY;
     for (int c = lane; c < nc; c += 64) m = fmaxf(m, p[c].m);
     m = wave_max(m);
+    const double om = (double)row_offset(m, e);
     double s = 0.0;
     for (int c = lane; c < nc; c += 64) {
         const RowPart r = p[c];
-        if (r.m != -INFINITY && r.s != 0.0) s += r.s * exp2(((double)r.m - (double)m) * c64);
+        if (r.m != -INFINITY && r.s != 0.0) s += r.s * exp2((double)row_offset(r.m, e) - om);
     }
     S = wave_sum(s);
     M = m;
@@ -59,13 +62,14 @@ __device__ __forceinline__ void merge_argmax(const RowPart *p, int nc, float &M,
 // is summed directly (never as S - S_top, which cancels when the top-4 hold
 // nearly all the mass).  Returns the row max M, the row top-4, the mass
 // outside it (S_rest) and inside it (S_top), all relative to exp2((z - M) c).
-__device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp, int nc, double c64,
-                                               float &M, Top4 &row_top, double &S_rest,
-                                               double &S_top)
+__device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp, int nc,
+                                               const ExpScale &e, float &M, Top4 &row_top,
+                                               double &S_rest, double &S_top)
 {
     const int lane = threadIdx.x & 63;
     double s_excl;
-    merge_sum(p, nc, c64, M, s_excl);
+    merge_sum(p, nc, e, M, s_excl);
+    const double om = (double)row_offset(M, e);
     if (nc == 1) {  // the chunk's top-4 is the row's; nothing else to move
         row_top = tp[0];
         S_rest = s_excl;
@@ -84,7 +88,7 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
-                    extra += exp2(((double)r.v[k] - (double)M) * c64);
+                    extra += exp_scaled64(r.v[k], om, e.c64);
         }
         S_rest = s_excl + wave_sum(extra);
     }
@@ -93,7 +97,7 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         if (lane == k && row_top.i[k] != INT_MAX && row_top.v[k] != -INFINITY)
-            st = exp2(((double)row_top.v[k] - (double)M) * c64);
+            st = exp_scaled64(row_top.v[k], om, e.c64);
     S_top = wave_sum(st);
 }
 
@@ -101,35 +105,34 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
 // One accept test ("Kangaroo: Self-Speculative Decoding via Shallow
 // Sub-Networks", "3. Lossless Speculative Verification"; glossary
 // "speculative decoding llm", "Why It Produces Identical Outputs"): accept x
-// iff u <= p(x) / q'(x), with the ratio formed in fp64 in the log domain,
-//   ln r = [(z_t(x) - m_t) - (z_d(x) - m_d)] / T + ln(D / S_t) + ln w(x),
-// with D = S_d unweighted, or S_rest + beta * S_top for the Saguaro-style
-// draft ("Speculative Speculative Decoding", "Method"), w(x) = 1/beta on the
-// draft's top-4 and 1 elsewhere (ln_beta = ln beta, from the host).  Only the
-// final exponential is fp32: rounding ln r to fp32 moves r by at most
-// r |ln r| 2^-24 <= 2.2e-8 where r <= 1, below the uniforms' 2^-24 grid.  A
-// token the draft law gives no mass is accepted (the ratio is +inf).  The
-// diagnostics p(x), q'(x) are only formed when asked for (fp32 logs: ~1e-6
-// relative).
-__device__ __forceinline__ bool decide(float T, float mt, double St, float md, double D,
-                                       bool weighted_top, double ln_beta, bool x_ok, float zt,
+// iff u <= p(x) / q'(x), with the ratio formed in fp64 in base 2,
+//   log2 r = (z_t(x) c - o_t) - (z_d(x) c - o_d) + log2(D / S_t) - log2 w(x),
+// where o_t, o_d are the rows' offsets, S_t the target row's sum relative to
+// o_t, D the draft row's normaliser relative to o_d (S_d unweighted, or
+// S_rest + beta * S_top for the Saguaro-style draft, "Speculative Speculative
+// Decoding", "Method"), and w(x) = beta on the draft's top-4, 1 elsewhere
+// (log2_beta from the host).  Only the final exponential is fp32: rounding
+// log2 r to fp32 moves r by at most r |ln r| 2^-24 <= 2.2e-8 where r <= 1,
+// below the uniforms' 2^-24 grid.  A token the draft law gives no mass is
+// accepted (the ratio is +inf).  The diagnostics p(x), q'(x) are only formed
+// when asked for.
+__device__ __forceinline__ bool decide(const ExpScale &e, float ot, double St, float od, double D,
+                                       bool weighted_top, double log2_beta, bool x_ok, float zt,
                                        float zd, float u, bool want_p, float &pt, float &pd)
 {
     pt = NAN;
     pd = NAN;
     if (!x_ok) return false;
-    const double Td = (double)T;
-    const double dt = (double)zt - (double)mt, dd = (double)zd - (double)md;  // exact
-    const bool no_draft_mass = dd == -INFINITY || (weighted_top && ln_beta == -INFINITY);
-    double lr = (dt - dd) / Td + log(D / St);
-    if (weighted_top) lr -= ln_beta;
-    const bool accept = no_draft_mass || (double)u <= (double)__expf((float)lr);
+    const double lt = (double)zt * e.c64 - (double)ot;  // log2(p(x) S_t), zt c exact
+    const double ld = (double)zd * e.c64 - (double)od;  // log2(q(x) D / w(x))
+    const bool no_draft_mass = zd == -INFINITY || (weighted_top && log2_beta == -INFINITY);
+    double lr = lt - ld + log2(D / St);
+    if (weighted_top) lr -= log2_beta;
+    const bool accept = no_draft_mass || (double)u <= (double)__builtin_amdgcn_exp2f((float)lr);
     if (want_p) {
-        const float lpt = (float)(dt / Td) - __logf((float)St);
-        float lpd = (float)(dd / Td) - __logf((float)D);
-        if (weighted_top) lpd += (float)ln_beta;
-        pt = __expf(lpt);
-        pd = __expf(lpd);
+        const double lpd = ld - log2(D) + (weighted_top ? log2_beta : 0.0);
+        pt = __builtin_amdgcn_exp2f((float)(lt - log2(St)));
+        pd = __builtin_amdgcn_exp2f((float)lpd);
     }
     return accept;
 }
@@ -140,26 +143,30 @@ __device__ __forceinline__ bool decide(float T, float mt, double St, float md, d
 // Speculative Decoding", "Key claims", the residual max(p_t - p_d, 0)):
 // p_t in mode 2; in mode 1
 //   r(v) = max(p_t(v) - q'(v), 0) = p_t(v) * (1 - 2^d(v))  for d(v) < 0, else 0,
-// both returned times S_t (p_t(v) S_t = exp2((z_t(v) - m_t) log2e / T)): a
+// both returned times S_t (p_t(v) S_t = exp2(z_t(v) c - o_t)): a
 // factor common to the whole row, which cancels in the inverse CDF;
-//   d(v) = log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) log2e / T + k2 (+ log2 beta),
+//   d(v) = log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) c + k2 (+ log2 beta),
+//   k2 = o_t - o_d + log2(S_t / D),
 // so r keeps its relative accuracy when p_t and q' nearly cancel (small
 // residual mass), where p_t - q' taken in fp32 would carry an absolute error
-// of ~1e-7 of p_t.  d is formed in fp32 from constants split into hi + lo
-// parts: fma(delta, c_hi, k_hi) rounds once, so d carries an error of a few
-// ulp of d itself, not of its terms.
+// of ~1e-7 of p_t.  k2 is split into fp32 hi + lo parts: fma(delta, c, k_hi)
+// rounds once, so d carries an error of a few ulp of d itself, not of its
+// terms.
 
 struct ResidualScale {
-    float c_hi, c_lo;    // log2e / T
+    float c;             // fp32(log2e / T)
     float k_hi, k_lo;    // k2
     float kt_hi, kt_lo;  // k2 + log2 beta (draft top-4 tokens)
+    int tq[4];           // 16-byte vector of each draft top-4 token, -1 for none
 };
 
+template <int VEC>
 __device__ __forceinline__ ResidualScale make_residual_scale(const SeqState &st, const ExpScale &e)
 {
     ResidualScale r;
-    r.c_hi = e.hi;
-    r.c_lo = e.lo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.tq[k] = st.top[k] >= 0 ? st.top[k] / VEC : -1;
+    r.c = e.c;
     r.k_hi = (float)st.k2;
     r.k_lo = (float)(st.k2 - (double)r.k_hi);
     const double kt = st.k2 + (double)st.lbeta;  // -inf when beta == 0
@@ -184,21 +191,18 @@ __device__ __forceinline__ float one_minus_exp2(float d)
     return d >= -1.f ? poly : direct;
 }
 
-// MODE 1: max(p_t - q', 0) * S_t; MODE 2: p_t * S_t.
-template <bool TOP, int MODE>
-__device__ __forceinline__ float residual_at(float zt, float zd, int v, const SeqState &st,
-                                             const ExpScale &e, const ResidualScale &rs)
+// MODE 1: max(p_t - q', 0) * S_t with the offset (k_hi, k_lo) of the token's
+// draft weight; MODE 2: p_t * S_t.  The clamp is fmaxf, which returns 0 for
+// the NaN of a token masked in both rows (p_t = 0 there).
+template <int MODE>
+__device__ __forceinline__ float residual_at(float zt, float zd, const SeqState &st, const ExpScale &e,
+                                             const ResidualScale &rs, float khi, float klo)
 {
-    const float pt = exp_scaled(zt, st.m_t, e);  // p_t(v) * S_t
+    const float pt = exp_scaled(zt, st.o_t, e);  // p_t(v) * S_t
     if (MODE == 2) return pt;
     const float delta = zd - zt;
-    bool top = false;
-    if (TOP) top = v == st.top[0] || v == st.top[1] || v == st.top[2] || v == st.top[3];
-    const float khi = top ? rs.kt_hi : rs.k_hi;
-    const float klo = top ? rs.kt_lo : rs.k_lo;
-    const float d = __builtin_fmaf(delta, rs.c_hi, khi) + __builtin_fmaf(delta, rs.c_lo, klo);
-    const float om = one_minus_exp2(d);
-    return om > 0.f ? pt * om : 0.f;  // q' >= p_t, a masked target token, or NaN: no mass
+    const float d = __builtin_fmaf(delta, rs.c, khi) + klo;
+    return pt * fmaxf(one_minus_exp2(d), 0.f);  // q' >= p_t: no mass
 }
 
 }  // namespace sv

@@ -133,7 +133,6 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
         a.temperature = temperature + b0;
         a.seed = seed;
         a.beta = beta;
-        a.ln_beta = std::log((double)beta);
         a.log2_beta = std::log2((double)beta);
         a.weighted = (beta < 1.f && K > 0) ? 1 : 0;
         a.accepted_len = accepted_len + b0;

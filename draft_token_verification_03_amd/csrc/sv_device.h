@@ -136,30 +136,40 @@ __device__ __forceinline__ uint4 load16_stream(const char *p)
 }
 
 // ---------------------------------------------------------------------------
-// Exponent scale log2(e)/T split as c_hi + c_lo: c_hi is rounded toward zero
-// so c_lo >= 0, and c_lo is kept strictly positive so that -inf logits give
-// exp2(-inf) = 0 and never 0 * inf.
+// Exponentials of a row at temperature T are taken in base 2 with the scale
+// c = fp32(log2(e) / T): an element z contributes exp2(z c - o), where the
+// row offset o = fp32(m c) belongs to the row's (running) maximum m.  One fma
+// per element forms the argument exactly and rounds it once.  Every later
+// step (merges, accept ratio, residual) uses the same c and the same offsets
+// in fp64, so the path is exactly the softmax at T' = log2(e) / c, within a
+// relative 2^-24 of T: the accept ratios move by ~1e-7 at most.
 
 struct ExpScale {
-    float hi, lo;
-    double c64;
+    float c;     // fp32(log2(e) / T)
+    double c64;  // the same value in fp64
 };
 
 __device__ __forceinline__ ExpScale make_scale(float T)
 {
     ExpScale e;
-    e.c64 = kLog2e / (double)T;
-    e.hi = __double2float_rz(e.c64);
-    e.lo = (float)(e.c64 - (double)e.hi);
-    if (!(e.lo > 0.f)) e.lo = 1e-30f;
+    e.c = (float)(kLog2e / (double)T);
+    e.c64 = (double)e.c;
     return e;
 }
 
-// 2^((x - m) * log2(e) / T) with the product carried to ~2^-48 relative.
-__device__ __forceinline__ float exp_scaled(float x, float m, const ExpScale &e)
+// Row offset of a maximum m (-inf for an empty row).
+__device__ __forceinline__ float row_offset(float m, const ExpScale &e) { return m * e.c; }
+
+// exp2(x c - o) for an element x and a finite offset o.
+__device__ __forceinline__ float exp_scaled(float x, float o, const ExpScale &e)
 {
-    const float d = x - m;
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(d, e.hi, d * e.lo));
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(x, e.c, -o));
+}
+
+// exp2(x c - o) in fp64 (x c is exact in fp64) for merges of partial sums.
+__device__ __forceinline__ double exp_scaled64(float x, double o, double c64)
+{
+    return exp2((double)x * c64 - o);
 }
 
 // ---------------------------------------------------------------------------

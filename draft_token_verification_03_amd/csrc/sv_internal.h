@@ -36,8 +36,8 @@ struct RowPart {
 struct SeqState {
     int32_t n;     // accepted drafts
     int32_t mode;  // 0: nothing to draw, 1: residual max(p_t - q', 0), 2: p_t alone
-    float m_t, m_d;
-    double k2;     // log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) log2e / T + k2 (+ log2 beta on the top-4)
+    float o_t, o_d;  // row offsets fp32(m c) of target row n and draft row n
+    double k2;       // log2 q'(v) - log2 p_t(v) = (z_d(v) - z_t(v)) c + k2 (+ log2 beta on the top-4)
     float inv_st;  // 1 / S_t: residual masses are summed relative to p_t * S_t
     float u_bonus;
     int32_t top[4];
@@ -72,7 +72,7 @@ struct Args {
     int64_t row_bytes;
     uint64_t seed;
     float beta;
-    double ln_beta, log2_beta;  // of beta, -inf for beta == 0
+    double log2_beta;       // log2(beta), -inf for beta == 0
     int32_t weighted;
     int32_t *accepted_len;
     int32_t *out_tokens;

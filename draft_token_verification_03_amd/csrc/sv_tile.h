@@ -57,20 +57,23 @@ __device__ __forceinline__ int elem_index(int q0, int u, int k, int vec)
     return (q0 + u * kBlock + (int)threadIdx.x) * vec + k;
 }
 
-// Running statistics of one sampling row: the wave-uniform maximum m and
-// this lane's fp64 sum of exp2((z - m) log2e / T).  Keeping m uniform across
-// the wave makes the rare rescale when m grows a uniform branch (a per-lane
-// maximum diverges on almost every tile and costs ~20% of the streaming rate
-// on gfx950).  Each vector's exponentials are added pairwise in fp32 and the
-// vector sum in fp64, so equal rows give bitwise-equal sums.
+// Running statistics of one sampling row: the wave-uniform maximum m, its
+// offset o = fp32(m c), and this lane's fp64 sum of exp2(z c - o).  Keeping m
+// uniform across the wave makes the rare rescale when m grows a uniform branch
+// (a per-lane maximum diverges on almost every tile and costs ~20% of the
+// streaming rate on gfx950), and the cross-lane maximum is only formed when
+// some lane's tile maximum exceeds m.  Each vector's exponentials are added
+// pairwise in fp32 and the vector sum in fp64, so equal rows give
+// bitwise-equal sums.
 struct RowRun {
-    float m;
+    float m, o;
     double s;
 };
 
 __device__ __forceinline__ void run_clear(RowRun &r)
 {
     r.m = -INFINITY;
+    r.o = -INFINITY;
     r.s = 0.0;
 }
 
@@ -92,23 +95,32 @@ __device__ __forceinline__ float tile_lane_max(const uint4 (&r)[U])
 __device__ __forceinline__ void run_raise(RowRun &run, float mw, const ExpScale &e)
 {
     if (mw > run.m) {
-        if (run.s != 0.0) run.s *= exp2(((double)run.m - (double)mw) * e.c64);
+        const float o = row_offset(mw, e);
+        if (run.s != 0.0) run.s *= exp2((double)run.o - (double)o);
         run.m = mw;
+        run.o = o;
     }
+}
+
+// Raise the running maximum to the wave's maximum of the lanes' tile maxima
+// `lm`, reducing across lanes only when some lane exceeds it (a uniform test).
+__device__ __forceinline__ void run_raise_lazy(RowRun &run, float lm, const ExpScale &e)
+{
+    if (__ballot(lm > run.m) != 0ull) run_raise(run, wave_max(lm), e);
 }
 
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_tile(const uint4 (&r)[U], const ExpScale &e, RowRun &run)
 {
     constexpr int VEC = Elt<DT>::kVec;
-    run_raise(run, wave_max(tile_lane_max<DT, U>(r)), e);
+    run_raise_lazy(run, tile_lane_max<DT, U>(r), e);
     if (run.m == -INFINITY) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float x[VEC], ev[VEC];
         Elt<DT>::unpack(r[u], x);
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.m, e);
+        for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.o, e);
 #pragma unroll
         for (int w = VEC / 2; w > 0; w >>= 1)
 #pragma unroll
@@ -145,7 +157,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
     constexpr int VEC = Elt<DT>::kVec;
     const int lane = threadIdx.x & 63;
     const float mx = tile_lane_max<DT, U>(r);
-    run_raise(run, wave_max(mx), e);
+    run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
     const float thr_v = W.v[3];
     const int thr_i = W.i[3];
@@ -156,7 +168,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
             float x[VEC], ev[VEC];
             Elt<DT>::unpack(r[u], x);
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.m, e);
+            for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.o, e);
 #pragma unroll
             for (int w = VEC / 2; w > 0; w >>= 1)
 #pragma unroll
@@ -178,7 +190,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
             const bool c = idx < V && better(x[k], idx, thr_v, thr_i);
             cmask |= (c ? 1u : 0u) << (u * VEC + k);
             ncand += c ? 1 : 0;
-            ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.m, e);
+            ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.o, e);
         }
 #pragma unroll
         for (int w = VEC / 2; w > 0; w >>= 1)
@@ -204,7 +216,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
                     int oi = idx;
                     top_insert_out(W, v, idx, ov, oi);  // on insertion (ov, oi) is the evicted entry
                     if (lane == 0 && oi != INT_MAX && ov != -INFINITY && have_m)
-                        lost += (double)exp_scaled(ov, run.m, e);
+                        lost += (double)exp_scaled(ov, run.o, e);
                 }
             }
         }
@@ -224,14 +236,14 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
                 float ov = x[k];
                 int oi = elem_index(q0, u, k, VEC);
                 top_insert_out(t, x[k], oi, ov, oi);
-                if (oi != INT_MAX && ov != -INFINITY && have_m) lost += (double)exp_scaled(ov, run.m, e);
+                if (oi != INT_MAX && ov != -INFINITY && have_m) lost += (double)exp_scaled(ov, run.o, e);
             }
         }
         const Top4 nw = wave_top4(t);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (t.i[k] != INT_MAX && t.v[k] != -INFINITY && !top_has(nw, t.i[k]) && have_m)
-                lost += (double)exp_scaled(t.v[k], run.m, e);
+                lost += (double)exp_scaled(t.v[k], run.o, e);
         W = nw;
     }
     run.s += lost;
@@ -269,7 +281,7 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
                                            double *lds_d, float &M, double &S)
 {
     M = block_max(run.m, lds_f);
-    const double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2(((double)run.m - (double)M) * e.c64);
+    const double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - (double)row_offset(M, e));
     S = block_sum(sc, lds_d);
 }
 
@@ -282,7 +294,8 @@ __device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &W,
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     M = block_max(run.m, lds_f);
-    double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2(((double)run.m - (double)M) * e.c64);
+    const double oM = (double)row_offset(M, e);
+    double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - oM);
     if (lane == 0) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -318,7 +331,7 @@ __device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &W,
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (W.i[k] != INT_MAX && W.v[k] != -INFINITY && !top_has(ct, W.i[k]))
-                sc += exp2(((double)W.v[k] - (double)M) * e.c64);
+                sc += exp_scaled64(W.v[k], oM, e.c64);
     }
     S_excl = block_sum(sc, lds_d);
 }

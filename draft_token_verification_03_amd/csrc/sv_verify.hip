@@ -316,7 +316,7 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
 // every thread; `publish` writes the sequence's outputs (all but the bonus
 // token of a sampling sequence) and its SeqState.
 template <int DT>
-__device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
+__device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K, nc = a.nc;
@@ -361,7 +361,7 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
 
     if (!fail) {
         const int nrows = greedy ? K + 1 : 2 * K + 1;
-        const double c64 = greedy ? 0.0 : kLog2e / (double)T;
+        const ExpScale e = make_scale(greedy ? 1.f : T);
         for (int r = wave; r < nrows; r += kWaves) {
             const RowPart *p = L.part + r * nc;
             if (greedy) {
@@ -377,7 +377,7 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
                 float M;
                 Top4 rt4;
                 double S_rest, S_top;
-                merge_weighted(p, L.ptop + i * nc, nc, c64, M, rt4, S_rest, S_top);
+                merge_weighted(p, L.ptop + i * nc, nc, e, M, rt4, S_rest, S_top);
                 if (lane == 0) {
                     L.m[r] = M;
                     L.S[r] = S_rest + (double)a.beta * S_top;
@@ -386,7 +386,7 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
             } else {
                 float M;
                 double S;
-                merge_sum(p, nc, c64, M, S);
+                merge_sum(p, nc, e, M, S);
                 if (lane == 0) {
                     L.m[r] = M;
                     L.S[r] = S;
@@ -406,8 +406,8 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
             const float u = philox_uniform(a.seed, gb, (uint32_t)i, kPurposeAccept);
             float pt, pd;
             const bool want_p = publish && (a.aux_pt != nullptr || a.aux_pd != nullptr);
-            L.acc[i] = decide(T, mt, L.S[i], md, L.S[K + 1 + i], in_top, a.ln_beta, x_ok && err == 0,
-                              zt, zd, u, want_p, pt, pd)
+            L.acc[i] = decide(e, row_offset(mt, e), L.S[i], row_offset(md, e), L.S[K + 1 + i], in_top,
+                              a.log2_beta, x_ok && err == 0, zt, zd, u, want_p, pt, pd)
                            ? 1
                            : 0;
             L.err[i] = err;
@@ -475,7 +475,8 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
                 }
                 st.n = n;
                 st.mode = n < K ? 1 : 2;
-                st.m_t = L.m[n];
+                const ExpScale e = make_scale(T);
+                st.o_t = row_offset(L.m[n], e);
                 st.inv_st = (float)(1.0 / L.S[n]);
                 st.T = T;
                 st.u_bonus = philox_uniform(a.seed, gb, (uint32_t)n, kPurposeBonus);
@@ -483,9 +484,8 @@ __device__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bo
                 for (int k = 0; k < 4; ++k) st.top[k] = -1;
                 st.lbeta = (float)a.log2_beta;
                 if (n < K) {
-                    st.m_d = L.m[K + 1 + n];
-                    st.k2 = ((double)L.m[n] - (double)L.m[K + 1 + n]) * (kLog2e / (double)T) +
-                            log2(L.S[n] / L.S[K + 1 + n]);
+                    st.o_d = row_offset(L.m[K + 1 + n], e);
+                    st.k2 = ((double)st.o_t - (double)st.o_d) + log2(L.S[n] / L.S[K + 1 + n]);
                     if (weighted) {
 #pragma unroll
                         for (int k = 0; k < 4; ++k)
@@ -536,7 +536,19 @@ __device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, const S
     if (MODE == 1) Elt<DT>::unpack(rd, xd);
 #pragma unroll
     for (int k = 0; k < VEC; ++k)
-        r[k] = residual_at<TOP, MODE>(xt[k], MODE == 1 ? xd[k] : 0.f, q * VEC + k, st, e, rs);
+        r[k] = residual_at<MODE>(xt[k], MODE == 1 ? xd[k] : 0.f, st, e, rs, rs.k_hi, rs.k_lo);
+    if (TOP && MODE == 1) {
+        // a vector holding one of the draft's top-4 tokens (at most four per
+        // row): recompute that token with its beta-weighted offset
+        if (q == rs.tq[0] || q == rs.tq[1] || q == rs.tq[2] || q == rs.tq[3]) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                const int v = q * VEC + k;
+                if (v == st.top[0] || v == st.top[1] || v == st.top[2] || v == st.top[3])
+                    r[k] = residual_at<MODE>(xt[k], xd[k], st, e, rs, rs.kt_hi, rs.kt_lo);
+            }
+        }
+    }
     float s[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) s[k] = r[k];
@@ -550,69 +562,106 @@ __device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, const S
 // Residual mass of the slots [s_begin, s_end) of the row pair into slot[].
 // Slot s covers the vectors [s*gs*kSlotVec, (s+1)*gs*kSlotVec); the NW waves
 // of the workgroup take the slots in turn, and a wave's 64 lanes read
-// kSlotVec consecutive vectors (1 KiB of each row) per load, kResLoads units in
-// flight per lane.  Each slot is summed by one wave in a fixed order (fp32
-// within a vector, fp64 across vectors and lanes).
-template <int DT, bool TOP, int NW, int MODE>
-__device__ void residual_slots(const char *trow, const char *drow, int V, int nvec, int s_begin,
-                               int s_end, int gs, const SeqState &st, const ExpScale &e,
-                               const ResidualScale &rs, double *slot)
+// kSlotVec consecutive vectors (1 KiB of each row) per load.  Item f = t*gs +
+// j of a wave is unit j of its t-th slot, kResLoads items per batch (a second
+// batch in flight measured slower: it costs occupancy).  FAST (aligned rows
+// of whole vectors) loads without any
+// branch (indices clamped into the row; items that are not live add
+// nothing), so that no loaded register passes a branch join, which would
+// make it wait for its load.  Each slot is summed by one wave in a fixed
+// order (fp32 within a vector, fp64 across vectors and lanes).
+template <int DT, int MODE>
+struct ResBatch {
+    uint4 rt[kResLoads], rd[kResLoads];
+    int q[kResLoads], t[kResLoads];
+    bool end[kResLoads], live[kResLoads];
+};
+
+template <int DT, int NW, int MODE, bool FAST>
+__device__ __forceinline__ void residual_issue(ResBatch<DT, MODE> &B, const char *trow, const char *drow,
+                                               bool ta, bool da, int V, int nvec, int s_begin, int gs,
+                                               int items, int f0, int &t, int &j)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < kResLoads; ++u) {
+        const int s = s_begin + wave + NW * t;
+        B.q[u] = (s * gs + j) * kSlotVec + lane;
+        B.t[u] = t;
+        B.end[u] = j == gs - 1;
+        B.live[u] = f0 + u < items && B.q[u] < nvec;
+        if (++j == gs) {
+            j = 0;
+            ++t;
+        }
+    }
+    if (FAST) {
+        // the re-read streams too: nontemporal loads
+#pragma unroll
+        for (int u = 0; u < kResLoads; ++u) B.rt[u] = load16_stream(trow + (size_t)min(B.q[u], nvec - 1) * 16);
+        if (MODE == 1) {
+#pragma unroll
+            for (int u = 0; u < kResLoads; ++u)
+                B.rd[u] = load16_stream(drow + (size_t)min(B.q[u], nvec - 1) * 16);
+        }
+    } else {
+        load_units<DT, kResLoads>(trow, ta, B.q, B.live, nvec, V, B.rt);
+        if (MODE == 1) load_units<DT, kResLoads>(drow, da, B.q, B.live, nvec, V, B.rd);
+    }
+}
+
+template <int DT, bool TOP, int NW, int MODE>
+__device__ __forceinline__ void residual_consume(const ResBatch<DT, MODE> &B, int items, int f0, int s_begin,
+                                                 const SeqState &st, const ExpScale &e,
+                                                 const ResidualScale &rs, double &acc, double *slot)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < kResLoads; ++u) {
+        if (f0 + u >= items) break;
+        float r[Elt<DT>::kVec];
+        const float sum = residual_vec<DT, TOP, MODE>(B.rt[u], B.rd[u], B.q[u], st, e, rs, r);
+        acc += B.live[u] ? (double)sum : 0.0;
+        if (B.end[u]) {
+            const double tot = wave_sum(acc);
+            if (lane == 0) slot[s_begin + wave + NW * B.t[u]] = tot;
+            acc = 0.0;
+        }
+    }
+}
+
+template <int DT, bool TOP, int NW, int MODE, bool FAST>
+__device__ __forceinline__ void residual_slots_impl(const char *trow, const char *drow, int V, int nvec,
+                                                    int s_begin, int s_end, int gs, const SeqState &st,
+                                                    const ExpScale &e, const ResidualScale &rs,
+                                                    double *slot)
+{
+    const int wave = threadIdx.x >> 6;
     const bool ta = ((uintptr_t)trow & 15) == 0, da = ((uintptr_t)drow & 15) == 0;
     const int ns = s_end - s_begin;
     const int my_slots = ns > wave ? (ns - wave + NW - 1) / NW : 0;
     const int items = my_slots * gs;
-    const bool fast = ta && (MODE == 2 || da) && V % Elt<DT>::kVec == 0;
+    if (items == 0) return;
     double acc = 0.0;
-    // item f = t * gs + j is unit j of the wave's t-th slot, s_begin + wave + NW * t
     int t = 0, j = 0;
     for (int f0 = 0; f0 < items; f0 += kResLoads) {
-        uint4 rt[kResLoads], rd[kResLoads];
-        int qv[kResLoads], tv[kResLoads];
-        bool endv[kResLoads], live[kResLoads];
-#pragma unroll
-        for (int u = 0; u < kResLoads; ++u) {
-            const int s = s_begin + wave + NW * t;
-            const int q = (s * gs + j) * kSlotVec + lane;
-            qv[u] = q;
-            tv[u] = t;
-            endv[u] = j == gs - 1;
-            live[u] = f0 + u < items && q < nvec;
-            if (++j == gs) {
-                j = 0;
-                ++t;
-            }
-        }
-        if (fast) {
-            // aligned rows of whole vectors: unconditional loads (indices
-            // clamped into the row) with no mask to wait on; a unit that is
-            // not live adds nothing below
-#pragma unroll
-            for (int u = 0; u < kResLoads; ++u)
-                rt[u] = *reinterpret_cast<const uint4 *>(trow + (size_t)min(qv[u], nvec - 1) * 16);
-            if (MODE == 1) {
-#pragma unroll
-                for (int u = 0; u < kResLoads; ++u)
-                    rd[u] = *reinterpret_cast<const uint4 *>(drow + (size_t)min(qv[u], nvec - 1) * 16);
-            }
-        } else {
-            load_units<DT, kResLoads>(trow, ta, qv, live, nvec, V, rt);
-            if (MODE == 1) load_units<DT, kResLoads>(drow, da, qv, live, nvec, V, rd);
-        }
-#pragma unroll
-        for (int u = 0; u < kResLoads; ++u) {
-            if (f0 + u >= items) break;
-            float r[Elt<DT>::kVec];
-            const float sum = residual_vec<DT, TOP, MODE>(rt[u], rd[u], qv[u], st, e, rs, r);
-            acc += live[u] ? (double)sum : 0.0;
-            if (endv[u]) {
-                const double tot = wave_sum(acc);
-                if (lane == 0) slot[s_begin + wave + NW * tv[u]] = tot;
-                acc = 0.0;
-            }
-        }
+        ResBatch<DT, MODE> A;
+        residual_issue<DT, NW, MODE, FAST>(A, trow, drow, ta, da, V, nvec, s_begin, gs, items, f0, t, j);
+        residual_consume<DT, TOP, NW, MODE>(A, items, f0, s_begin, st, e, rs, acc, slot);
     }
+}
+
+template <int DT, bool TOP, int NW, int MODE>
+__device__ __forceinline__ void residual_slots(const char *trow, const char *drow, int V, int nvec,
+                                               int s_begin, int s_end, int gs, const SeqState &st,
+                                               const ExpScale &e, const ResidualScale &rs, double *slot)
+{
+    const bool fast = ((uintptr_t)trow & 15) == 0 && (MODE == 2 || ((uintptr_t)drow & 15) == 0) &&
+                      V % Elt<DT>::kVec == 0;
+    if (fast)
+        residual_slots_impl<DT, TOP, NW, MODE, true>(trow, drow, V, nvec, s_begin, s_end, gs, st, e, rs, slot);
+    else
+        residual_slots_impl<DT, TOP, NW, MODE, false>(trow, drow, V, nvec, s_begin, s_end, gs, st, e, rs, slot);
 }
 
 // One workgroup per (sequence, group of a.spg slots): the accept scan, then
@@ -628,7 +677,7 @@ __global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
     const SeqState st = accept_sequence<DT>(a, b, L, g == 0);
     if (st.mode == 0) return;
     const ExpScale e = make_scale(st.T);
-    const ResidualScale rs = make_residual_scale(st, e);
+    const ResidualScale rs = make_residual_scale<Elt<DT>::kVec>(st, e);
     const char *trow = target_row(a, b, st.n);
     const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
     const int s0 = g * a.spg, s1 = min(a.nslot, s0 + a.spg);
@@ -650,7 +699,7 @@ __global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
 // that element, or INT_MAX when rounding leaves `thr` above the range; `last`
 // receives the last element of the range with positive mass.
 template <int DT, bool TOP, int MODE>
-__device__ int scan_range(const char *trow, const char *drow, int V, int nvec, int q0, int q1,
+__device__ __forceinline__ int scan_range(const char *trow, const char *drow, int V, int nvec, int q0, int q1,
                           double base, double thr, const SeqState &st, const ExpScale &e,
                           const ResidualScale &rs, int &last, double *lds_d, int *lds_i)
 {
@@ -692,7 +741,7 @@ __device__ int scan_range(const char *trow, const char *drow, int V, int nvec, i
 // Inverse CDF over the slot masses in slot[0..nslot): returns the token (-1
 // when the mass is 0) and Z, the total mass.
 template <int DT, bool TOP, int MODE>
-__device__ int draw_token(const char *trow, const char *drow, int V, int nvec, int nslot, int gs,
+__device__ __forceinline__ int draw_token(const char *trow, const char *drow, int V, int nvec, int nslot, int gs,
                           float u, const SeqState &st, const ExpScale &e, const ResidualScale &rs,
                           const double *slot, double &Z, double *lds_d, int *lds_i)
 {
@@ -752,7 +801,7 @@ __global__ __launch_bounds__(kBlock) void bonus_kernel(const Args a)
     __syncthreads();
     if (st.mode == 0) return;
     const ExpScale e = make_scale(st.T);
-    const ResidualScale rs = make_residual_scale(st, e);
+    const ResidualScale rs = make_residual_scale<Elt<DT>::kVec>(st, e);
     const char *trow = target_row(a, b, st.n);
     const char *drow = st.mode == 1 ? draft_row(a, b, st.n) : trow;
     double Z;
@@ -799,12 +848,14 @@ __global__ __launch_bounds__(64) void rowstats_finish_kernel(const Args a)
             a.rs_argmax[r] = I;
         }
     } else {
+        const ExpScale e = make_scale(T);
         float M;
         double S;
-        merge_sum(p, a.nc, kLog2e / (double)T, M, S);
+        merge_sum(p, a.nc, e, M, S);
         if (lane == 0) {
+            // S is relative to fp32(M c); the log-sum is relative to M c
             a.rs_max[r] = M;
-            a.rs_logsum[r] = log(S);
+            a.rs_logsum[r] = log(S) + ((double)row_offset(M, e) - (double)M * e.c64) * 0.6931471805599453;
             a.rs_argmax[r] = -1;
         }
     }
