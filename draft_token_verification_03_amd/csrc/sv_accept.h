@@ -57,48 +57,54 @@ __device__ __forceinline__ void merge_argmax(const RowPart *p, int nc, float &M,
     I = i;
 }
 
+// The normaliser D = S_rest + beta * S_top of a beta-weighted draft row from
+// the mass outside its top-4 and the top-4 itself, relative to the offset om.
+__device__ __forceinline__ double weighted_norm(double S_rest, const Top4 &t, double om, double c64,
+                                                double beta)
+{
+    double st = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (t.i[k] != INT_MAX && t.v[k] != -INFINITY) st += exp_scaled64(t.v[k], om, c64);
+    return S_rest + beta * st;
+}
+
 // A beta-weighted draft row.  Partials carry, per chunk, the chunk's top-4 and
 // the sum over the chunk's other elements, so the mass outside the row's top-4
 // is summed directly (never as S - S_top, which cancels when the top-4 hold
-// nearly all the mass).  Returns the row max M, the row top-4, the mass
-// outside it (S_rest) and inside it (S_top), all relative to exp2((z - M) c).
+// nearly all the mass).  A row of one chunk already carries D (the streaming
+// pass forms it).  Returns the row max M, the row top-4 and D, relative to
+// exp2((z - M) c).
 __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp, int nc,
-                                               const ExpScale &e, float &M, Top4 &row_top,
-                                               double &S_rest, double &S_top)
+                                               const ExpScale &e, double beta, float &M, Top4 &row_top,
+                                               double &D)
 {
     const int lane = threadIdx.x & 63;
     double s_excl;
     merge_sum(p, nc, e, M, s_excl);
-    const double om = (double)row_offset(M, e);
-    if (nc == 1) {  // the chunk's top-4 is the row's; nothing else to move
+    if (nc == 1) {
         row_top = tp[0];
-        S_rest = s_excl;
-    } else {
-        Top4 t;
-        top_clear(t);
-        for (int c = lane; c < nc; c += 64) {
-            const Top4 r = tp[c];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) top_insert(t, r.v[k], r.i[k]);
-        }
-        row_top = wave_top4(t);
-        double extra = 0.0;
-        for (int c = lane; c < nc; c += 64) {
-            const Top4 r = tp[c];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
-                    extra += exp_scaled64(r.v[k], om, e.c64);
-        }
-        S_rest = s_excl + wave_sum(extra);
+        D = s_excl;
+        return;
     }
-    // lane k < 4 adds the k-th entry of the row top-4
-    double st = 0.0;
+    const double om = (double)row_offset(M, e);
+    Top4 t;
+    top_clear(t);
+    for (int c = lane; c < nc; c += 64) {
+        const Top4 r = tp[c];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (lane == k && row_top.i[k] != INT_MAX && row_top.v[k] != -INFINITY)
-            st = exp_scaled64(row_top.v[k], om, e.c64);
-    S_top = wave_sum(st);
+        for (int k = 0; k < 4; ++k) top_insert(t, r.v[k], r.i[k]);
+    }
+    row_top = wave_top4(t);
+    double extra = 0.0;
+    for (int c = lane; c < nc; c += 64) {
+        const Top4 r = tp[c];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
+                extra += exp_scaled64(r.v[k], om, e.c64);
+    }
+    D = weighted_norm(s_excl + wave_sum(extra), row_top, om, e.c64, beta);
 }
 
 // ---------------------------------------------------------------------------
@@ -111,14 +117,15 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
 // o_t, D the draft row's normaliser relative to o_d (S_d unweighted, or
 // S_rest + beta * S_top for the Saguaro-style draft, "Speculative Speculative
 // Decoding", "Method"), and w(x) = beta on the draft's top-4, 1 elsewhere
-// (log2_beta from the host).  Only the final exponential is fp32: rounding
+// (log2_beta from the host), and lq = log2(D / S_t) from the caller.  Only the
+// final exponential is fp32: rounding
 // log2 r to fp32 moves r by at most r |ln r| 2^-24 <= 2.2e-8 where r <= 1,
 // below the uniforms' 2^-24 grid.  A token the draft law gives no mass is
 // accepted (the ratio is +inf).  The diagnostics p(x), q'(x) are only formed
 // when asked for.
 __device__ __forceinline__ bool decide(const ExpScale &e, float ot, double St, float od, double D,
-                                       bool weighted_top, double log2_beta, bool x_ok, float zt,
-                                       float zd, float u, bool want_p, float &pt, float &pd)
+                                       double lq, bool weighted_top, double log2_beta, bool x_ok,
+                                       float zt, float zd, float u, bool want_p, float &pt, float &pd)
 {
     pt = NAN;
     pd = NAN;
@@ -126,7 +133,7 @@ __device__ __forceinline__ bool decide(const ExpScale &e, float ot, double St, f
     const double lt = (double)zt * e.c64 - (double)ot;  // log2(p(x) S_t), zt c exact
     const double ld = (double)zd * e.c64 - (double)od;  // log2(q(x) D / w(x))
     const bool no_draft_mass = zd == -INFINITY || (weighted_top && log2_beta == -INFINITY);
-    double lr = lt - ld + log2(D / St);
+    double lr = lt - ld + lq;
     if (weighted_top) lr -= log2_beta;
     const bool accept = no_draft_mass || (double)u <= (double)__builtin_amdgcn_exp2f((float)lr);
     if (want_p) {

@@ -30,6 +30,10 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     // kernel's LDS staging
     const int64_t rows = (int64_t)p->sB * p->R;
     int64_t nc = (kFillBlocks + rows - 1) / rows;
+    // long rows in a batch that fills the grid by itself: two chunks a row
+    // halve the size of the grid's workgroups, so its last round leaves less
+    // of the chip idle
+    if (nc == 1 && p->row_bytes >= kSplitRowBytes) nc = 2;
     const int64_t nc_max = std::max<int64_t>(1, p->nvec / kBlock);
     const int64_t nc_stage =
         kStageBytes / ((int64_t)sizeof(RowPart) * p->R + (int64_t)sizeof(Top4) * K);

@@ -15,6 +15,7 @@ constexpr int kMaxK = 128;               // drafted positions per sequence
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kMaxChunks = 1024;         // streaming chunks per row
 constexpr int kFillBlocks = 2048;        // workgroups the streaming grid aims for
+constexpr int64_t kSplitRowBytes = 256 * 1024;  // rows this long take at least two chunks
 constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
 constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials
 constexpr int kResFill = 1024;           // workgroups the residual grid aims for (one round)
@@ -22,12 +23,14 @@ constexpr int kResLoads = 4;             // residual units in flight per lane (p
 constexpr int kSlotVec = 64;             // 16-byte vectors per residual slot unit (one per lane)
 constexpr int kSlotUnits = 4;            // units per slot when the batch alone fills the grid
 constexpr int kMaxResSlots = 4096;       // residual slots per row (coarser slots beyond)
+constexpr int kThreadMerge = 4;          // chunks per row the accept scan merges per thread
 constexpr uint32_t kPurposeAccept = 0u, kPurposeBonus = 1u;
 
 // One (row, chunk) partial of the streaming pass.
 struct RowPart {
     float m;      // chunk maximum
-    int32_t idx;  // lowest index attaining m (greedy rows)
+    int32_t idx;  // lowest index attaining m (greedy rows); in chunk 0 of a sampling
+                  // row i < K, the bits of the fp32 logit at drafted token x_i
     double s;     // sum of exp2((z - m) * log2e / T) over the chunk; for a beta-weighted
                   // draft row, over the chunk's elements outside the chunk's top-4
 };

@@ -129,15 +129,64 @@ __device__ __forceinline__ void run_sum_tile(const uint4 (&r)[U], const ExpScale
     }
 }
 
-// Beta-weighted draft row: as run_sum_tile, and the wave keeps the top-4 W of
-// the elements it has seen, by (value desc, index asc), identical in every
-// lane; the lanes' sums cover the wave's elements outside W.  W's 4th entry
-// is a threshold no later element reaches in most tiles (after t tiles a new
-// tile holds a candidate with probability ~4/t), so most tiles take the plain
-// sum.  A tile with a few candidates inserts them one at a time, in a
-// wave-uniform loop; the first tile, or one with many candidates (rising
-// rows), merges per-lane lists instead.  Whatever drops out of W, or never
-// enters it, joins lane 0's sum.
+// Beta-weighted draft row: as run_sum_tile, and the workgroup keeps the
+// chunk's top-4 so far, by (value desc, index asc), in four LDS slots of
+// 64-bit keys that every wave reads and updates.  A key orders like its
+// (value, index) pair, so the slots take new entries with atomic maxima: an
+// insert walks down the slots, and at each one the larger key stays and the
+// smaller moves on, which keeps the slots plus the keys that fall off the end
+// equal to everything inserted, and the slots the four best, under any
+// interleaving of the waves.  The lanes' sums cover every element that
+// never enters the slots or falls out of them.  The 4th slot is a floor no
+// later element reaches in most tiles (one shared list sees four waves'
+// elements, so after t tiles a wave's next tile holds a new entry with
+// probability ~1/t), so most tiles take the plain sum.  A tile with a few
+// candidates has each inserted by its own lane; the first tile, or one with
+// many candidates (rising rows), reduces per-lane lists to the wave's top-4
+// first and inserts those four.
+
+// Key of (v, i), i in [0, INT_MAX): larger keys are better entries; -0 counts
+// as +0, as in `better`.  Key 0 is an empty slot.
+__device__ __forceinline__ uint64_t top_key(float v, int i)
+{
+    uint32_t b = __float_as_uint(v + 0.0f);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)(0x7fffffff - i);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k)
+{
+    if (k == 0) return -INFINITY;
+    uint32_t b = (uint32_t)(k >> 32);
+    b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
+    return __uint_as_float(b);
+}
+
+__device__ __forceinline__ int key_index(uint64_t k)
+{
+    return k == 0 ? INT_MAX : 0x7fffffff - (int)(uint32_t)k;
+}
+
+// Insert key k into the slots; returns the key that falls out (k itself if it
+// does not enter, 0 if it took an empty slot).
+__device__ __forceinline__ uint64_t slots_insert(uint64_t *slots, uint64_t k)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t old = atomicMax((unsigned long long *)&slots[j], (unsigned long long)k);
+        k = old < k ? old : k;
+    }
+    return k;
+}
+
+// The 4th slot as (value, index); a stale read is a lower bound of the
+// current one, as slots only rise.
+__device__ __forceinline__ void slots_floor(const uint64_t *slots, float &fv, int &fi)
+{
+    const uint64_t k = __hip_atomic_load(&slots[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    fv = key_value(k);
+    fi = key_index(k);
+}
 
 __device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &out_v, int &out_i)
 {
@@ -152,16 +201,19 @@ constexpr int kSerialCandidates = 16;
 
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
-                                                 const ExpScale &e, RowRun &run, Top4 &W)
+                                                 const ExpScale &e, RowRun &run, uint64_t *slots)
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int lane = threadIdx.x & 63;
+    float fv;
+    int fi;
+    slots_floor(slots, fv, fi);
     const float mx = tile_lane_max<DT, U>(r);
     run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
-    const float thr_v = W.v[3];
-    const int thr_i = W.i[3];
-    if (__ballot(mx >= thr_v) == 0ull) {  // no element can enter W
+    // the lane's first token of the tile is its lowest
+    const bool maybe = mx > fv || (mx == fv && elem_index(q0, 0, 0, VEC) < fi);
+    if (__ballot(maybe) == 0ull) {  // no element can enter the slots
         if (!have_m) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -177,7 +229,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
         }
         return;
     }
-    // candidates: elements that beat W's 4th entry; the others join the sum
+    // candidates: elements that beat the floor; the others join the sum
     uint32_t cmask = 0;  // bit u * VEC + k
     int ncand = 0;
 #pragma unroll
@@ -187,7 +239,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int idx = elem_index(q0, u, k, VEC);
-            const bool c = idx < V && better(x[k], idx, thr_v, thr_i);
+            const bool c = idx < V && better(x[k], idx, fv, fi);
             cmask |= (c ? 1u : 0u) << (u * VEC + k);
             ncand += c ? 1 : 0;
             ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.o, e);
@@ -198,34 +250,28 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
             for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
         run.s += (double)ev[0];
     }
-    double lost = 0.0;  // mass of candidates that end outside W
-    if (W.i[3] != INT_MAX && wave_sum_int(ncand) <= kSerialCandidates) {
+    // keys that fall out of the slots, by the lane that inserted them; each
+    // is at most the element inserted, so at most the wave's maximum
+    double lost = 0.0;
+    if (wave_sum_int(ncand) <= kSerialCandidates) {
+        if (cmask != 0u) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[VEC];
-            Elt<DT>::unpack(r[u], x);
+            for (int u = 0; u < U; ++u) {
+                float x[VEC];
+                Elt<DT>::unpack(r[u], x);
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                uint64_t bits = __ballot((cmask >> (u * VEC + k)) & 1u);
-                while (bits) {
-                    const int src = __ffsll((unsigned long long)bits) - 1;
-                    bits &= bits - 1;
-                    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), src));
-                    const int idx = __builtin_amdgcn_readlane(elem_index(q0, u, k, VEC), src);
-                    float ov = v;
-                    int oi = idx;
-                    top_insert_out(W, v, idx, ov, oi);  // on insertion (ov, oi) is the evicted entry
-                    if (lane == 0 && oi != INT_MAX && ov != -INFINITY && have_m)
-                        lost += (double)exp_scaled(ov, run.o, e);
+                for (int k = 0; k < VEC; ++k) {
+                    if (!((cmask >> (u * VEC + k)) & 1u)) continue;
+                    const uint64_t out = slots_insert(slots, top_key(x[k], elem_index(q0, u, k, VEC)));
+                    if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
                 }
             }
         }
     } else {
-        // per-lane lists of the candidates (lane 0 also holds W), then the
-        // wave's top-4 of all of them
+        // per-lane lists of the candidates, the wave's top-4 of them, and
+        // lanes 0..3 insert its entries
         Top4 t;
         top_clear(t);
-        if (lane == 0) t = W;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float x[VEC];
@@ -236,15 +282,20 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
                 float ov = x[k];
                 int oi = elem_index(q0, u, k, VEC);
                 top_insert_out(t, x[k], oi, ov, oi);
-                if (oi != INT_MAX && ov != -INFINITY && have_m) lost += (double)exp_scaled(ov, run.o, e);
+                if (oi != INT_MAX && have_m) lost += (double)exp_scaled(ov, run.o, e);
             }
         }
         const Top4 nw = wave_top4(t);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (t.i[k] != INT_MAX && t.v[k] != -INFINITY && !top_has(nw, t.i[k]) && have_m)
+            if (t.i[k] != INT_MAX && !top_has(nw, t.i[k]) && have_m)
                 lost += (double)exp_scaled(t.v[k], run.o, e);
-        W = nw;
+        const float v = lane == 0 ? nw.v[0] : lane == 1 ? nw.v[1] : lane == 2 ? nw.v[2] : nw.v[3];
+        const int i = lane == 0 ? nw.i[0] : lane == 1 ? nw.i[1] : lane == 2 ? nw.i[2] : nw.i[3];
+        if (lane < 4 && i != INT_MAX) {
+            const uint64_t out = slots_insert(slots, top_key(v, i));
+            if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
+        }
     }
     run.s += lost;
 }
@@ -285,54 +336,20 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
     S = block_sum(sc, lds_d);
 }
 
-// Weighted draft row chunk: block max M, the chunk's top-4 and the mass
-// outside it (entries of the waves' top-4 lists that miss the chunk top-4
-// join the sum).
-__device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &W, const ExpScale &e,
-                                               float *lds_f, int *lds_i, double *lds_d, float &M,
-                                               double &S_excl, Top4 &ct)
+// Weighted draft row chunk: block max M, the chunk's top-4 (the slots, once
+// every wave has finished) and the mass outside it.
+__device__ __forceinline__ void run_finish_top(const RowRun &run, const uint64_t *slots, const ExpScale &e,
+                                               float *lds_f, double *lds_d, float &M, double &S_excl,
+                                               Top4 &ct)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    M = block_max(run.m, lds_f);
-    const double oM = (double)row_offset(M, e);
-    double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - oM);
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            lds_f[4 + wave * 4 + k] = W.v[k];
-            lds_i[4 + wave * 4 + k] = W.i[k];
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        Top4 c;
-        top_clear(c);
-        if (lane < kWaves * 4) {
-            c.v[0] = lds_f[4 + lane];
-            c.i[0] = lds_i[4 + lane];
-        }
-        const Top4 r = wave_top4(c);
-        if (lane == 0) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                lds_f[k] = r.v[k];
-                lds_i[k] = r.i[k];
-            }
-        }
-    }
-    __syncthreads();
+    M = block_max(run.m, lds_f);  // its barrier also orders every insert before the reads
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        ct.v[k] = lds_f[k];
-        ct.i[k] = lds_i[k];
+        const uint64_t key = slots[k];
+        ct.v[k] = key_value(key);
+        ct.i[k] = key_index(key);
     }
-    __syncthreads();
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (W.i[k] != INT_MAX && W.v[k] != -INFINITY && !top_has(ct, W.i[k]))
-                sc += exp_scaled64(W.v[k], oM, e.c64);
-    }
+    const double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - (double)row_offset(M, e));
     S_excl = block_sum(sc, lds_d);
 }
 

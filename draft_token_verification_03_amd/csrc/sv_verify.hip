@@ -168,7 +168,7 @@ __device__ __forceinline__ const char *draft_row(const Args &a, int b, int i)
 // reductions of sv_tile.h: a wave-uniform running max with per-lane fp64
 // sums, lanes visiting their elements in increasing index order (so argmax
 // and top-4 ties resolve to the lowest token id), and for a weighted draft row
-// the wave's top-4 kept out of the sum.  The first tile is requested before
+// the workgroup's top-4 kept out of the sum.  The first tile is requested before
 // the sequence's temperature is known, so the row stream starts one memory
 // round trip earlier; a draft row of a greedy sequence (whose draft logits
 // were passed anyway) wastes that one tile.  Rows a sequence does not use
@@ -188,6 +188,13 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
     const int q1 = min(a.nvec, q0 + a.cvec);
     uint4 r[kLoads];
     issue_tile<DT, ALIGNED>(row, q0, q1, a.V, r);
+    // a sampling row's logit at its drafted token, read while the first tile
+    // is in flight, saves the accept step a dependent gather
+    float zx = 0.f;
+    if (chunk == 0 && i < a.K && threadIdx.x == 0) {
+        const int x = a.tokens[(int64_t)b * a.K + i];
+        if (x >= 0 && x < a.V) zx = Elt<DT>::scalar(row, x);
+    }
 
     const bool greedy = T == 0.f;
     if (!temperature_ok(T) || (is_draft && greedy)) return;
@@ -208,20 +215,23 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
         const ExpScale e = make_scale(T);
         RowRun run;
         run_clear(run);
-        Top4 t4;
-        top_clear(t4);
         if (track_top) {
+            __shared__ uint64_t slots[4];  // the chunk's top-4 keys, empty at first
+            if (threadIdx.x < 4) slots[threadIdx.x] = 0;
+            __syncthreads();
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
-                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, t4);
+                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, slots);
             });
-            run_finish_top(run, t4, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
+            run_finish_top(run, slots, e, lds_f, lds_d, part.m, part.s, ct);
+            if (a.nc == 1 && threadIdx.x == 0)  // a whole row: its normaliser D
+                part.s = weighted_norm(part.s, ct, (double)row_offset(part.m, e), e.c64, (double)a.beta);
         } else {
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
                 run_sum_tile<DT, kLoads>(t, e, run);
             });
             run_finish(run, e, lds_f, lds_d, part.m, part.s);
         }
-        part.idx = -1;
+        part.idx = __float_as_int(zx);
     }
     if (threadIdx.x == 0) {
         a.part[(int64_t)slot_row * a.nc + chunk] = part;
@@ -250,19 +260,24 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
 // Shallow Sub-Networks", "3. Lossless Speculative Verification"; greedy:
 // "LayerSkip Guide: Early Exit & Self-Speculative Decoding", "2. The Drafting
 // and Single-Pass Verification Pipeline"), run by every residual workgroup
-// of the sequence (all reach the same outcome; the first writes it).  The
-// LDS it uses is laid out by accept_lds(), sized from (R, K, nc) so that a
-// workgroup holds only what its sequence needs.
+// of the sequence (all reach the same outcome; the first writes it).  Thread
+// i stands for position i <= K: it takes the statistics of target row i and
+// draft row i, makes the accept test of drafted token x_i, and prepares the
+// state of the bonus draw as if the scan stopped at i.  The first position
+// that stops it (a rejection, an unusable row, or position K) is n; thread n
+// publishes.  With a few chunks per row each thread loads and merges its own
+// rows' partials; with more, the partials are staged in LDS and merged one row
+// per wave first.  The LDS is laid out by accept_lds_layout(), sized from
+// (R, K, nc).
 
 struct AcceptLds {
-    RowPart *part;  // [R][nc] staged partials
+    RowPart *part;  // [R][nc] staged partials (staged merges only)
     Top4 *ptop;     // [K][nc] staged chunk top-4 lists (weighted draft rows)
     double *S;      // [R] S_t, or the draft normaliser D
     float *m;       // [R]
     int *idx;       // [R]
     Top4 *top;      // [K] row top-4 of each weighted draft row
-    int *x, *acc, *err;
-    float *pt, *pd;
+    int *flag;      // [K + 1] 1: position stops the scan, 3: and its rows are unusable
     SeqState *st;
 };
 
@@ -280,17 +295,14 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
         return base ? base + o : nullptr;
     };
     static_assert(sizeof(RowPart) == 16 && sizeof(Top4) == 32, "16-byte staging granules");
-    unsigned char *p_part = take(sizeof(RowPart) * (size_t)R * nc);  // ends on a granule:
-    unsigned char *p_ptop = take(weighted ? sizeof(Top4) * (size_t)K * nc : 0);  // contiguous
-    unsigned char *p_S = take(sizeof(double) * (size_t)R);
-    unsigned char *p_m = take(sizeof(float) * (size_t)R);
-    unsigned char *p_idx = take(sizeof(int) * (size_t)R);
-    unsigned char *p_top = take(sizeof(Top4) * (size_t)K);
-    unsigned char *p_x = take(sizeof(int) * (size_t)K);
-    unsigned char *p_acc = take(sizeof(int) * (size_t)K);
-    unsigned char *p_err = take(sizeof(int) * (size_t)K);
-    unsigned char *p_pt = take(sizeof(float) * (size_t)K);
-    unsigned char *p_pd = take(sizeof(float) * (size_t)K);
+    const bool staged = nc > kThreadMerge;
+    unsigned char *p_part = take(staged ? sizeof(RowPart) * (size_t)R * nc : 0);  // ends on a granule:
+    unsigned char *p_ptop = take(staged && weighted ? sizeof(Top4) * (size_t)K * nc : 0);  // contiguous
+    unsigned char *p_S = take(staged ? sizeof(double) * (size_t)R : 0);
+    unsigned char *p_m = take(staged ? sizeof(float) * (size_t)R : 0);
+    unsigned char *p_idx = take(staged ? sizeof(int) * (size_t)R : 0);
+    unsigned char *p_top = take(staged && weighted ? sizeof(Top4) * (size_t)K : 0);
+    unsigned char *p_flag = take(sizeof(int) * (size_t)(K + 1));
     unsigned char *p_st = take(sizeof(SeqState));
     if (L) {
         L->part = reinterpret_cast<RowPart *>(p_part);
@@ -299,33 +311,31 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
         L->m = reinterpret_cast<float *>(p_m);
         L->idx = reinterpret_cast<int *>(p_idx);
         L->top = reinterpret_cast<Top4 *>(p_top);
-        L->x = reinterpret_cast<int *>(p_x);
-        L->acc = reinterpret_cast<int *>(p_acc);
-        L->err = reinterpret_cast<int *>(p_err);
-        L->pt = reinterpret_cast<float *>(p_pt);
-        L->pd = reinterpret_cast<float *>(p_pd);
+        L->flag = reinterpret_cast<int *>(p_flag);
         L->st = reinterpret_cast<SeqState *>(p_st);
     }
     return off;
 }
 
-// Round trip 1: the temperature, the drafted tokens, and the partials and
-// top-4 lists of all 2K + 1 rows into LDS in 16-byte granules (greedy
-// sequences use the first K + 1 rows).  Round trip 2 gathers the drafted
-// tokens' logits while the partials are merged.  Returns the outcome to
-// every thread; `publish` writes the sequence's outputs (all but the bonus
-// token of a sampling sequence) and its SeqState.
+// Statistics of the rows of one position: target row i, and for i < K draft
+// row i (max, sum S_t or normaliser D, its top-4 when weighted) and the
+// logits at the drafted token, which chunk 0's partials carry.
+struct PosRows {
+    float mt, md, zt, zd;
+    double St, D;
+    int am;  // target argmax (greedy)
+    Top4 top;
+};
+
+// Staged merges: the partials and top-4 lists of all 2K + 1 rows in LDS (16-byte
+// granules; greedy sequences use the first K + 1 rows) and merge one row per
+// wave.
 template <int DT>
-__device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
+__device__ __forceinline__ void merge_rows(const Args &a, int b, float T, bool greedy, bool weighted,
+                                           const AcceptLds &L)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K, nc = a.nc;
-    const uint32_t gb = (uint32_t)(a.b0 + b);  // Philox keys on the sequence's index in the call
-    int32_t *out = a.out_tokens + (int64_t)b * (K + 1);
-
-    const float T = a.temperature[b];
-    int x = -1;
-    if (tid < K) x = a.tokens[(int64_t)b * K + tid];
     {
         const int P = a.R * nc;
         const int PT = a.weighted ? K * nc : 0;
@@ -342,175 +352,277 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
             if (j1 < total4) s4[j1] = v1;
         }
     }
-    const bool greedy = T == 0.f;
-    const bool weighted = a.weighted && !greedy;
-    int fail = 0;
-    if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
-    else if (!greedy && K > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
-
-    const bool x_ok = x >= 0 && x < a.V;
-    float zt = 0.f, zd = 0.f;
-    if (tid < K) {
-        L.x[tid] = x;
-        if (!fail && !greedy && x_ok) {
-            zt = Elt<DT>::scalar(target_row(a, b, tid), x);
-            zd = Elt<DT>::scalar(draft_row(a, b, tid), x);
+    __syncthreads();
+    const int nrows = greedy ? K + 1 : 2 * K + 1;
+    const ExpScale e = make_scale(greedy ? 1.f : T);
+    for (int r = wave; r < nrows; r += kWaves) {
+        const RowPart *p = L.part + r * nc;
+        if (greedy) {
+            float M;
+            int I;
+            merge_argmax(p, nc, M, I);
+            if (lane == 0) {
+                L.m[r] = M;
+                L.idx[r] = I;
+            }
+        } else if (weighted && r > K) {
+            const int i = r - (K + 1);
+            float M;
+            Top4 rt4;
+            double D;
+            merge_weighted(p, L.ptop + i * nc, nc, e, (double)a.beta, M, rt4, D);
+            if (lane == 0) {
+                L.m[r] = M;
+                L.S[r] = D;
+                L.top[i] = rt4;
+            }
+        } else {
+            float M;
+            double S;
+            merge_sum(p, nc, e, M, S);
+            if (lane == 0) {
+                L.m[r] = M;
+                L.S[r] = S;
+            }
         }
     }
     __syncthreads();
+}
 
-    if (!fail) {
-        const int nrows = greedy ? K + 1 : 2 * K + 1;
-        const ExpScale e = make_scale(greedy ? 1.f : T);
-        for (int r = wave; r < nrows; r += kWaves) {
-            const RowPart *p = L.part + r * nc;
-            if (greedy) {
-                float M;
-                int I;
-                merge_argmax(p, nc, M, I);
-                if (lane == 0) {
-                    L.m[r] = M;
-                    L.idx[r] = I;
-                }
-            } else if (weighted && r > K) {
-                const int i = r - (K + 1);
-                float M;
-                Top4 rt4;
-                double S_rest, S_top;
-                merge_weighted(p, L.ptop + i * nc, nc, e, M, rt4, S_rest, S_top);
-                if (lane == 0) {
-                    L.m[r] = M;
-                    L.S[r] = S_rest + (double)a.beta * S_top;
-                    L.top[i] = rt4;
-                }
-            } else {
-                float M;
-                double S;
-                merge_sum(p, nc, e, M, S);
-                if (lane == 0) {
-                    L.m[r] = M;
-                    L.S[r] = S;
-                }
+// Rows of at most kThreadMerge chunks: each position thread loads and merges
+// its own rows' partials (the same formulas as the wave merges, in chunk
+// order).  Loads are issued before the temperature is known.
+
+struct PosLoads {
+    RowPart t[kThreadMerge], d[kThreadMerge];
+    Top4 top[kThreadMerge];
+};
+
+__device__ __forceinline__ void load_position(const Args &a, int b, int i, PosLoads &pl)
+{
+    const int K = a.K, nc = a.nc;
+    const RowPart *gt = a.part + ((int64_t)b * a.R + i) * nc;
+    const RowPart *gd = a.part + ((int64_t)b * a.R + K + 1 + i) * nc;
+    const Top4 *gtop = a.top + ((int64_t)b * K + i) * nc;
+#pragma unroll
+    for (int c = 0; c < kThreadMerge; ++c) {
+        pl.t[c] = RowPart{};
+        pl.d[c] = RowPart{};
+        top_clear(pl.top[c]);
+        if (c < nc) {
+            pl.t[c] = gt[c];
+            if (i < K) {
+                pl.d[c] = gd[c];
+                if (a.weighted) pl.top[c] = gtop[c];
             }
         }
-        __syncthreads();
+    }
+}
 
-        if (!greedy && tid < K) {
-            const int i = tid;
-            const float mt = L.m[i], md = L.m[K + 1 + i];
-            int err = 0;
-            if (!isfinite(mt)) err |= SV_ERR_ROW;
-            if (!isfinite(md)) err |= SV_ERR_ROW;
-            else if (!(L.S[K + 1 + i] > 0.0)) err |= SV_ERR_DRAFT_MASS;
-            const bool in_top = weighted && top_has(L.top[i], x);
-            const float u = philox_uniform(a.seed, gb, (uint32_t)i, kPurposeAccept);
-            float pt, pd;
-            const bool want_p = publish && (a.aux_pt != nullptr || a.aux_pd != nullptr);
-            L.acc[i] = decide(e, row_offset(mt, e), L.S[i], row_offset(md, e), L.S[K + 1 + i], in_top,
-                              a.log2_beta, x_ok && err == 0, zt, zd, u, want_p, pt, pd)
-                           ? 1
-                           : 0;
-            L.err[i] = err;
-            L.pt[i] = pt;
-            L.pd[i] = pd;
+__device__ __forceinline__ void thread_merge_sum(const RowPart (&p)[kThreadMerge], int nc, const ExpScale &e,
+                                                 float &M, double &S)
+{
+    M = p[0].m;
+#pragma unroll
+    for (int c = 1; c < kThreadMerge; ++c)
+        if (c < nc) M = fmaxf(M, p[c].m);
+    const double om = (double)row_offset(M, e);
+    S = 0.0;
+#pragma unroll
+    for (int c = 0; c < kThreadMerge; ++c)
+        if (c < nc && p[c].m != -INFINITY && p[c].s != 0.0)
+            S += nc == 1 ? p[c].s : p[c].s * exp2((double)row_offset(p[c].m, e) - om);
+}
+
+// Fill the position's row statistics from its loads (sampling rows need the
+// temperature's scale e; greedy rows take the argmax).
+__device__ __forceinline__ void thread_rows(const PosLoads &pl, int nc, int i, int K, bool greedy,
+                                            bool weighted, double beta, const ExpScale &e, PosRows &pr)
+{
+    pr.zt = __int_as_float(pl.t[0].idx);
+    pr.zd = __int_as_float(pl.d[0].idx);
+    if (greedy) {
+        float v = pl.t[0].m;
+        int j = pl.t[0].idx;
+#pragma unroll
+        for (int c = 1; c < kThreadMerge; ++c)
+            if (c < nc && better(pl.t[c].m, pl.t[c].idx, v, j)) {
+                v = pl.t[c].m;
+                j = pl.t[c].idx;
+            }
+        pr.mt = v;
+        pr.am = j;
+        return;
+    }
+    thread_merge_sum(pl.t, nc, e, pr.mt, pr.St);
+    if (i >= K) return;
+    double s;
+    thread_merge_sum(pl.d, nc, e, pr.md, s);
+    if (!weighted) {
+        pr.D = s;
+        return;
+    }
+    if (nc == 1) {  // the streaming pass formed D
+        pr.top = pl.top[0];
+        pr.D = s;
+        return;
+    }
+    Top4 t;
+    top_clear(t);
+#pragma unroll
+    for (int c = 0; c < kThreadMerge; ++c)
+        if (c < nc) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) top_insert(t, pl.top[c].v[k], pl.top[c].i[k]);
         }
-        __syncthreads();
+    const double om = (double)row_offset(pr.md, e);
+    double extra = 0.0;
+#pragma unroll
+    for (int c = 0; c < kThreadMerge; ++c)
+        if (c < nc) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float v = pl.top[c].v[k];
+                const int j = pl.top[c].i[k];
+                if (j != INT_MAX && v != -INFINITY && !top_has(t, j)) extra += exp_scaled64(v, om, e.c64);
+            }
+        }
+    pr.top = t;
+    pr.D = weighted_norm(s + extra, t, om, e.c64, beta);
+}
+
+// Returns the outcome to every thread; `publish` writes the sequence's
+// outputs (all but the bonus token of a sampling sequence) and its SeqState.
+template <int DT>
+__device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int K = a.K, nc = a.nc;
+    const bool pos = tid <= K;  // this thread stands for position tid
+    const uint32_t gb = (uint32_t)(a.b0 + b);  // Philox keys on the sequence's index in the call
+    int32_t *out = a.out_tokens + (int64_t)b * (K + 1);
+
+    // one round trip: temperature, drafted token, and (one chunk per row) the
+    // position's partials
+    const float T = a.temperature[b];
+    int x = -1;
+    if (tid < K) x = a.tokens[(int64_t)b * K + tid];
+    PosRows pr;
+    pr.mt = pr.md = -INFINITY;
+    pr.zt = pr.zd = 0.f;
+    pr.St = pr.D = 0.0;
+    pr.am = -1;
+    top_clear(pr.top);
+    const bool greedy = T == 0.f;
+    const bool weighted = a.weighted && !greedy;
+    const bool own = nc <= kThreadMerge;
+    PosLoads pl;
+    if (own && pos) load_position(a, b, tid, pl);
+    int fail = 0;
+    if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
+    else if (!greedy && K > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
+    if (own && pos && !fail)
+        thread_rows(pl, nc, tid, K, greedy, weighted, (double)a.beta, make_scale(greedy ? 1.f : T), pr);
+    if (!own && !fail) {
+        merge_rows<DT>(a, b, T, greedy, weighted, L);
+        if (pos) {
+            pr.mt = L.m[tid];
+            pr.St = L.S[tid];
+            pr.am = L.idx[tid];
+            pr.zt = __int_as_float(L.part[tid * nc].idx);
+        }
+        if (tid < K && !greedy) {
+            pr.md = L.m[K + 1 + tid];
+            pr.D = L.S[K + 1 + tid];
+            pr.zd = __int_as_float(L.part[(K + 1 + tid) * nc].idx);
+            if (weighted) pr.top = L.top[tid];
+        }
     }
 
-    if (tid == 0) {
-        int n = K;
-        int err_bits = 0;
-        SeqState st = {};
-        st.mode = 0;
-        if (!fail && greedy) {
-            for (int i = 0; i <= K; ++i) {
-                if (!isfinite(L.m[i])) {
-                    fail = SV_ERR_ROW;
-                    break;
-                }
-                if (i < K && L.x[i] == L.idx[i]) continue;
-                n = i;
-                break;
-            }
-            if (!fail && publish) {
-                for (int i = 0; i < n; ++i) out[i] = L.x[i];
-                if (n < K) {
-                    const int xn = L.x[n];
-                    if (xn < 0 || xn >= a.V) err_bits |= SV_ERR_TOKEN;
-                }
-                out[n] = L.idx[n];
-                for (int i = n + 1; i <= K; ++i) out[i] = -1;
-                a.accepted_len[b] = n;
-                if (a.aux_pt)
-                    for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
-                if (a.aux_pd)
-                    for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
-                if (a.aux_z) a.aux_z[b] = NAN;
-            }
-        } else if (!fail) {
-            for (int i = 0; i < K; ++i) {
-                if (L.err[i]) {  // rows of this position are unusable and it is reached
-                    fail = L.err[i];
-                    break;
-                }
-                if (!L.acc[i]) {
-                    n = i;
-                    break;
-                }
-            }
-            if (!fail && n == K && !isfinite(L.m[K])) fail = SV_ERR_ROW;
-            if (!fail) {
-                if (publish) {
-                    for (int i = 0; i < n; ++i) out[i] = L.x[i];
-                    for (int i = n; i <= K; ++i) out[i] = -1;  // out[n]: the bonus step
-                    if (n < K) {
-                        const int xn = L.x[n];
-                        if (xn < 0 || xn >= a.V) err_bits |= SV_ERR_TOKEN;
-                    }
-                    a.accepted_len[b] = n;
-                    if (a.aux_pt)
-                        for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = i <= n ? L.pt[i] : NAN;
-                    if (a.aux_pd)
-                        for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = i <= n ? L.pd[i] : NAN;
-                }
-                st.n = n;
-                st.mode = n < K ? 1 : 2;
-                const ExpScale e = make_scale(T);
-                st.o_t = row_offset(L.m[n], e);
-                st.inv_st = (float)(1.0 / L.S[n]);
-                st.T = T;
-                st.u_bonus = philox_uniform(a.seed, gb, (uint32_t)n, kPurposeBonus);
+    // this position: does it stop the scan, and the bonus state if it is n
+    int err = fail;
+    bool stop = true;
+    float ppt = NAN, ppd = NAN;
+    SeqState cs = {};
+    cs.mode = 0;
+    if (pos && !fail) {
+        if (greedy) {
+            if (!isfinite(pr.mt)) err = SV_ERR_ROW;
+            stop = err != 0 || tid == K || x != pr.am;
+        } else {
+            const ExpScale e = make_scale(T);
+            const float ot = row_offset(pr.mt, e);
+            if (!isfinite(pr.mt)) err = SV_ERR_ROW;
+            cs.n = tid;
+            cs.o_t = ot;
+            cs.inv_st = (float)(1.0 / pr.St);
+            cs.T = T;
+            cs.u_bonus = philox_uniform(a.seed, gb, (uint32_t)tid, kPurposeBonus);
+            cs.lbeta = (float)a.log2_beta;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) st.top[k] = -1;
-                st.lbeta = (float)a.log2_beta;
-                if (n < K) {
-                    st.o_d = row_offset(L.m[K + 1 + n], e);
-                    st.k2 = ((double)st.o_t - (double)st.o_d) + log2(L.S[n] / L.S[K + 1 + n]);
-                    if (weighted) {
+            for (int k = 0; k < 4; ++k) cs.top[k] = -1;
+            if (tid < K) {
+                if (!isfinite(pr.md)) err |= SV_ERR_ROW;
+                else if (!(pr.D > 0.0)) err |= SV_ERR_DRAFT_MASS;
+                const bool x_ok = x >= 0 && x < a.V;
+                const bool in_top = weighted && top_has(pr.top, x);
+                const float u = philox_uniform(a.seed, gb, (uint32_t)tid, kPurposeAccept);
+                const float od = row_offset(pr.md, e);
+                const double lq = log2(pr.D / pr.St);
+                const bool want_p = publish && (a.aux_pt != nullptr || a.aux_pd != nullptr);
+                const bool acc = decide(e, ot, pr.St, od, pr.D, lq, in_top, a.log2_beta, x_ok && err == 0,
+                                        pr.zt, pr.zd, u, want_p, ppt, ppd);
+                stop = err != 0 || !acc;
+                cs.mode = 1;
+                cs.o_d = od;
+                cs.k2 = ((double)ot - (double)od) - lq;
+                if (weighted) {
 #pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            st.top[k] = L.top[n].i[k] == INT_MAX ? -1 : L.top[n].i[k];
-                    }
+                    for (int k = 0; k < 4; ++k) cs.top[k] = pr.top.i[k] == INT_MAX ? -1 : pr.top.i[k];
                 }
+            } else {
+                cs.mode = 2;
             }
         }
-        if (fail) {
-            if (publish) {
-                a.accepted_len[b] = 0;
-                for (int i = 0; i <= K; ++i) out[i] = -1;
-                if (a.aux_pt)
-                    for (int i = 0; i < K; ++i) a.aux_pt[(int64_t)b * K + i] = NAN;
-                if (a.aux_pd)
-                    for (int i = 0; i < K; ++i) a.aux_pd[(int64_t)b * K + i] = NAN;
-                if (a.aux_z) a.aux_z[b] = NAN;
-            }
+    }
+    if (pos) L.flag[tid] = stop ? (err ? 3 : 1) : 0;
+    __syncthreads();
+
+    // n: the first position that stops the scan (position K always does)
+    int n = K;
+    for (int g0 = 0; g0 <= K; g0 += 64) {
+        const int i = g0 + lane;
+        const uint64_t m = __ballot(i <= K && L.flag[i] != 0);
+        if (m != 0ull) {
+            n = g0 + __ffsll((unsigned long long)m) - 1;
+            break;
+        }
+    }
+    const bool bad = (L.flag[n] & 2) != 0;  // failed: no outputs but -1
+    if (publish && pos) {
+        int v = -1;
+        if (!bad && tid < n) v = x;
+        if (!bad && greedy && tid == n) v = pr.am;
+        out[tid] = v;
+        if (tid < K) {
+            const bool keep = !bad && !greedy && tid <= n;
+            if (a.aux_pt) a.aux_pt[(int64_t)b * K + tid] = keep ? ppt : NAN;
+            if (a.aux_pd) a.aux_pd[(int64_t)b * K + tid] = keep ? ppd : NAN;
+        }
+    }
+    if (tid == n) {
+        int err_bits = err;
+        SeqState st = cs;
+        if (bad || greedy) {
             st = SeqState{};
             st.mode = 0;
-            err_bits |= fail;
         }
+        if (!bad && n < K && (x < 0 || x >= a.V)) err_bits |= SV_ERR_TOKEN;
         *L.st = st;
         if (publish) {
             a.seq[b] = st;
+            a.accepted_len[b] = bad ? 0 : n;
+            if ((bad || greedy) && a.aux_z) a.aux_z[b] = NAN;
             if (err_bits && a.error_word) atomicOr(a.error_word, err_bits);
         }
     }

@@ -230,6 +230,71 @@ def test_draft_lengths(sv, oracle_mod, K):
         run_both(sv, oracle_mod, inp, seed=K, ptol=_ptol(dtype)).check()
 
 
+def _shaped_draft_rows(rng, K, V):
+    """Draft rows whose top-4 forms in every way a streaming pass can meet:
+    rising and falling rows (every element, or none, a new entry), constant
+    rows and repeated maxima (ties broken by index), the top at the ragged
+    tail, signed zeros at the top, rows of mostly -inf, and Zipf-like rows."""
+    rows = np.empty((K, V), dtype=np.float32)
+    for i in range(K):
+        s = i % 8
+        if s == 0:
+            r = np.linspace(-6.0, 6.0, V)
+        elif s == 1:
+            r = np.linspace(6.0, -6.0, V)
+        elif s == 2:
+            r = np.zeros(V)
+        elif s == 3:
+            r = rng.normal(size=V)
+            r[-7:] = 5.0 + np.arange(7) * 0.25
+        elif s == 4:
+            r = rng.normal(size=V) * 2
+            r[rng.choice(V, size=6, replace=False)] = r.max() + 1.0
+        elif s == 5:
+            r = np.full(V, -1.0)
+            pos = rng.choice(V, size=6, replace=False)
+            r[pos[:3]] = -0.0
+            r[pos[3:]] = 0.0
+        elif s == 6:
+            r = np.full(V, -np.inf)
+            r[rng.choice(V, size=2, replace=False)] = rng.normal(size=2)
+        else:
+            r = rng.normal(size=V) * 3 - 1.1 * np.log1p(rng.permutation(V))
+        rows[i] = r
+    return rows
+
+
+def _top4_indices(row):
+    order = np.lexsort((np.arange(row.size), -row.astype(np.float64)))
+    return order[:4]
+
+
+@pytest.mark.parametrize("B,V", [(6, 70001), (48, 9001), (64, 20011), (128, 20011)])
+def test_weighted_draft_rows_of_every_shape(sv, oracle_mod, B, V):
+    """Beta-weighted draft rows: top-4 selection under ties, rising rows and
+    ragged tails, with many chunks per row (few sequences: merged per wave),
+    three and two chunks (merged per position thread) and one chunk."""
+    rng = np.random.default_rng(B + V)
+    K = 8
+    drf = np.stack([_shaped_draft_rows(rng, K, V) for _ in range(B)])
+    tgt = np.concatenate([drf, rng.normal(size=(B, 1, V)).astype(np.float32) * 2], axis=1)
+    tgt[:, :K] += (0.5 * rng.normal(size=(B, K, V))).astype(np.float32)
+    tgt[:, 6::8] = np.where(np.isinf(drf[:, 6::8]), 0.0, tgt[:, 6::8])  # targets stay finite
+    temps = rng.uniform(0.5, 1.2, size=B).astype(np.float32)
+    for dtype in ("fp32", "bf16"):
+        d_used = to_bf16_bits(drf).view(np.uint16).astype(np.uint32) if dtype == "bf16" else None
+        tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+        for b in range(B):
+            for i in range(K):
+                row = drf[b, i] if d_used is None else (d_used[b, i] << 16).view(np.float32)
+                if rng.random() < 0.6:
+                    tok[b, i] = _top4_indices(row)[rng.integers(0, 4)]
+        for beta in (0.5, 0.05):
+            _say(f"weighted shapes B={B} V={V} dtype={dtype} beta={beta}")
+            inp = _inputs_from_numpy(tgt, drf, tok, temps, beta, dtype)
+            run_both(sv, oracle_mod, inp, seed=B, ptol=_ptol(dtype)).check()
+
+
 def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod):
     rng = np.random.default_rng(3)
     B, K, V = 16, 5, 50000
