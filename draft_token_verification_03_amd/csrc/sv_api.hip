@@ -60,6 +60,8 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     off = align256(off + sizeof(RowPart) * (size_t)rows * p->nc);
     p->off_top = off;
     off = align256(off + sizeof(Top4) * (size_t)p->sB * K * p->nc);
+    p->off_tope = off;
+    off = align256(off + sizeof(double4) * (size_t)p->sB * K * p->nc);
     p->off_seq = off;
     off = align256(off + sizeof(SeqState) * (size_t)p->sB);
     p->off_slot = off;
@@ -89,6 +91,7 @@ static Args sub_args(const Plan &p, void *ws, int32_t b0, int32_t nb)
     a.row_bytes = p.row_bytes;
     a.part = reinterpret_cast<RowPart *>(w + p.off_part);
     a.top = reinterpret_cast<Top4 *>(w + p.off_top);
+    a.tope = reinterpret_cast<double4 *>(w + p.off_tope);
     a.seq = reinterpret_cast<SeqState *>(w + p.off_seq);
     a.slot = reinterpret_cast<double *>(w + p.off_slot);
     return a;

@@ -59,7 +59,7 @@ struct Plan {
     int32_t nc, cvec;       // streaming chunks per row, vectors per chunk
     int32_t nslot, gs;      // residual slots per row, kSlotVec-vector units per slot
     int32_t ng, spg;        // residual workgroups per sequence, slots per workgroup
-    size_t off_part, off_top, off_seq, off_slot;
+    size_t off_part, off_top, off_tope, off_seq, off_slot;
     size_t bytes;           // total workspace
 };
 
@@ -81,6 +81,7 @@ struct Args {
     int32_t *out_tokens;
     RowPart *part;          // [sB][R][nc]
     Top4 *top;              // [sB][K][nc]
+    double4 *tope;          // [sB][K][nc] exp2((v - m_c) c) of each chunk top-4 entry (nc > 1)
     SeqState *seq;          // [sB]
     double *slot;           // [sB][nslot] residual mass of each slot
     float *aux_pt, *aux_pd, *aux_z;

@@ -223,8 +223,23 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
                 run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, slots);
             });
             run_finish_top(run, slots, e, lds_f, lds_d, part.m, part.s, ct);
-            if (a.nc == 1 && threadIdx.x == 0)  // a whole row: its normaliser D
-                part.s = weighted_norm(part.s, ct, (double)row_offset(part.m, e), e.c64, (double)a.beta);
+            if (threadIdx.x < 4) {
+                // lane k: the mass of entry k, relative to the chunk's offset;
+                // one chunk a row: the row's normaliser D (lane 0 adds the quad)
+                const int k = threadIdx.x;
+                const float v = k == 0 ? ct.v[0] : k == 1 ? ct.v[1] : k == 2 ? ct.v[2] : ct.v[3];
+                const int ix = k == 0 ? ct.i[0] : k == 1 ? ct.i[1] : k == 2 ? ct.i[2] : ct.i[3];
+                const double w = (ix != INT_MAX && v != -INFINITY)
+                                     ? exp_scaled64(v, (double)row_offset(part.m, e), e.c64)
+                                     : 0.0;
+                if (a.nc == 1) {
+                    double q = w + dpp_double<kDppQuadXor1>(w);
+                    q += dpp_double<kDppQuadXor2>(q);
+                    part.s += (double)a.beta * q;
+                } else {
+                    reinterpret_cast<double *>(&a.tope[((int64_t)b * a.K + i) * a.nc + chunk])[k] = w;
+                }
+            }
         } else {
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
                 run_sum_tile<DT, kLoads>(t, e, run);
@@ -396,6 +411,7 @@ __device__ __forceinline__ void merge_rows(const Args &a, int b, float T, bool g
 struct PosLoads {
     RowPart t[kThreadMerge], d[kThreadMerge];
     Top4 top[kThreadMerge];
+    double4 tope[kThreadMerge];
 };
 
 __device__ __forceinline__ void load_position(const Args &a, int b, int i, PosLoads &pl)
@@ -404,38 +420,79 @@ __device__ __forceinline__ void load_position(const Args &a, int b, int i, PosLo
     const RowPart *gt = a.part + ((int64_t)b * a.R + i) * nc;
     const RowPart *gd = a.part + ((int64_t)b * a.R + K + 1 + i) * nc;
     const Top4 *gtop = a.top + ((int64_t)b * K + i) * nc;
+    const double4 *gtope = a.tope + ((int64_t)b * K + i) * nc;
 #pragma unroll
     for (int c = 0; c < kThreadMerge; ++c) {
         pl.t[c] = RowPart{};
         pl.d[c] = RowPart{};
         top_clear(pl.top[c]);
+        pl.tope[c] = make_double4(0.0, 0.0, 0.0, 0.0);
         if (c < nc) {
             pl.t[c] = gt[c];
             if (i < K) {
                 pl.d[c] = gd[c];
-                if (a.weighted) pl.top[c] = gtop[c];
+                if (a.weighted) {
+                    pl.top[c] = gtop[c];
+                    if (nc > 1) pl.tope[c] = gtope[c];
+                }
             }
         }
     }
 }
 
+// M and S of a row from its chunk partials, and each chunk's factor
+// f_c = exp2(o_c - o_M) (exactly 1 for a chunk that holds the row max).
 __device__ __forceinline__ void thread_merge_sum(const RowPart (&p)[kThreadMerge], int nc, const ExpScale &e,
-                                                 float &M, double &S)
+                                                 float &M, double &S, double (&f)[kThreadMerge])
 {
     M = p[0].m;
 #pragma unroll
     for (int c = 1; c < kThreadMerge; ++c)
         if (c < nc) M = fmaxf(M, p[c].m);
-    const double om = (double)row_offset(M, e);
+    const float oM = row_offset(M, e);
     S = 0.0;
 #pragma unroll
-    for (int c = 0; c < kThreadMerge; ++c)
-        if (c < nc && p[c].m != -INFINITY && p[c].s != 0.0)
-            S += nc == 1 ? p[c].s : p[c].s * exp2((double)row_offset(p[c].m, e) - om);
+    for (int c = 0; c < kThreadMerge; ++c) {
+        f[c] = 0.0;
+        if (c < nc && p[c].m != -INFINITY) {
+            const float oc = row_offset(p[c].m, e);
+            f[c] = oc == oM ? 1.0 : exp2((double)oc - (double)oM);
+            if (p[c].s != 0.0) S += p[c].s * f[c];
+        }
+    }
+}
+
+// Insert (v, i) with mass w into the list t (masses tw); returns the mass
+// that leaves it (w itself when (v, i) does not enter).
+__device__ __forceinline__ double top_insert_mass(Top4 &t, double (&tw)[4], float v, int i, double w)
+{
+    if (!better(v, i, t.v[3], t.i[3])) return w;
+    const double out = tw[3];
+    t.v[3] = v;
+    t.i[3] = i;
+    tw[3] = w;
+#pragma unroll
+    for (int k = 3; k > 0; --k) {
+        if (better(t.v[k], t.i[k], t.v[k - 1], t.i[k - 1])) {
+            const float tv = t.v[k];
+            const int ti = t.i[k];
+            const double tm = tw[k];
+            t.v[k] = t.v[k - 1];
+            t.i[k] = t.i[k - 1];
+            tw[k] = tw[k - 1];
+            t.v[k - 1] = tv;
+            t.i[k - 1] = ti;
+            tw[k - 1] = tm;
+        }
+    }
+    return out;
 }
 
 // Fill the position's row statistics from its loads (sampling rows need the
-// temperature's scale e; greedy rows take the argmax).
+// temperature's scale e; greedy rows take the argmax).  A weighted draft row
+// of several chunks merges the chunks' top-4 lists, whose entries carry their
+// masses (relative to their chunk's offset, from the streaming pass): the
+// row's top-4 form S_top, every other entry joins the mass outside it.
 __device__ __forceinline__ void thread_rows(const PosLoads &pl, int nc, int i, int K, bool greedy,
                                             bool weighted, double beta, const ExpScale &e, PosRows &pr)
 {
@@ -454,41 +511,29 @@ __device__ __forceinline__ void thread_rows(const PosLoads &pl, int nc, int i, i
         pr.am = j;
         return;
     }
-    thread_merge_sum(pl.t, nc, e, pr.mt, pr.St);
+    double f[kThreadMerge];
+    thread_merge_sum(pl.t, nc, e, pr.mt, pr.St, f);
     if (i >= K) return;
     double s;
-    thread_merge_sum(pl.d, nc, e, pr.md, s);
-    if (!weighted) {
+    thread_merge_sum(pl.d, nc, e, pr.md, s, f);
+    if (!weighted || nc == 1) {  // one chunk: the streaming pass formed D
+        if (weighted) pr.top = pl.top[0];
         pr.D = s;
         return;
     }
-    if (nc == 1) {  // the streaming pass formed D
-        pr.top = pl.top[0];
-        pr.D = s;
-        return;
-    }
-    Top4 t;
-    top_clear(t);
-#pragma unroll
-    for (int c = 0; c < kThreadMerge; ++c)
-        if (c < nc) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) top_insert(t, pl.top[c].v[k], pl.top[c].i[k]);
-        }
-    const double om = (double)row_offset(pr.md, e);
+    Top4 t = pl.top[0];
+    double tw[4] = {pl.tope[0].x * f[0], pl.tope[0].y * f[0], pl.tope[0].z * f[0], pl.tope[0].w * f[0]};
     double extra = 0.0;
 #pragma unroll
-    for (int c = 0; c < kThreadMerge; ++c)
+    for (int c = 1; c < kThreadMerge; ++c)
         if (c < nc) {
+            const double w[4] = {pl.tope[c].x * f[c], pl.tope[c].y * f[c], pl.tope[c].z * f[c],
+                                 pl.tope[c].w * f[c]};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float v = pl.top[c].v[k];
-                const int j = pl.top[c].i[k];
-                if (j != INT_MAX && v != -INFINITY && !top_has(t, j)) extra += exp_scaled64(v, om, e.c64);
-            }
+            for (int k = 0; k < 4; ++k) extra += top_insert_mass(t, tw, pl.top[c].v[k], pl.top[c].i[k], w[k]);
         }
     pr.top = t;
-    pr.D = weighted_norm(s + extra, t, om, e.c64, beta);
+    pr.D = (s + extra) + beta * (((tw[0] + tw[1]) + tw[2]) + tw[3]);
 }
 
 // Returns the outcome to every thread; `publish` writes the sequence's
