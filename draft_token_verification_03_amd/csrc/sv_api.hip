@@ -25,11 +25,14 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     p->row_bytes = (int64_t)V * elt;
     p->nvec = (int32_t)(((int64_t)V + p->vec - 1) / p->vec);
 
-    // streaming: ~kFillBlocks workgroups per sub-batch, >= one vector per
-    // thread, and one sequence's partials and top-4 lists within the tail
-    // kernel's LDS staging
+    // streaming: ~kFillBlocks workgroups per sub-batch (one round of resident
+    // workgroups), >= one vector per thread, and one sequence's partials and
+    // top-4 lists within the accept scan's LDS staging
     const int64_t rows = (int64_t)p->sB * p->R;
     int64_t nc = (kFillBlocks + rows - 1) / rows;
+    // rows enough to cover the chip with a few chunks each: at most as many as
+    // the accept scan merges per thread
+    if (rows * kThreadMerge >= kCUs) nc = std::min<int64_t>(nc, kThreadMerge);
     // long rows in a batch that fills the grid by itself: two chunks a row
     // halve the size of the grid's workgroups, so its last round leaves less
     // of the chip idle

@@ -14,7 +14,8 @@ namespace sv {
 constexpr int kMaxK = 128;               // drafted positions per sequence
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kMaxChunks = 1024;         // streaming chunks per row
-constexpr int kFillBlocks = 2048;        // workgroups the streaming grid aims for
+constexpr int kFillBlocks = 768;         // workgroups the streaming grid aims for (one round)
+constexpr int kCUs = 256;                // compute units of the chip
 constexpr int64_t kSplitRowBytes = 256 * 1024;  // rows this long take at least two chunks
 constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
 constexpr int kStageBytes = 24 * 1024;   // LDS staging of one sequence's partials

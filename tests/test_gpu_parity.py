@@ -269,7 +269,7 @@ def _top4_indices(row):
     return order[:4]
 
 
-@pytest.mark.parametrize("B,V", [(6, 70001), (48, 9001), (64, 20011), (128, 20011)])
+@pytest.mark.parametrize("B,V", [(3, 70001), (16, 9001), (32, 20011), (128, 20011)])
 def test_weighted_draft_rows_of_every_shape(sv, oracle_mod, B, V):
     """Beta-weighted draft rows: top-4 selection under ties, rising rows and
     ragged tails, with many chunks per row (few sequences: merged per wave),
