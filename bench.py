@@ -85,7 +85,8 @@ def cpu_baseline(inp, w, seconds: float) -> dict:
     return {"value": logits / el, "unit": "logits/s", "cores": min(threads, nseq),
             "kind": "oracle",
             "sample": f"{nseq} of {w.B} sequences of {w.tag()}, {calls} calls in {el:.1f} s, "
-                      f"OpenMP over sequences with {threads} threads"}
+                      f"OpenMP over sequences, {threads} threads in the team, "
+                      f"{min(threads, nseq)} busy (one sequence each at a time)"}
 
 
 def main() -> int:

@@ -20,6 +20,8 @@
 // launches wrote, so no workgroup ever waits for another.
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "sv_accept.h"
 #include "sv_tile.h"
 
@@ -257,12 +259,13 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
 template <int DT, bool TOP>
 __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
 {
+    // without draft logits only the target rows 0..K of each sequence are launched
+    const int rl = a.draft ? a.R : a.K + 1;
     const int chunk = blockIdx.x % a.nc;
-    const int slot_row = blockIdx.x / a.nc;
-    const int b = slot_row / a.R;
-    const int j = slot_row - b * a.R;
+    const int b = (blockIdx.x / a.nc) / rl;
+    const int j = blockIdx.x / a.nc - b * rl;
+    const int slot_row = b * a.R + j;
     const bool is_draft = j > a.K;
-    if (is_draft && a.draft == nullptr) return;
     const int i = is_draft ? j - (a.K + 1) : j;
     const float T = a.temperature[b];
     const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
@@ -1036,12 +1039,15 @@ __global__ void uniforms_kernel(uint64_t seed, int32_t B, int32_t P, float *out)
 template <int DT, bool TOP>
 static void launch_all(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)
 {
-    if (begin) (void)hipEventRecord(begin, s);
-    stats_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.R * a.nc), kBlock, 0, s>>>(a);
-    if (end) (void)hipEventRecord(end, s);
+    const unsigned grid = (unsigned)((int64_t)a.B * (a.draft ? a.R : a.K + 1) * a.nc);
+    if (begin || end)  // the dispatch itself stamps the kernel's start and end
+        hipExtLaunchKernelGGL(stats_kernel<DT, TOP>, dim3(grid), dim3(kBlock), 0, s, begin, end, 0, a);
+    else
+        stats_kernel<DT, TOP><<<grid, kBlock, 0, s>>>(a);
     const size_t lds = accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, nullptr, nullptr);
     residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ng), kBlock, lds, s>>>(a);
-    bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
+    // without draft logits (K > 0) every sequence is greedy or fails: no bonus draw
+    if (a.draft || a.K == 0) bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
 }
 
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)

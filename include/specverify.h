@@ -88,8 +88,8 @@ typedef struct sv_aux {
     float *p_draft;       /* [B, K] q_i(x_i) (beta-weighted) at evaluated positions, else NaN         */
     float *residual_mass; /* [B]    C(V-1) of the bonus draw; NaN in greedy mode                      */
     int32_t *error_word;  /* [1]    SV_ERR_* bits are OR-ed in: zero it before the call           */
-    void *pass_begin;     /* hipEvent_t recorded on `stream` right before the streaming-pass launch */
-    void *pass_end;       /* and right after it (first sub-batch only): times the dominant kernel   */
+    void *pass_begin;     /* hipEvent_t stamped with the start of the streaming-pass kernel      */
+    void *pass_end;       /* and with its end (first sub-batch only): times the dominant kernel  */
 } sv_aux;
 
 /*
@@ -110,10 +110,10 @@ size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype
  *   workspace      device buffer of >= spec_verify_workspace_size(...) bytes
  *                  (see "Workspace" above)
  *   aux            host pointer to an sv_aux, or NULL
- * B == 0 is a no-op.  Returns SV_OK after enqueuing the work: four kernel
- * launches per sub-batch of at most 8192 sequences (streaming pass, accept
- * scan, residual chunk sums, bonus draw), the last two skipped when
- * draft_logits is NULL and K > 0.
+ * B == 0 is a no-op.  Returns SV_OK after enqueuing the work: three kernel
+ * launches per sub-batch of at most 8192 sequences (streaming pass; accept
+ * scan and residual slot masses; bonus draw), the last one skipped when
+ * draft_logits is NULL and K > 0 (every sequence is then greedy or fails).
  */
 int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
