@@ -159,10 +159,10 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps
     mean_acc = float(acc.float().mean().item())
     # Timed region 2 (roofline): the same K steps again, now with a pair of
-    # events per step that the library records on the kernels' stream right
-    # before and after the streaming-pass launch.  Each event is recorded once
-    # beforehand so that the HIP event exists.  Kept apart from region 1
-    # because the extra event records widen the gaps between launches.
+    # events per step that the streaming-pass dispatch itself stamps with the
+    # kernel's start and end.  Each event is recorded once beforehand so that
+    # the HIP event exists.  Kept apart from region 1 so that nothing about the
+    # events can touch the value.
     pass_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
     for e0, e1 in pass_ev:
@@ -179,6 +179,20 @@ def main() -> int:
     torch.cuda.synchronize()
     pass_ms = sum(e0.elapsed_time(e1) for e0, e1 in pass_ev) / args.steps
     ms_with_events = start2.elapsed_time(stop2) / args.steps
+    # Timed region 3 (the pass's read floor): the streaming pass's grid, rows,
+    # chunks and loads with its arithmetic taken out, over the same replicas,
+    # stamped the same way.
+    sink = torch.empty(1, dtype=torch.int32, device=dev)
+    for k in range(args.warmup):
+        r = replicas[k % reps]
+        sv.stream_probe(r["target"], None if w.greedy else r["draft"], sink=sink, stream=stream)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        r = replicas[k % reps]
+        sv.stream_probe(r["target"], None if w.greedy else r["draft"], sink=sink, events=pass_ev[k],
+                        stream=stream)
+    torch.cuda.synchronize()
+    floor_ms = sum(e0.elapsed_time(e1) for e0, e1 in pass_ev) / args.steps
 
     logits_per_step = w.B * (w.K + 1) * w.V
     value = logits_per_step / (ms * 1e-3)
@@ -211,7 +225,13 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "stats_kernel (streaming pass)", "kernel_ms": pass_ms,
-                     "algorithmic_bytes_per_launch": pass_bytes},
+                     "algorithmic_bytes_per_launch": pass_bytes,
+                     "read_floor": {"kernel_ms": floor_ms,
+                                    "achieved": pass_bytes / (floor_ms * 1e-3) / 1e9,
+                                    "frac": pass_bytes / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "pass_over_floor": pass_ms / floor_ms,
+                                    "what": "the pass's grid, rows, chunks and loads without its "
+                                            "arithmetic (spec_verify_stream_probe)"}},
         "step_roofline": {"achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
                           "scope": "algorithmic bytes of the whole step / step time",
                           "ms_per_step_with_pass_events": ms_with_events},

@@ -30,7 +30,7 @@ SV_ERR_DRAFT_MASS = 8
 SV_ERR_NO_DRAFT = 16
 
 EXPORTED = ("spec_verify", "spec_verify_workspace_size", "spec_verify_row_stats",
-            "spec_verify_uniforms", "spec_verify_status_str")
+            "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_status_str")
 
 
 class SpecVerifyError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_row_stats.restype = i32
     lib.spec_verify_uniforms.argtypes = [u64, i32, i32, P, P]
     lib.spec_verify_uniforms.restype = i32
+    lib.spec_verify_stream_probe.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
+    lib.spec_verify_stream_probe.restype = i32
     lib.spec_verify_status_str.argtypes = [i32]
     lib.spec_verify_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -236,6 +238,23 @@ def row_stats(logits: torch.Tensor, temperature, *, stream=None):
         _ptr(logits), rows, V, code, _ptr(temperature), _ptr(mx), _ptr(ls), _ptr(am), _ptr(ws),
         ws.numel(), _stream(stream)))
     return mx, ls, am
+
+
+def stream_probe(target: torch.Tensor, draft, *, sink=None, events=None, stream=None) -> None:
+    """The streaming pass over these logits with its arithmetic taken out (a
+    measurement aid: its duration is the read floor of the pass).  `events`:
+    optional (begin, end) torch.cuda.Event pair stamped with the kernel's
+    start and end."""
+    B, K1, V = target.shape
+    code = _dtype_code(target)
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=target.device)
+    b_ev = e_ev = None
+    if events is not None:
+        b_ev, e_ev = events[0].cuda_event, events[1].cuda_event
+    _check(load_library().spec_verify_stream_probe(
+        _ptr(target), _ptr(draft) if draft is not None else None, B, K1 - 1, V, code, _ptr(sink),
+        b_ev, e_ev, _stream(stream)))
 
 
 def uniforms(seed: int, B: int, P: int, *, device="cuda", stream=None) -> torch.Tensor:

@@ -211,6 +211,40 @@ int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+int32_t spec_verify_stream_probe(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
+                                 int32_t V, int32_t dtype, uint32_t *sink, void *begin, void *end,
+                                 void *stream)
+{
+    if (B < 0 || K < 0 || K > sv::kMaxK || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !sink) return SV_EINVAL;
+    const size_t elt = dtype == SV_F32 ? 4 : 2;
+    if (((uintptr_t)target_logits % elt) || (draft_logits && ((uintptr_t)draft_logits % elt)))
+        return SV_EINVAL;
+    sv::Plan p;
+    if (!sv::make_plan(B, K, V, dtype, &p)) return SV_EINVAL;
+    for (int32_t b0 = 0; b0 < B; b0 += p.sB) {
+        const int32_t nb = std::min(p.sB, B - b0);
+        sv::Args a = {};
+        a.B = nb;
+        a.K = K;
+        a.V = V;
+        a.R = p.R;
+        a.nvec = p.nvec;
+        a.nc = p.nc;
+        a.cvec = p.cvec;
+        a.dtype = dtype;
+        a.row_bytes = p.row_bytes;
+        a.target = static_cast<const char *>(target_logits) + (int64_t)b0 * (K + 1) * p.row_bytes;
+        a.draft = draft_logits ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
+                               : nullptr;
+        sv::launch_stream_probe(a, sink, static_cast<hipStream_t>(stream),
+                                b0 == 0 ? static_cast<hipEvent_t>(begin) : nullptr,
+                                b0 == 0 ? static_cast<hipEvent_t>(end) : nullptr);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 int32_t spec_verify_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, void *stream)
 {
     if (B < 0 || P < 0) return SV_EINVAL;

@@ -98,5 +98,6 @@ struct Args {
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 void launch_rowstats(const Args &a, hipStream_t s);
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s);
+void launch_stream_probe(const Args &a, uint32_t *sink, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 
 }  // namespace sv

@@ -1021,6 +1021,38 @@ __global__ __launch_bounds__(64) void rowstats_finish_kernel(const Args a)
     }
 }
 
+// The streaming pass's grid, rows, chunks, loads and tiles with its
+// arithmetic taken out (each thread folds its vectors into one word): the
+// floor that pass is measured against.  `sink` is written for one fold value
+// in 2^32 only, which keeps the loads.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void stream_probe_kernel(const Args a, uint32_t *sink)
+{
+    const int rl = a.draft ? a.R : a.K + 1;
+    const int chunk = blockIdx.x % a.nc;
+    const int b = (blockIdx.x / a.nc) / rl;
+    const int j = blockIdx.x / a.nc - b * rl;
+    const bool is_draft = j > a.K;
+    const int i = is_draft ? j - (a.K + 1) : j;
+    const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
+    const int q0 = chunk * a.cvec;
+    const int q1 = min(a.nvec, q0 + a.cvec);
+    uint32_t acc = 0;
+    auto fold = [&](uint4 (&t)[kLoads], int) {
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) acc ^= t[u].x ^ t[u].y ^ t[u].z ^ t[u].w;
+    };
+    uint4 r[kLoads];
+    if (((uintptr_t)row & 15) == 0) {
+        issue_tile<DT, true>(row, q0, q1, a.V, r);
+        stream_chunk<DT, true>(row, q0, q1, a.V, r, fold);
+    } else {
+        issue_tile<DT, false>(row, q0, q1, a.V, r);
+        stream_chunk<DT, false>(row, q0, q1, a.V, r, fold);
+    }
+    if (acc == 0x9E3779B9u) *sink = acc;
+}
+
 __global__ void uniforms_kernel(uint64_t seed, int32_t B, int32_t P, float *out)
 {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1067,6 +1099,15 @@ void launch_rowstats(const Args &a, hipStream_t s)
     if (a.dtype == SV_F32) stats_kernel<0, false><<<grid, kBlock, 0, s>>>(a);
     else stats_kernel<1, false><<<grid, kBlock, 0, s>>>(a);
     rowstats_finish_kernel<<<(unsigned)a.B, 64, 0, s>>>(a);
+}
+
+void launch_stream_probe(const Args &a, uint32_t *sink, hipStream_t s, hipEvent_t begin, hipEvent_t end)
+{
+    const unsigned grid = (unsigned)((int64_t)a.B * (a.draft ? a.R : a.K + 1) * a.nc);
+    if (a.dtype == SV_F32)
+        hipExtLaunchKernelGGL(stream_probe_kernel<0>, dim3(grid), dim3(kBlock), 0, s, begin, end, 0, a, sink);
+    else
+        hipExtLaunchKernelGGL(stream_probe_kernel<1>, dim3(grid), dim3(kBlock), 0, s, begin, end, 0, a, sink);
 }
 
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s)

@@ -142,6 +142,21 @@ int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32
  */
 int32_t spec_verify_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, void *stream);
 
+/*
+ * Measurement aid: the streaming pass of spec_verify for these arguments
+ * (same grid, rows, chunks, 16-byte loads and tiles, every target row and,
+ * when draft_logits is not NULL, every draft row) with its arithmetic taken
+ * out, so that its duration is the read floor the pass runs against.
+ *   sink         one device uint32; written only for one input pattern in
+ *                2^32 (it keeps the loads), so its contents are meaningless
+ *   begin, end   hipEvent_t or NULL: stamped with the start and end of the
+ *                first sub-batch's kernel
+ * Validation as for spec_verify (no workspace).  Returns after enqueuing.
+ */
+int32_t spec_verify_stream_probe(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
+                                 int32_t V, int32_t dtype, uint32_t *sink, void *begin, void *end,
+                                 void *stream);
+
 /* Static description of a status code. */
 const char *spec_verify_status_str(int32_t status);
 

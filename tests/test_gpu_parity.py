@@ -429,6 +429,25 @@ def test_batch_beyond_one_sub_batch(sv, oracle_mod):
             uniform=lambda b, pos, pur: oracle_mod.uniform(5, b, pos, pur)).check()
 
 
+def test_stream_probe_runs_and_is_timed(sv):
+    """The read-floor probe (a measurement aid) enqueues, stamps its events and
+    leaves the logits untouched."""
+    rng = np.random.default_rng(11)
+    B, K, V = 4, 3, 10007
+    tgt, drf, tok = _random_case(rng, B, K, V)
+    for dtype in ("fp32", "bf16"):
+        inp = _inputs_from_numpy(tgt, drf, tok, np.ones(B, np.float32), 1.0, dtype)
+        before = inp["target"].clone()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
+        ev[1].record()
+        for draft in (inp["draft"], None):
+            sv.stream_probe(inp["target"], draft, events=ev)
+            torch.cuda.synchronize()
+            assert ev[0].elapsed_time(ev[1]) > 0.0
+        assert torch.equal(before, inp["target"])
+
+
 def test_empty_batch(sv):
     t = torch.empty((0, 3, 10), dtype=torch.float32, device="cuda")
     d = torch.empty((0, 2, 10), dtype=torch.float32, device="cuda")
