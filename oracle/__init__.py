@@ -31,6 +31,7 @@ ERR_TEMPERATURE = 2
 ERR_ROW = 4
 ERR_DRAFT_MASS = 8
 ERR_NO_DRAFT = 16
+ERR_DRAFT_LEN = 32
 
 _lib = None
 
@@ -73,6 +74,9 @@ def _load():
     lib.oracle_draft_logprobs.restype = i32
     lib.oracle_spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f64,
                                        P, P, P, P, P, P, P, P, P, i32]
+    lib.oracle_spec_verify_ragged.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, f64,
+                                              P, P, P, P, P, P, P, P, P, P, i32]
+    lib.oracle_spec_verify_ragged.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
     lib.oracle_spec_verify.restype = i32
@@ -157,7 +161,7 @@ def max_threads() -> int:
 
 def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray, seed: int,
                 temperature, beta: float = 1.0, nthreads: int = 0,
-                seq_ids: np.ndarray | None = None) -> dict:
+                seq_ids: np.ndarray | None = None, draft_len: np.ndarray | None = None) -> dict:
     """Run the oracle on a whole batch.
 
     target: [B, K+1, V] float32 or uint16 (bf16 bits); draft: [B, K, V] same
@@ -167,6 +171,9 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
     [B, K], residual_mass / margin_bonus / seq_error [B], and error (int).
     seq_ids [B] gives the global sequence index each row's uniforms are keyed
     by (default 0..B-1), so a sample of a larger batch can be verified alone.
+    draft_len [B] (default K for every sequence) gives ragged draft lengths
+    K_b <= K; draft_conf [B, K] is the draft confidence max_v p_d (NaN past
+    K_b, for greedy and for failed sequences).
     """
     lib = _load()
     t_raw, dt = _as_raw(target)
@@ -195,11 +202,16 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
         "margin_accept": np.zeros((B, K), dtype=np.float64),
         "margin_bonus": np.zeros(B, dtype=np.float64),
         "seq_error": np.zeros(B, dtype=np.int32),
+        "draft_conf": np.zeros((B, K), dtype=np.float64),
     }
-    err = lib.oracle_spec_verify(
-        _ptr(t_raw), _ptr(d_raw), _ptr(tok), B, K, V, dt, int(seed) & (2**64 - 1), _ptr(temp),
-        float(beta), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["p_target"]),
-        _ptr(res["p_draft"]), _ptr(res["residual_mass"]), _ptr(res["margin_accept"]),
-        _ptr(res["margin_bonus"]), _ptr(res["seq_error"]), _ptr(seq_ids), int(nthreads))
+    if draft_len is not None:
+        draft_len = np.ascontiguousarray(np.asarray(draft_len, dtype=np.int32))
+        assert draft_len.shape == (B,)
+    err = lib.oracle_spec_verify_ragged(
+        _ptr(t_raw), _ptr(d_raw), _ptr(tok), _ptr(draft_len), B, K, V, dt, int(seed) & (2**64 - 1),
+        _ptr(temp), float(beta), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]),
+        _ptr(res["p_target"]), _ptr(res["p_draft"]), _ptr(res["residual_mass"]),
+        _ptr(res["margin_accept"]), _ptr(res["margin_bonus"]), _ptr(res["seq_error"]),
+        _ptr(res["draft_conf"]), _ptr(seq_ids), int(nthreads))
     res["error"] = int(err)
     return res

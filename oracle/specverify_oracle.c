@@ -37,7 +37,15 @@
  *  - both softmaxes use the same per-sequence temperature T; T == 0 is greedy;
  *  - beta multiplies the probabilities of the 4 largest draft logits (ties by
  *    lower token id) and the draft law is renormalised; beta == 1 is off;
- *  - a draft token outside [0, V) is rejected (ratio 0) and flagged.
+ *  - a draft token outside [0, V) is rejected (ratio 0) and flagged;
+ *  - ragged draft lengths (Kangaroo's second early exit stops drafting once
+ *    the draft's confidence falls below a threshold, so a round carries
+ *    K_b <= K drafts): sequence b verifies positions 0..K_b-1 and draws the
+ *    bonus from target row K_b after K_b acceptances, with the uniforms keyed
+ *    exactly as for K = K_b; rows past K_b are never read;
+ *  - the draft confidence of position i is max_v p_d(v) of draft row i at the
+ *    sequence temperature, before the beta re-weighting (NaN for greedy
+ *    sequences, whose draft rows are not read).
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +66,7 @@
 #define OR_ERR_ROW 4         /* a row whose maximum logit is not finite   */
 #define OR_ERR_DRAFT_MASS 8  /* beta re-weighting left zero draft mass    */
 #define OR_ERR_NO_DRAFT 16   /* T > 0 and K > 0 but no draft logits given */
+#define OR_ERR_DRAFT_LEN 32  /* a ragged draft length outside [0, K]       */
 
 /* ------------------------------------------------------------------ */
 /* Philox4x32-10 (SC'11): 10 rounds of a multiply/xor S-box; the 2-word key
@@ -272,6 +281,8 @@ typedef struct {
     double *margin_bonus;     /* [B]      or NULL */
     int32_t *seq_error;       /* [B]      or NULL */
     const int32_t *seq_ids;   /* [B] global sequence index used by the uniforms, or NULL */
+    const int32_t *draft_len; /* [B] drafts of each sequence (K_b <= K), or NULL for K */
+    double *draft_conf;       /* [B, K]   or NULL */
 } or_call;
 
 static const void *or_row_ptr(const void *base, int dtype, size_t row, int32_t V)
@@ -290,6 +301,7 @@ static void or_fail_sequence(const or_call *c, int32_t b)
         if (c->p_target) c->p_target[(size_t)b * c->K + i] = NAN;
         if (c->p_draft) c->p_draft[(size_t)b * c->K + i] = NAN;
         if (c->margin_accept) c->margin_accept[(size_t)b * c->K + i] = NAN;
+        if (c->draft_conf) c->draft_conf[(size_t)b * c->K + i] = NAN;
     }
     if (c->residual_mass) c->residual_mass[b] = NAN;
     if (c->margin_bonus) c->margin_bonus[b] = NAN;
@@ -297,21 +309,29 @@ static void or_fail_sequence(const or_call *c, int32_t b)
 
 static int or_verify_sequence(const or_call *c, int32_t b)
 {
-    const int32_t K = c->K, V = c->V;
+    const int32_t Kr = c->K, V = c->V; /* row layout: K + 1 target rows, K draft rows */
     int err = 0;
-    int32_t *out = c->out_tokens + (size_t)b * (K + 1);
-    const int32_t *x = c->tokens + (size_t)b * K;
+    int32_t *out = c->out_tokens + (size_t)b * (Kr + 1);
+    const int32_t *x = c->tokens + (size_t)b * Kr;
     const uint32_t gb = c->seq_ids ? (uint32_t)c->seq_ids[b] : (uint32_t)b;
     const double nan = NAN;
 
-    for (int32_t j = 0; j <= K; ++j) out[j] = -1;
-    for (int32_t i = 0; i < K; ++i) {
-        if (c->p_target) c->p_target[(size_t)b * K + i] = nan;
-        if (c->p_draft) c->p_draft[(size_t)b * K + i] = nan;
-        if (c->margin_accept) c->margin_accept[(size_t)b * K + i] = nan;
+    for (int32_t j = 0; j <= Kr; ++j) out[j] = -1;
+    for (int32_t i = 0; i < Kr; ++i) {
+        if (c->p_target) c->p_target[(size_t)b * Kr + i] = nan;
+        if (c->p_draft) c->p_draft[(size_t)b * Kr + i] = nan;
+        if (c->margin_accept) c->margin_accept[(size_t)b * Kr + i] = nan;
+        if (c->draft_conf) c->draft_conf[(size_t)b * Kr + i] = nan;
     }
     if (c->residual_mass) c->residual_mass[b] = nan;
     if (c->margin_bonus) c->margin_bonus[b] = nan;
+
+    /* this sequence's drafts: positions 0..K-1 are verified, row K is the bonus row */
+    const int32_t K = c->draft_len ? c->draft_len[b] : Kr;
+    if (K < 0 || K > Kr) {
+        or_fail_sequence(c, b);
+        return OR_ERR_DRAFT_LEN;
+    }
 
     double T = (double)c->temperature[b];
     if (!(T >= 0.0) || isinf(T)) {
@@ -324,7 +344,7 @@ static int or_verify_sequence(const or_call *c, int32_t b)
          * mismatch (or position K) emits the target argmax.                 */
         int32_t n = K;
         for (int32_t i = 0; i <= K; ++i) {
-            const void *row = or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + i, V);
+            const void *row = or_row_ptr(c->target, c->dtype, (size_t)b * (Kr + 1) + i, V);
             if (!isfinite(oracle_row_max(row, c->dtype, V))) {
                 or_fail_sequence(c, b);
                 return err | OR_ERR_ROW;
@@ -348,14 +368,24 @@ static int or_verify_sequence(const or_call *c, int32_t b)
         return OR_ERR_NO_DRAFT;
     }
 
+    /* Draft confidence of each drafted position: max_v p_d(v) = exp(m/T - L),
+     * before any beta re-weighting (every drafted row, reached or not). */
+    if (c->draft_conf)
+        for (int32_t i = 0; i < K; ++i) {
+            const void *row = or_row_ptr(c->draft, c->dtype, (size_t)b * Kr + i, V);
+            double m = oracle_row_max(row, c->dtype, V);
+            c->draft_conf[(size_t)b * Kr + i] =
+                isfinite(m) ? exp(m / T - oracle_row_lognorm(row, c->dtype, V, T)) : nan;
+        }
+
     /* Sampling: accept x_i iff u_i <= ratio_i = p_t(x_i) / p_d'(x_i). */
     int weighted = c->beta < 1.0;
     int32_t n = K;
     or_row rt, rd;
     for (int32_t i = 0; i < K; ++i) {
-        int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + i, V),
+        int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (Kr + 1) + i, V),
                            c->dtype, V, T, 0, 1.0);
-        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * K + i, V), c->dtype, V,
+        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * Kr + i, V), c->dtype, V,
                         T, weighted, c->beta);
         if (e) {
             or_fail_sequence(c, b);
@@ -368,13 +398,13 @@ static int or_verify_sequence(const or_call *c, int32_t b)
         } else {
             double lpt = or_logprob(&rt, x[i]);
             double lpd = or_logprob(&rd, x[i]);
-            if (c->p_target) c->p_target[(size_t)b * K + i] = exp(lpt);
-            if (c->p_draft) c->p_draft[(size_t)b * K + i] = exp(lpd);
+            if (c->p_target) c->p_target[(size_t)b * Kr + i] = exp(lpt);
+            if (c->p_draft) c->p_draft[(size_t)b * Kr + i] = exp(lpd);
             /* a draft token the draft law gives zero mass cannot be rejected */
             ratio = (lpd == -INFINITY) ? INFINITY : exp(lpt - lpd);
         }
         double u = oracle_uniform(c->seed, gb, (uint32_t)i, OR_ACCEPT);
-        if (c->margin_accept) c->margin_accept[(size_t)b * K + i] = fabs(u - ratio);
+        if (c->margin_accept) c->margin_accept[(size_t)b * Kr + i] = fabs(u - ratio);
         if (u <= ratio) {
             out[i] = x[i];
             continue;
@@ -385,10 +415,10 @@ static int or_verify_sequence(const or_call *c, int32_t b)
 
     /* Residual law at position n: max(p_t - p_d', 0) after a rejection,
      * the target row K itself after K acceptances.                        */
-    int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (K + 1) + n, V), c->dtype,
+    int e = or_prepare(&rt, or_row_ptr(c->target, c->dtype, (size_t)b * (Kr + 1) + n, V), c->dtype,
                        V, T, 0, 1.0);
     if (n < K)
-        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * K + n, V), c->dtype, V, T,
+        e |= or_prepare(&rd, or_row_ptr(c->draft, c->dtype, (size_t)b * Kr + n, V), c->dtype, V, T,
                         weighted, c->beta);
     if (e) {
         or_fail_sequence(c, b);
@@ -449,16 +479,17 @@ static int or_verify_sequence(const or_call *c, int32_t b)
 /* Verify every sequence of a batch.  Returns the OR of the error bits.
  * nthreads <= 0 uses the OpenMP default; sequences are independent, so the
  * result does not depend on the thread count.                              */
-int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t *tokens,
-                           int32_t B, int32_t K, int32_t V, int32_t dtype, uint64_t seed,
-                           const float *temperature, double beta, int32_t *accepted_len,
-                           int32_t *out_tokens, double *p_target, double *p_draft,
-                           double *residual_mass, double *margin_accept, double *margin_bonus,
-                           int32_t *seq_error, const int32_t *seq_ids, int32_t nthreads)
+int32_t oracle_spec_verify_ragged(const void *target, const void *draft, const int32_t *tokens,
+                                  const int32_t *draft_len, int32_t B, int32_t K, int32_t V,
+                                  int32_t dtype, uint64_t seed, const float *temperature,
+                                  double beta, int32_t *accepted_len, int32_t *out_tokens,
+                                  double *p_target, double *p_draft, double *residual_mass,
+                                  double *margin_accept, double *margin_bonus, int32_t *seq_error,
+                                  double *draft_conf, const int32_t *seq_ids, int32_t nthreads)
 {
     or_call c = {target, draft, tokens, B, K, V, dtype, seed, temperature, beta,
                  accepted_len, out_tokens, p_target, p_draft, residual_mass,
-                 margin_accept, margin_bonus, seq_error, seq_ids};
+                 margin_accept, margin_bonus, seq_error, seq_ids, draft_len, draft_conf};
     int32_t all_err = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -470,6 +501,20 @@ int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t 
         all_err |= e;
     }
     return all_err;
+}
+
+/* The batch with every sequence drafting K tokens. */
+int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t *tokens,
+                           int32_t B, int32_t K, int32_t V, int32_t dtype, uint64_t seed,
+                           const float *temperature, double beta, int32_t *accepted_len,
+                           int32_t *out_tokens, double *p_target, double *p_draft,
+                           double *residual_mass, double *margin_accept, double *margin_bonus,
+                           int32_t *seq_error, const int32_t *seq_ids, int32_t nthreads)
+{
+    return oracle_spec_verify_ragged(target, draft, tokens, NULL, B, K, V, dtype, seed, temperature,
+                                     beta, accepted_len, out_tokens, p_target, p_draft,
+                                     residual_mass, margin_accept, margin_bonus, seq_error, NULL,
+                                     seq_ids, nthreads);
 }
 
 /* Full draft log-law ln p_d'(v) of one row (for invariant checks). */

@@ -390,3 +390,125 @@ def test_results_do_not_depend_on_thread_count(oracle_mod):
         assert np.array_equal(a[key], b[key])
     for key in ("p_target", "p_draft", "residual_mass"):
         assert np.array_equal(a[key], b[key], equal_nan=True)
+
+
+# --------------------------------------------------------------------------
+# Ragged draft lengths (K: the drafter stops early, so a round carries
+# K_b <= K drafts) and the exported draft confidence.
+
+def _ragged_batch(rng, B, K, V, dtype):
+    tgt = (rng.normal(size=(B, K + 1, V)) * 2).astype(np.float32)
+    drf = (tgt[:, :K] + 0.6 * rng.normal(size=(B, K, V))).astype(np.float32)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    am = drf.argmax(axis=2)
+    tok = np.where(rng.random((B, K)) < 0.5, am, tok).astype(np.int32)
+    kb = rng.integers(0, K + 1, size=B).astype(np.int32)
+    # rows past a sequence's drafts must never be read: poison them
+    for b in range(B):
+        tgt[b, kb[b] + 1:] = np.nan
+        drf[b, kb[b]:] = np.nan
+    if dtype == "bf16":
+        return to_bf16_bits(tgt), to_bf16_bits(drf), tok, kb
+    return tgt, drf, tok, kb
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("beta", [1.0, 0.5])
+def test_ragged_sequence_equals_its_truncation(oracle_mod, dtype, beta):
+    """Pin (ragged lengths reduce to the plain case): sequence b with K_b
+    drafts gives exactly what the K = K_b verify gives on its truncated rows
+    (same uniforms: keyed by b, position and purpose), greedy and sampling,
+    and never reads the rows past K_b (they hold NaN here)."""
+    rng = np.random.default_rng(61 if dtype == "fp32" else 62)
+    B, K, V = 40, 5, 300
+    tgt, drf, tok, kb = _ragged_batch(rng, B, K, V, dtype)
+    temps = rng.choice([0.0, 0.6, 1.0, 1.4], size=B).astype(np.float32)
+    res = oracle_mod.spec_verify(tgt, drf, tok, 9, temps, beta, draft_len=kb)
+    assert res["error"] & ~oracle_mod.ERR_TOKEN == 0
+    for b in range(B):
+        k = int(kb[b])
+        one = oracle_mod.spec_verify(tgt[b:b + 1, :k + 1], drf[b:b + 1, :k], tok[b:b + 1, :k], 9,
+                                     temps[b:b + 1], beta, seq_ids=np.array([b]))
+        assert res["accepted_len"][b] == one["accepted_len"][0]
+        assert list(res["out_tokens"][b, :k + 1]) == list(one["out_tokens"][0])
+        assert np.all(res["out_tokens"][b, k + 1:] == -1)
+        assert res["seq_error"][b] == one["seq_error"][0]
+        for key in ("p_target", "p_draft", "margin_accept", "draft_conf"):
+            assert np.array_equal(res[key][b, :k], one[key][0], equal_nan=True), key
+            assert np.all(np.isnan(res[key][b, k:])), key
+        for key in ("residual_mass", "margin_bonus"):
+            assert np.array_equal(res[key][b:b + 1], one[key], equal_nan=True), key
+
+
+def test_ragged_length_out_of_range_fails_the_sequence(oracle_mod):
+    rng = np.random.default_rng(63)
+    B, K, V = 4, 3, 64
+    tgt = rng.normal(size=(B, K + 1, V)).astype(np.float32)
+    drf = rng.normal(size=(B, K, V)).astype(np.float32)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    res = oracle_mod.spec_verify(tgt, drf, tok, 0, 1.0, 1.0, draft_len=np.array([3, -1, 4, 0]))
+    assert list(res["seq_error"]) == [0, oracle_mod.ERR_DRAFT_LEN, oracle_mod.ERR_DRAFT_LEN, 0]
+    assert np.all(res["out_tokens"][1:3] == -1) and np.all(res["accepted_len"][1:3] == 0)
+    # K_b = 0: no draft to test, the bonus comes from target row 0
+    assert res["accepted_len"][3] == 0 and res["out_tokens"][3, 0] >= 0
+    assert np.all(res["out_tokens"][3, 1:] == -1)
+
+
+@pytest.mark.slow
+def test_ragged_output_law_chi2(oracle_mod):
+    """Pin (closed-form law per sequence, K): with drafts drawn from the draft
+    law and each trial drafting K_b in {0, 1, 2} of K = 2 positions, the
+    token emitted at every reached position i <= K_b follows p_i (chi-square
+    p > 0.01), the accept probability at i < K_b is sum_v min(p_i, q_i), and
+    a trial stops at K_b at the latest."""
+    rng = np.random.default_rng(64)
+    V, K, T, beta = 10, 2, 0.8, 0.5
+    tgt, drf = _fixed_rows(rng, V, K)
+    tz, dz = exact_values(tgt), exact_values(drf)
+    Tq = float(np.float32(T))
+    p = [softmax(tz[i], Tq) for i in range(K + 1)]
+    q = [draft_law(dz[i], Tq, beta) for i in range(K)]
+    ntrials = 600_000
+    tokens = np.stack([sample_categorical(rng, q[i], ntrials) for i in range(K)], axis=1)
+    kb = rng.integers(0, K + 1, size=ntrials).astype(np.int32)
+    target = np.ascontiguousarray(np.broadcast_to(tgt, (ntrials,) + tgt.shape))
+    draft = np.ascontiguousarray(np.broadcast_to(drf, (ntrials,) + drf.shape))
+    res = oracle_mod.spec_verify(target, draft, tokens.astype(np.int32), 31, np.float32(T), beta,
+                                 draft_len=kb)
+    assert res["error"] == 0
+    n, out = res["accepted_len"], res["out_tokens"]
+    assert np.all(n <= kb)
+    for k in range(K + 1):
+        grp = kb == k
+        for i in range(k + 1):
+            reached = grp & (n >= i)
+            y = out[reached, i]
+            assert np.all(y >= 0)
+            assert chi2_pvalue(np.bincount(y, minlength=V), p[i]) > 0.01, (k, i)
+            if i < k:
+                alpha = np.minimum(p[i], q[i]).sum()
+                assert binom_pvalue(int((n[reached] > i).sum()), int(reached.sum()), alpha) > 0.01
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_draft_confidence_is_the_softmax_maximum(oracle_mod, dtype):
+    """Pin (library routine): the exported draft confidence of position i is
+    max_v softmax(z_d / T) of draft row i (scipy), before the beta
+    re-weighting, for every drafted position (reached or not); NaN past K_b,
+    for greedy sequences and for failed ones."""
+    rng = np.random.default_rng(65)
+    B, K, V = 12, 4, 777
+    tgt, drf, tok, kb = _ragged_batch(rng, B, K, V, dtype)
+    temps = np.array([0.5, 1.0, 1.7, 0.0] * 3, dtype=np.float32)
+    temps[5] = -1.0  # invalid: the sequence fails
+    for beta in (1.0, 0.3):
+        res = oracle_mod.spec_verify(tgt, drf, tok, 4, temps, beta, draft_len=kb)
+        conf = res["draft_conf"]
+        dz = exact_values(drf)
+        for b in range(B):
+            for i in range(K):
+                if i >= kb[b] or temps[b] <= 0.0:
+                    assert np.isnan(conf[b, i]), (b, i)
+                    continue
+                want = softmax(dz[b, i], float(np.float32(temps[b]))).max()
+                assert abs(conf[b, i] - want) <= 1e-12 * want, (b, i, conf[b, i], want)
