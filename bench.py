@@ -98,6 +98,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ragged", action="store_true",
+                    help="ragged draft lengths K_b ~ U{0..K} per sequence (spec_verify_ragged)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="instead, run torch copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -111,7 +113,7 @@ def main() -> int:
     import torch
 
     import draft_token_verification_03_amd as sv
-    from workload import WORKLOADS, make_inputs
+    from workload import WORKLOADS, make_inputs, ragged_lengths, ragged_rows
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -131,6 +133,15 @@ def main() -> int:
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
     base = make_inputs(w, seed=args.seed, device=dev)
     alg_bytes = w.algorithmic_bytes()
+    draft_len = None
+    logits_per_step = w.B * (w.K + 1) * w.V
+    pass_bytes = w.stream_bytes()
+    if args.ragged:  # only the rows the sequences drafted are read and verified
+        draft_len = ragged_lengths(w, args.seed, dev)
+        rows = ragged_rows(w, draft_len)
+        alg_bytes += (rows - (w.stream_bytes() // (w.V * w.elt_bytes))) * w.V * w.elt_bytes
+        pass_bytes = rows * w.V * w.elt_bytes
+        logits_per_step = (int(draft_len.sum().item()) + w.B) * w.V
     # at least two copies: consecutive steps never read the same bytes, so no
     # step is served from what the previous one left in the Infinity Cache
     reps = max(2, math.ceil(2 * MALL_BYTES / alg_bytes))
@@ -142,7 +153,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     calls = [sv.Verifier(r["target"], None if w.greedy else r["draft"], r["tokens"],
                          r["temperature"], r["beta"], workspace=ws, accepted_len=acc,
-                         out_tokens=out, stream=stream) for r in replicas]
+                         out_tokens=out, stream=stream, draft_len=draft_len) for r in replicas]
 
     for k in range(args.warmup):
         calls[k % reps](args.seed + k)
@@ -183,23 +194,21 @@ def main() -> int:
     # chunks and loads with its arithmetic taken out, over the same replicas,
     # stamped the same way.
     sink = torch.empty(1, dtype=torch.int32, device=dev)
-    for k in range(args.warmup):
+    for k in range(0 if args.ragged else args.warmup):
         r = replicas[k % reps]
         sv.stream_probe(r["target"], None if w.greedy else r["draft"], sink=sink, stream=stream)
     torch.cuda.synchronize()
-    for k in range(args.steps):
+    for k in range(0 if args.ragged else args.steps):
         r = replicas[k % reps]
         sv.stream_probe(r["target"], None if w.greedy else r["draft"], sink=sink, events=pass_ev[k],
                         stream=stream)
     torch.cuda.synchronize()
-    floor_ms = sum(e0.elapsed_time(e1) for e0, e1 in pass_ev) / args.steps
+    floor_ms = None if args.ragged else sum(e0.elapsed_time(e1) for e0, e1 in pass_ev) / args.steps
 
-    logits_per_step = w.B * (w.K + 1) * w.V
     value = logits_per_step / (ms * 1e-3)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    pass_bytes = w.stream_bytes()
     pass_achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    traffic = None if args.ragged else load_traffic(args.workload)
     rec = {
         "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
         "value": value,
@@ -213,7 +222,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.tag(), "B": w.B, "K": w.K, "V": w.V,
+        "config": {"workload": w.tag() + ("_ragged" if args.ragged else ""), "B": w.B, "K": w.K,
+                   "V": w.V, "verified_logits_per_step": logits_per_step,
                    "temperature": w.temperature if w.temperature is not None
                    else f"U[{w.t_lo},{w.t_hi}] per sequence",
                    "beta": w.beta, "replicas_rotated": reps,
@@ -221,12 +231,15 @@ def main() -> int:
                    "rows_per_s": w.B * (w.K + 1) / (ms * 1e-3),
                    "sequences_per_s": w.B / (ms * 1e-3),
                    "mean_accepted_len": mean_acc,
+                   "draft_len": (f"U{{0..{w.K}}} per sequence, mean "
+                                 f"{float(draft_len.float().mean().item()):.3f}"
+                                 if draft_len is not None else w.K),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "stats_kernel (streaming pass)", "kernel_ms": pass_ms,
                      "algorithmic_bytes_per_launch": pass_bytes,
-                     "read_floor": {"kernel_ms": floor_ms,
+                     "read_floor": None if floor_ms is None else {"kernel_ms": floor_ms,
                                     "achieved": pass_bytes / (floor_ms * 1e-3) / 1e9,
                                     "frac": pass_bytes / (floor_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                     "pass_over_floor": pass_ms / floor_ms,

@@ -28,8 +28,9 @@ SV_ERR_TEMPERATURE = 2
 SV_ERR_ROW = 4
 SV_ERR_DRAFT_MASS = 8
 SV_ERR_NO_DRAFT = 16
+SV_ERR_DRAFT_LEN = 32
 
-EXPORTED = ("spec_verify", "spec_verify_workspace_size", "spec_verify_row_stats",
+EXPORTED = ("spec_verify", "spec_verify_ragged", "spec_verify_workspace_size", "spec_verify_row_stats",
             "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_status_str")
 
 
@@ -40,7 +41,8 @@ class SpecVerifyError(RuntimeError):
 class _Aux(ctypes.Structure):
     _fields_ = [("p_target", ctypes.c_void_p), ("p_draft", ctypes.c_void_p),
                 ("residual_mass", ctypes.c_void_p), ("error_word", ctypes.c_void_p),
-                ("pass_begin", ctypes.c_void_p), ("pass_end", ctypes.c_void_p)]
+                ("pass_begin", ctypes.c_void_p), ("pass_end", ctypes.c_void_p),
+                ("draft_conf", ctypes.c_void_p)]
 
 
 _lib = None
@@ -62,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f32, P, P, P, sz,
                                 ctypes.POINTER(_Aux), P]
     lib.spec_verify.restype = i32
+    lib.spec_verify_ragged.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, f32, P, P, P, sz,
+                                       ctypes.POINTER(_Aux), P]
+    lib.spec_verify_ragged.restype = i32
     lib.spec_verify_row_stats.argtypes = [P, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.spec_verify_row_stats.restype = i32
     lib.spec_verify_uniforms.argtypes = [u64, i32, i32, P, P]
@@ -124,14 +129,16 @@ class Verifier:
     temperature a float or a [B] float32 tensor (0 = greedy); beta in [0, 1].
     The outputs accepted_len [B] and out_tokens [B, K+1] (int32) are
     allocated unless passed in, and so is the workspace.  With aux=True the
-    diagnostics p_target, p_draft, residual_mass and error_word are written
-    too (error_word is cleared before every call).
+    diagnostics p_target, p_draft, residual_mass, draft_conf and error_word
+    are written too (error_word is cleared before every call).  draft_len, a
+    [B] int32 tensor, gives ragged draft lengths K_b <= K
+    (spec_verify_ragged).
     """
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
                  temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
                  accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
-                 aux: bool = False, stream=None):
+                 aux: bool = False, stream=None, draft_len: torch.Tensor | None = None):
         if target.dim() != 3:
             raise ValueError("target must be [B, K+1, V]")
         B, K1, V = target.shape
@@ -145,6 +152,9 @@ class Verifier:
                 raise ValueError("draft must be a contiguous [B, K, V] tensor of the target's dtype")
         if tokens.shape != (B, K) or tokens.dtype != torch.int32 or not tokens.is_contiguous():
             raise ValueError("tokens must be a contiguous [B, K] int32 tensor")
+        if draft_len is not None and (draft_len.shape != (B,) or draft_len.dtype != torch.int32
+                                      or not draft_len.is_contiguous()):
+            raise ValueError("draft_len must be a contiguous [B] int32 tensor")
         if not torch.is_tensor(temperature):
             temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
         if temperature.shape != (B,) or temperature.dtype != torch.float32:
@@ -159,7 +169,7 @@ class Verifier:
         self.shape = (B, K, V)
         self.accepted_len, self.out_tokens = accepted_len, out_tokens
         # keep every buffer alive for as long as the bound call
-        self._keep = (target, draft, tokens, temperature, workspace)
+        self._keep = (target, draft, tokens, temperature, workspace, draft_len)
         self.aux = None
         self._aux = _Aux()
         if aux:
@@ -168,13 +178,19 @@ class Verifier:
                 "p_draft": torch.empty((B, K), dtype=torch.float32, device=dev),
                 "residual_mass": torch.empty((B,), dtype=torch.float32, device=dev),
                 "error_word": torch.zeros((1,), dtype=torch.int32, device=dev),
+                "draft_conf": torch.empty((B, K), dtype=torch.float32, device=dev),
             }
             self._aux.p_target = self.aux["p_target"].data_ptr()
             self._aux.p_draft = self.aux["p_draft"].data_ptr()
             self._aux.residual_mass = self.aux["residual_mass"].data_ptr()
             self._aux.error_word = self.aux["error_word"].data_ptr()
-        self._fn = load_library().spec_verify
-        self._head = (_ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code)
+            self._aux.draft_conf = self.aux["draft_conf"].data_ptr()
+        if draft_len is None:
+            self._fn = load_library().spec_verify
+            self._head = (_ptr(target), _ptr(draft), _ptr(tokens), B, K, V, code)
+        else:
+            self._fn = load_library().spec_verify_ragged
+            self._head = (_ptr(target), _ptr(draft), _ptr(tokens), _ptr(draft_len), B, K, V, code)
         self._mid = (_ptr(temperature), ctypes.c_float(float(beta)), _ptr(accepted_len),
                      _ptr(out_tokens), _ptr(workspace), workspace.numel())
         self._stream = _stream(stream)
@@ -204,18 +220,20 @@ class Verifier:
 def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
                 seed: int, temperature, beta: float = 1.0, *, workspace: torch.Tensor | None = None,
                 accepted_len: torch.Tensor | None = None, out_tokens: torch.Tensor | None = None,
-                aux: bool = False, stream=None):
+                aux: bool = False, stream=None, draft_len: torch.Tensor | None = None):
     """Verify K drafted tokens per sequence (one call of the C entry point).
 
     Arguments as for Verifier.  Returns (accepted_len [B] int32, out_tokens
     [B, K+1] int32), plus a dict of diagnostics (p_target, p_draft,
-    residual_mass, error_word) if aux=True.  The work is enqueued on `stream`
-    (default: the current stream); a workspace of at least
+    residual_mass, draft_conf, error_word) if aux=True.  The work is enqueued
+    on `stream` (default: the current stream); a workspace of at least
     workspace_size(B, K, V, dtype) bytes may be passed in (e.g. from
-    alloc_workspace) to avoid an allocation per call.
+    alloc_workspace) to avoid an allocation per call.  draft_len [B] int32
+    gives ragged draft lengths (spec_verify_ragged).
     """
     return Verifier(target, draft, tokens, temperature, beta, workspace=workspace,
-                    accepted_len=accepted_len, out_tokens=out_tokens, aux=aux, stream=stream)(seed)
+                    accepted_len=accepted_len, out_tokens=out_tokens, aux=aux, stream=stream,
+                    draft_len=draft_len)(seed)
 
 
 def row_stats(logits: torch.Tensor, temperature, *, stream=None):

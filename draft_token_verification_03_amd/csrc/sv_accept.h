@@ -73,20 +73,16 @@ __device__ __forceinline__ double weighted_norm(double S_rest, const Top4 &t, do
 // the sum over the chunk's other elements, so the mass outside the row's top-4
 // is summed directly (never as S - S_top, which cancels when the top-4 hold
 // nearly all the mass).  A row of one chunk already carries D (the streaming
-// pass forms it).  Returns the row max M, the row top-4 and D, relative to
-// exp2((z - M) c).
+// pass forms it).  Returns the row max M, the row top-4, D and the row's sum
+// before the re-weighting Du, relative to exp2((z - M) c).  (Rows of more
+// than one chunk only.)
 __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp, int nc,
                                                const ExpScale &e, double beta, float &M, Top4 &row_top,
-                                               double &D)
+                                               double &D, double &Du)
 {
     const int lane = threadIdx.x & 63;
     double s_excl;
     merge_sum(p, nc, e, M, s_excl);
-    if (nc == 1) {
-        row_top = tp[0];
-        D = s_excl;
-        return;
-    }
     const double om = (double)row_offset(M, e);
     Top4 t;
     top_clear(t);
@@ -104,7 +100,9 @@ __device__ __forceinline__ void merge_weighted(const RowPart *p, const Top4 *tp,
             if (r.i[k] != INT_MAX && r.v[k] != -INFINITY && !top_has(row_top, r.i[k]))
                 extra += exp_scaled64(r.v[k], om, e.c64);
     }
-    D = weighted_norm(s_excl + wave_sum(extra), row_top, om, e.c64, beta);
+    const double s_rest = s_excl + wave_sum(extra);
+    D = weighted_norm(s_rest, row_top, om, e.c64, beta);
+    Du = weighted_norm(s_rest, row_top, om, e.c64, 1.0);
 }
 
 // ---------------------------------------------------------------------------

@@ -120,7 +120,8 @@ static int32_t validate(const void *target_logits, const void *draft_logits,
 }
 
 static int32_t verify(const void *target_logits, const void *draft_logits,
-                      const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                      const int32_t *draft_tokens, const int32_t *draft_len, int32_t B, int32_t K,
+                      int32_t V, int32_t dtype,
                       uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                       int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                       const sv_aux *aux, void *stream)
@@ -140,6 +141,7 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
         a.draft = draft_logits ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
                                : nullptr;
         a.tokens = draft_tokens ? draft_tokens + (int64_t)b0 * K : nullptr;
+        a.draft_len = draft_len ? draft_len + b0 : nullptr;
         a.temperature = temperature + b0;
         a.seed = seed;
         a.beta = beta;
@@ -151,6 +153,7 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
             a.aux_pt = aux->p_target ? aux->p_target + (int64_t)b0 * K : nullptr;
             a.aux_pd = aux->p_draft ? aux->p_draft + (int64_t)b0 * K : nullptr;
             a.aux_z = aux->residual_mass ? aux->residual_mass + b0 : nullptr;
+            a.aux_conf = aux->draft_conf ? aux->draft_conf + (int64_t)b0 * K : nullptr;
             a.error_word = aux->error_word;
         }
         hipEvent_t begin = nullptr, end = nullptr;
@@ -180,8 +183,21 @@ int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_aux *aux, void *stream)
 {
-    return sv::verify(target_logits, draft_logits, draft_tokens, B, K, V, dtype, seed, temperature,
-                      beta, accepted_len, out_tokens, workspace, workspace_bytes, aux, stream);
+    return sv::verify(target_logits, draft_logits, draft_tokens, nullptr, B, K, V, dtype, seed,
+                      temperature, beta, accepted_len, out_tokens, workspace, workspace_bytes, aux,
+                      stream);
+}
+
+int32_t spec_verify_ragged(const void *target_logits, const void *draft_logits,
+                           const int32_t *draft_tokens, const int32_t *draft_len, int32_t B,
+                           int32_t K, int32_t V, int32_t dtype, uint64_t seed,
+                           const float *temperature, float beta, int32_t *accepted_len,
+                           int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                           const sv_aux *aux, void *stream)
+{
+    return sv::verify(target_logits, draft_logits, draft_tokens, draft_len, B, K, V, dtype, seed,
+                      temperature, beta, accepted_len, out_tokens, workspace, workspace_bytes, aux,
+                      stream);
 }
 
 int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,

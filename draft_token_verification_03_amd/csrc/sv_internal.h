@@ -70,6 +70,7 @@ struct Args {
     const char *target;     // the sub-batch's first target row
     const char *draft;
     const int32_t *tokens;
+    const int32_t *draft_len;   // [B] drafts of each sequence (K_b <= K), or null for K
     const float *temperature;
     int32_t B, K, V, R, nvec, nc, cvec, nslot, gs, ng, spg, dtype;
     int32_t b0;             // index of the sub-batch's first sequence in the call
@@ -85,7 +86,7 @@ struct Args {
     double4 *tope;          // [sB][K][nc] exp2((v - m_c) c) of each chunk top-4 entry (nc > 1)
     SeqState *seq;          // [sB]
     double *slot;           // [sB][nslot] residual mass of each slot
-    float *aux_pt, *aux_pd, *aux_z;
+    float *aux_pt, *aux_pd, *aux_z, *aux_conf;
     int32_t *error_word;    // error bits are OR-ed in
     // row-statistics entry point outputs
     float *rs_max;

@@ -180,8 +180,8 @@ __device__ __forceinline__ const char *draft_row(const Args &a, int b, int i)
 // One (row, chunk) of the streaming pass; the first tile is requested before
 // the temperature is looked at.
 template <int DT, bool TOP, bool ALIGNED>
-__device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int b, int i, bool is_draft,
-                                            int slot_row, int chunk, float T)
+__device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int b, int i, int kb,
+                                            bool is_draft, int slot_row, int chunk, float T)
 {
     __shared__ float lds_f[4 + kWaves * 4];
     __shared__ int lds_i[4 + kWaves * 4];
@@ -193,7 +193,7 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
     // a sampling row's logit at its drafted token, read while the first tile
     // is in flight, saves the accept step a dependent gather
     float zx = 0.f;
-    if (chunk == 0 && i < a.K && threadIdx.x == 0) {
+    if (chunk == 0 && i < kb && threadIdx.x == 0) {
         const int x = a.tokens[(int64_t)b * a.K + i];
         if (x >= 0 && x < a.V) zx = Elt<DT>::scalar(row, x);
     }
@@ -238,6 +238,8 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
                     double q = w + dpp_double<kDppQuadXor1>(w);
                     q += dpp_double<kDppQuadXor2>(q);
                     part.s += (double)a.beta * q;
+                    if (k == 0)  // the top-4 mass itself, for the draft confidence (before beta)
+                        reinterpret_cast<double *>(&a.tope[(int64_t)b * a.K + i])[0] = q;
                 } else {
                     reinterpret_cast<double *>(&a.tope[((int64_t)b * a.K + i) * a.nc + chunk])[k] = w;
                 }
@@ -267,10 +269,15 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
     const int slot_row = b * a.R + j;
     const bool is_draft = j > a.K;
     const int i = is_draft ? j - (a.K + 1) : j;
+    int kb = a.K;
+    if (a.draft_len) {  // ragged drafts: rows past the sequence's are not read
+        kb = a.draft_len[b];
+        if (kb < 0 || kb > a.K || i > kb || (is_draft && i == kb)) return;
+    }
     const float T = a.temperature[b];
     const char *row = is_draft ? draft_row(a, b, i) : target_row(a, b, i);
-    if (((uintptr_t)row & 15) == 0) stats_chunk<DT, TOP, true>(a, row, b, i, is_draft, slot_row, chunk, T);
-    else stats_chunk<DT, TOP, false>(a, row, b, i, is_draft, slot_row, chunk, T);
+    if (((uintptr_t)row & 15) == 0) stats_chunk<DT, TOP, true>(a, row, b, i, kb, is_draft, slot_row, chunk, T);
+    else stats_chunk<DT, TOP, false>(a, row, b, i, kb, is_draft, slot_row, chunk, T);
 }
 
 // ---------------------------------------------------------------------------
@@ -295,6 +302,7 @@ struct AcceptLds {
     float *m;       // [R]
     int *idx;       // [R]
     Top4 *top;      // [K] row top-4 of each weighted draft row
+    double *Su;     // [K] a weighted draft row's sum before the beta re-weighting
     int *flag;      // [K + 1] 1: position stops the scan, 3: and its rows are unusable
     SeqState *st;
 };
@@ -320,6 +328,7 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
     unsigned char *p_m = take(staged ? sizeof(float) * (size_t)R : 0);
     unsigned char *p_idx = take(staged ? sizeof(int) * (size_t)R : 0);
     unsigned char *p_top = take(staged && weighted ? sizeof(Top4) * (size_t)K : 0);
+    unsigned char *p_Su = take(staged && weighted ? sizeof(double) * (size_t)K : 0);
     unsigned char *p_flag = take(sizeof(int) * (size_t)(K + 1));
     unsigned char *p_st = take(sizeof(SeqState));
     if (L) {
@@ -329,6 +338,7 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
         L->m = reinterpret_cast<float *>(p_m);
         L->idx = reinterpret_cast<int *>(p_idx);
         L->top = reinterpret_cast<Top4 *>(p_top);
+        L->Su = reinterpret_cast<double *>(p_Su);
         L->flag = reinterpret_cast<int *>(p_flag);
         L->st = reinterpret_cast<SeqState *>(p_st);
     }
@@ -340,7 +350,7 @@ __host__ __device__ inline size_t accept_lds_layout(int R, int K, int nc, bool w
 // logits at the drafted token, which chunk 0's partials carry.
 struct PosRows {
     float mt, md, zt, zd;
-    double St, D;
+    double St, D, Du;  // Du: the draft row's sum before the beta re-weighting
     int am;  // target argmax (greedy)
     Top4 top;
 };
@@ -387,11 +397,12 @@ __device__ __forceinline__ void merge_rows(const Args &a, int b, float T, bool g
             const int i = r - (K + 1);
             float M;
             Top4 rt4;
-            double D;
-            merge_weighted(p, L.ptop + i * nc, nc, e, (double)a.beta, M, rt4, D);
+            double D, Du;
+            merge_weighted(p, L.ptop + i * nc, nc, e, (double)a.beta, M, rt4, D, Du);
             if (lane == 0) {
                 L.m[r] = M;
                 L.S[r] = D;
+                L.Su[i] = Du;
                 L.top[i] = rt4;
             }
         } else {
@@ -436,7 +447,7 @@ __device__ __forceinline__ void load_position(const Args &a, int b, int i, PosLo
                 pl.d[c] = gd[c];
                 if (a.weighted) {
                     pl.top[c] = gtop[c];
-                    if (nc > 1) pl.tope[c] = gtope[c];
+                    pl.tope[c] = gtope[c];  // one chunk: .x is the row's top-4 mass
                 }
             }
         }
@@ -520,8 +531,11 @@ __device__ __forceinline__ void thread_rows(const PosLoads &pl, int nc, int i, i
     double s;
     thread_merge_sum(pl.d, nc, e, pr.md, s, f);
     if (!weighted || nc == 1) {  // one chunk: the streaming pass formed D
-        if (weighted) pr.top = pl.top[0];
-        pr.D = s;
+        pr.D = pr.Du = s;
+        if (weighted) {
+            pr.top = pl.top[0];
+            pr.Du = s + (1.0 - beta) * pl.tope[0].x;
+        }
         return;
     }
     Top4 t = pl.top[0];
@@ -536,7 +550,9 @@ __device__ __forceinline__ void thread_rows(const PosLoads &pl, int nc, int i, i
             for (int k = 0; k < 4; ++k) extra += top_insert_mass(t, tw, pl.top[c].v[k], pl.top[c].i[k], w[k]);
         }
     pr.top = t;
-    pr.D = (s + extra) + beta * (((tw[0] + tw[1]) + tw[2]) + tw[3]);
+    const double st = ((tw[0] + tw[1]) + tw[2]) + tw[3];
+    pr.D = (s + extra) + beta * st;
+    pr.Du = (s + extra) + st;
 }
 
 // Returns the outcome to every thread; `publish` writes the sequence's
@@ -545,14 +561,17 @@ template <int DT>
 __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const AcceptLds &L, bool publish)
 {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int K = a.K, nc = a.nc;
-    const bool pos = tid <= K;  // this thread stands for position tid
+    const int K = a.K, nc = a.nc;  // K: drafts in the row layout, K + 1 output slots
     const uint32_t gb = (uint32_t)(a.b0 + b);  // Philox keys on the sequence's index in the call
     int32_t *out = a.out_tokens + (int64_t)b * (K + 1);
 
-    // one round trip: temperature, drafted token, and (one chunk per row) the
-    // position's partials
+    // one round trip: temperature, this sequence's draft count, drafted token,
+    // and (a few chunks per row) the position's partials
     const float T = a.temperature[b];
+    const int kb = a.draft_len ? a.draft_len[b] : K;
+    const bool kb_ok = kb >= 0 && kb <= K;
+    const int Kp = kb_ok ? kb : 0;  // positions 0..Kp; position Kp is the bonus row
+    const bool pos = tid <= Kp;     // this thread stands for position tid
     int x = -1;
     if (tid < K) x = a.tokens[(int64_t)b * K + tid];
     PosRows pr;
@@ -565,12 +584,13 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
     const bool weighted = a.weighted && !greedy;
     const bool own = nc <= kThreadMerge;
     PosLoads pl;
-    if (own && pos) load_position(a, b, tid, pl);
+    if (own && tid <= K) load_position(a, b, tid, pl);  // issued before kb is known
     int fail = 0;
-    if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
-    else if (!greedy && K > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
+    if (!kb_ok) fail = SV_ERR_DRAFT_LEN;
+    else if (!temperature_ok(T)) fail = SV_ERR_TEMPERATURE;
+    else if (!greedy && Kp > 0 && a.draft == nullptr) fail = SV_ERR_NO_DRAFT;
     if (own && pos && !fail)
-        thread_rows(pl, nc, tid, K, greedy, weighted, (double)a.beta, make_scale(greedy ? 1.f : T), pr);
+        thread_rows(pl, nc, tid, Kp, greedy, weighted, (double)a.beta, make_scale(greedy ? 1.f : T), pr);
     if (!own && !fail) {
         merge_rows<DT>(a, b, T, greedy, weighted, L);
         if (pos) {
@@ -579,24 +599,27 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
             pr.am = L.idx[tid];
             pr.zt = __int_as_float(L.part[tid * nc].idx);
         }
-        if (tid < K && !greedy) {
+        if (tid < Kp && !greedy) {
             pr.md = L.m[K + 1 + tid];
-            pr.D = L.S[K + 1 + tid];
+            pr.D = pr.Du = L.S[K + 1 + tid];
             pr.zd = __int_as_float(L.part[(K + 1 + tid) * nc].idx);
-            if (weighted) pr.top = L.top[tid];
+            if (weighted) {
+                pr.top = L.top[tid];
+                pr.Du = L.Su[tid];
+            }
         }
     }
 
     // this position: does it stop the scan, and the bonus state if it is n
     int err = fail;
     bool stop = true;
-    float ppt = NAN, ppd = NAN;
+    float ppt = NAN, ppd = NAN, conf = NAN;
     SeqState cs = {};
     cs.mode = 0;
     if (pos && !fail) {
         if (greedy) {
             if (!isfinite(pr.mt)) err = SV_ERR_ROW;
-            stop = err != 0 || tid == K || x != pr.am;
+            stop = err != 0 || tid == Kp || x != pr.am;
         } else {
             const ExpScale e = make_scale(T);
             const float ot = row_offset(pr.mt, e);
@@ -609,7 +632,7 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
             cs.lbeta = (float)a.log2_beta;
 #pragma unroll
             for (int k = 0; k < 4; ++k) cs.top[k] = -1;
-            if (tid < K) {
+            if (tid < Kp) {
                 if (!isfinite(pr.md)) err |= SV_ERR_ROW;
                 else if (!(pr.D > 0.0)) err |= SV_ERR_DRAFT_MASS;
                 const bool x_ok = x >= 0 && x < a.V;
@@ -624,6 +647,9 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
                 cs.mode = 1;
                 cs.o_d = od;
                 cs.k2 = ((double)ot - (double)od) - lq;
+                // draft confidence max_v p_d (before beta): exp2(m c - o_d) / S_d
+                if (a.aux_conf && isfinite(pr.md))
+                    conf = (float)(exp2((double)pr.md * e.c64 - (double)od) / pr.Du);
                 if (weighted) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) cs.top[k] = pr.top.i[k] == INT_MAX ? -1 : pr.top.i[k];
@@ -636,18 +662,18 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
     if (pos) L.flag[tid] = stop ? (err ? 3 : 1) : 0;
     __syncthreads();
 
-    // n: the first position that stops the scan (position K always does)
-    int n = K;
-    for (int g0 = 0; g0 <= K; g0 += 64) {
+    // n: the first position that stops the scan (position Kp always does)
+    int n = Kp;
+    for (int g0 = 0; g0 <= Kp; g0 += 64) {
         const int i = g0 + lane;
-        const uint64_t m = __ballot(i <= K && L.flag[i] != 0);
+        const uint64_t m = __ballot(i <= Kp && L.flag[i] != 0);
         if (m != 0ull) {
             n = g0 + __ffsll((unsigned long long)m) - 1;
             break;
         }
     }
     const bool bad = (L.flag[n] & 2) != 0;  // failed: no outputs but -1
-    if (publish && pos) {
+    if (publish && tid <= K) {  // every output slot, past the sequence's drafts too
         int v = -1;
         if (!bad && tid < n) v = x;
         if (!bad && greedy && tid == n) v = pr.am;
@@ -656,6 +682,7 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
             const bool keep = !bad && !greedy && tid <= n;
             if (a.aux_pt) a.aux_pt[(int64_t)b * K + tid] = keep ? ppt : NAN;
             if (a.aux_pd) a.aux_pd[(int64_t)b * K + tid] = keep ? ppd : NAN;
+            if (a.aux_conf) a.aux_conf[(int64_t)b * K + tid] = (!bad && !greedy) ? conf : NAN;
         }
     }
     if (tid == n) {
@@ -665,7 +692,7 @@ __device__ __forceinline__ SeqState accept_sequence(const Args &a, int b, const 
             st = SeqState{};
             st.mode = 0;
         }
-        if (!bad && n < K && (x < 0 || x >= a.V)) err_bits |= SV_ERR_TOKEN;
+        if (!bad && n < Kp && (x < 0 || x >= a.V)) err_bits |= SV_ERR_TOKEN;
         *L.st = st;
         if (publish) {
             a.seq[b] = st;
@@ -1079,7 +1106,7 @@ static void launch_all(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_
     const size_t lds = accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, nullptr, nullptr);
     residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ng), kBlock, lds, s>>>(a);
     // without draft logits (K > 0) every sequence is greedy or fails: no bonus draw
-    if (a.draft || a.K == 0) bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
+    if (a.draft || a.K == 0 || a.draft_len) bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
 }
 
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)

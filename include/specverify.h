@@ -81,6 +81,7 @@ extern "C" {
 #define SV_ERR_ROW 4            /* a used row has no finite maximum: outputs are -1     */
 #define SV_ERR_DRAFT_MASS 8     /* beta == 0 left a draft row with zero mass: outputs -1 */
 #define SV_ERR_NO_DRAFT 16      /* T > 0 but draft_logits is NULL: outputs are -1       */
+#define SV_ERR_DRAFT_LEN 32     /* a ragged draft length outside [0, K]: outputs are -1 */
 
 /* Optional per-call diagnostics; every field may be NULL. */
 typedef struct sv_aux {
@@ -90,6 +91,11 @@ typedef struct sv_aux {
     int32_t *error_word;  /* [1]    SV_ERR_* bits are OR-ed in: zero it before the call           */
     void *pass_begin;     /* hipEvent_t stamped with the start of the streaming-pass kernel      */
     void *pass_end;       /* and with its end (first sub-batch only): times the dominant kernel  */
+    float *draft_conf;    /* [B, K] draft confidence max_v p_d(v) of each drafted position at the
+                             sequence temperature, before the beta re-weighting (every drafted
+                             position, reached or not); NaN past the sequence's drafts, in greedy
+                             mode and for failed sequences.  Appended last: zero-initialise the
+                             whole struct. */
 } sv_aux;
 
 /*
@@ -120,6 +126,28 @@ int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_aux *aux, void *stream);
+
+/*
+ * The verify step with ragged draft lengths ("Kangaroo: Self-Speculative
+ * Decoding via Shallow Sub-Networks", its second early exit stops drafting
+ * when the draft's confidence falls below a threshold, so a round carries
+ * K_b <= K drafts per sequence):
+ *   draft_len      [B] int32 device array: K_b in [0, K] (out of range:
+ *                  SV_ERR_DRAFT_LEN, the sequence's outputs are -1); NULL
+ *                  means K for every sequence (exactly spec_verify)
+ * The logit tensors keep their [B, K+1, V] and [B, K, V] layouts; sequence b
+ * verifies drafts 0..K_b-1 and, after K_b acceptances, draws its bonus from
+ * target row K_b; rows past those are never read.  out_tokens keeps K+1
+ * slots (-1 after the bonus), uniforms are keyed as for K = K_b, and
+ * draft_logits may be NULL when every sampling sequence has K_b == 0.
+ * Everything else as spec_verify.
+ */
+int32_t spec_verify_ragged(const void *target_logits, const void *draft_logits,
+                           const int32_t *draft_tokens, const int32_t *draft_len, int32_t B,
+                           int32_t K, int32_t V, int32_t dtype, uint64_t seed,
+                           const float *temperature, float beta, int32_t *accepted_len,
+                           int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                           const sv_aux *aux, void *stream);
 
 /*
  * Per-row statistics of `rows` rows of V logits (the streaming pass of the

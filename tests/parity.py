@@ -39,10 +39,15 @@ class Report:
         assert self.flips <= flip_rate * self.decisions + 1, (self.flips, self.decisions)
 
 
+def _draft_len(h, b) -> int:
+    dl = h.get("draft_len")
+    return int(dl[b]) if dl is not None else h["tokens"].shape[1]
+
+
 def _bonus_within_margin(h, b, n, tok_g, u, Z_o, margin) -> bool:
     """Is u within `margin` of the oracle-law CDF interval of token tok_g?"""
     T = float(h["temperature"][b])
-    K = h["tokens"].shape[1]
+    K = _draft_len(h, b)
     tz = exact_values(h["target"][b, n])
     if n < K:
         dz = exact_values(h["draft"][b, n])
@@ -61,9 +66,11 @@ def _bonus_within_margin(h, b, n, tok_g, u, Z_o, margin) -> bool:
 def compare(gpu: dict, orc: dict, h: dict, seed: int, seq_ids=None, margin: float = 1e-6,
             ptol: float = 1e-5, uniform=None) -> Report:
     """gpu: numpy arrays accepted_len, out_tokens (+ optional p_target,
-    p_draft, residual_mass, error_word); orc: oracle.spec_verify result on
-    the same inputs h (numpy host inputs); uniform(b, pos, purpose) gives the
-    oracle's uniforms for the excusal check of bonus draws."""
+    p_draft, residual_mass, draft_conf, error_word); orc: oracle.spec_verify
+    result on the same inputs h (numpy host inputs, with draft_len for ragged
+    calls); uniform(b, pos, purpose) gives the oracle's uniforms for the
+    excusal check of bonus draws.  The draft confidence depends on no
+    decision: it is compared at every position of every sequence."""
     rep = Report()
     B, K1 = orc["out_tokens"].shape
     K = K1 - 1
@@ -74,12 +81,24 @@ def compare(gpu: dict, orc: dict, h: dict, seed: int, seq_ids=None, margin: floa
         n_o, n_g = int(orc["accepted_len"][b]), int(gpu["accepted_len"][b])
         out_o, out_g = orc["out_tokens"][b], gpu["out_tokens"][b]
         tag = f"seq {gb}"
+        Kb = _draft_len(h, b)
+        if "draft_conf" in gpu:
+            for i in range(K):
+                co, cg = orc["draft_conf"][b, i], gpu["draft_conf"][b, i]
+                if np.isnan(co) or np.isnan(cg):
+                    if not (np.isnan(co) and np.isnan(cg)):
+                        rep.failures.append(f"{tag}: draft_conf[{i}] {cg} vs oracle {co}")
+                    continue
+                err = abs(float(cg) - float(co))
+                rep.max_p_err = max(rep.max_p_err, err)
+                if not err <= ptol:
+                    rep.failures.append(f"{tag}: draft_conf[{i}] {cg} vs {co}")
         if orc["seq_error"][b] != 0 or temps[b] == 0.0:
             if n_o != n_g or not np.array_equal(out_o, out_g):
                 rep.failures.append(f"{tag}: exact mismatch n {n_o}/{n_g} out {out_o}/{out_g}")
             rep.decisions += min(n_o + 1, K1)
             continue
-        rep.decisions += (n_o + 1 if n_o < K else K) + 1
+        rep.decisions += (n_o + 1 if n_o < Kb else Kb) + 1
         m = min(n_o, n_g)
         if not np.array_equal(out_g[:m], h["tokens"][b, :m]):
             rep.failures.append(f"{tag}: accepted prefix differs from drafts")

@@ -43,7 +43,7 @@ def run_gpu(sv, inp: dict, seed: int, draft_none: bool = False,
             workspace=None) -> dict:
     acc, out, aux = sv.spec_verify(inp["target"], None if draft_none else inp["draft"],
                                    inp["tokens"], seed, inp["temperature"], inp["beta"], aux=True,
-                                   workspace=workspace)
+                                   workspace=workspace, draft_len=inp.get("draft_len"))
     torch.cuda.synchronize()
     res = {"accepted_len": acc.cpu().numpy(), "out_tokens": out.cpu().numpy()}
     for k, v in aux.items():
@@ -58,7 +58,7 @@ def run_both(sv, oracle_mod, inp: dict, seed: int, ptol: float, draft_none: bool
     if draft_none:
         h["draft"] = None
     o = oracle_mod.spec_verify(h["target"], h["draft"], h["tokens"], seed, h["temperature"],
-                               h["beta"])
+                               h["beta"], draft_len=h.get("draft_len"))
     return compare(g, o, h, seed, ptol=ptol,
                    uniform=lambda b, pos, pur: oracle_mod.uniform(seed, b, pos, pur))
 
@@ -293,6 +293,53 @@ def test_weighted_draft_rows_of_every_shape(sv, oracle_mod, B, V):
             _say(f"weighted shapes B={B} V={V} dtype={dtype} beta={beta}")
             inp = _inputs_from_numpy(tgt, drf, tok, temps, beta, dtype)
             run_both(sv, oracle_mod, inp, seed=B, ptol=_ptol(dtype)).check()
+
+
+@pytest.mark.parametrize("B,V", [(5, 30011), (40, 3001), (300, 2053)])
+def test_ragged_draft_lengths(sv, oracle_mod, B, V):
+    """Ragged draft lengths (spec_verify_ragged): K_b in [0, K] per sequence,
+    mixed greedy and sampling, beta on and off, many, a few and one chunk per
+    row; rows past K_b hold NaN (they must never be read); lengths outside
+    [0, K] fail their sequence."""
+    rng = np.random.default_rng(B * 7 + V)
+    K = 5
+    tgt, drf, tok = _random_case(rng, B, K, V)
+    kb = rng.integers(0, K + 1, size=B).astype(np.int32)
+    kb[:3] = [0, K, 2]
+    if B > 10:
+        kb[7], kb[9] = -1, K + 1
+    for b in range(B):
+        if 0 <= kb[b] <= K:
+            tgt[b, kb[b] + 1:] = np.nan
+            drf[b, kb[b]:] = np.nan
+    temps = rng.choice([0.0, 0.6, 1.0, 1.3], size=B).astype(np.float32)
+    for dtype in ("fp32", "bf16"):
+        for beta in (1.0, 0.5):
+            _say(f"ragged lengths B={B} V={V} dtype={dtype} beta={beta}")
+            inp = _inputs_from_numpy(tgt, drf, tok, temps, beta, dtype)
+            inp["draft_len"] = torch.from_numpy(kb).cuda()
+            rep = run_both(sv, oracle_mod, inp, seed=B, ptol=_ptol(dtype))
+            rep.check()
+
+
+def test_ragged_without_draft_logits(sv, oracle_mod):
+    """No draft logits: greedy sequences, and sampling sequences that drafted
+    nothing (K_b = 0, bonus from target row 0); a sampling sequence with
+    K_b > 0 fails."""
+    rng = np.random.default_rng(77)
+    B, K, V = 12, 4, 5003
+    tgt, drf, tok = _random_case(rng, B, K, V)
+    kb = np.array([0, 0, 3, 4, 0, 1, 0, 2, 0, 4, 0, 3], dtype=np.int32)
+    temps = np.array([0.8, 1.0, 0.0, 0.0, 0.7, 0.9, 1.2, 0.0, 0.5, 0.0, 1.0, 0.0], np.float32)
+    for dtype in ("fp32", "bf16"):
+        _say(f"ragged without drafts dtype={dtype}")
+        inp = _inputs_from_numpy(tgt, drf, tok, temps, 1.0, dtype)
+        inp["draft_len"] = torch.from_numpy(kb).cuda()
+        rep = run_both(sv, oracle_mod, inp, seed=3, ptol=_ptol(dtype), draft_none=True)
+        rep.check()
+        g = run_gpu(sv, inp, seed=3, draft_none=True)
+        assert g["error_word"] & sv.SV_ERR_NO_DRAFT  # sequence 5 samples with K_b = 1
+        assert np.all(g["out_tokens"][5] == -1)
 
 
 def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod):

@@ -174,6 +174,20 @@ def sample_drafts(draft: torch.Tensor, temp: torch.Tensor, beta: float,
     return out.view(B, K)
 
 
+def ragged_lengths(w, seed: int, device) -> torch.Tensor:
+    """Per-sequence draft counts K_b ~ U{0..K} (a drafter that stops early, as
+    Kangaroo's confidence exit does), seeded; int32 [B] on `device`."""
+    g = torch.Generator().manual_seed(1_000_003 * (seed + 1) + w.B)
+    return torch.randint(0, w.K + 1, (w.B,), generator=g, dtype=torch.int32).to(device)
+
+
+def ragged_rows(w, draft_len) -> int:
+    """Logit rows a ragged call reads: K_b + 1 target rows, and K_b draft rows
+    when sampling."""
+    kb = int(draft_len.sum().item())
+    return kb + w.B + (0 if w.greedy else kb)
+
+
 def to_numpy_inputs(inp: dict, b0: int = 0, b1: int | None = None) -> dict:
     """Host copies for the oracle: float32 arrays, or uint16 arrays holding
     bf16 bit patterns (sequences b0..b1 only)."""
@@ -188,4 +202,6 @@ def to_numpy_inputs(inp: dict, b0: int = 0, b1: int | None = None) -> dict:
         "tokens": inp["tokens"][b0:b1].contiguous().cpu().numpy(),
         "temperature": inp["temperature"][b0:b1].contiguous().cpu().numpy(),
         "beta": inp["beta"],
+        "draft_len": (inp["draft_len"][b0:b1].contiguous().cpu().numpy()
+                      if inp.get("draft_len") is not None else None),
     }
