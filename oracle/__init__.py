@@ -77,6 +77,9 @@ def _load():
     lib.oracle_spec_verify_ragged.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, f64,
                                               P, P, P, P, P, P, P, P, P, P, i32]
     lib.oracle_spec_verify_ragged.restype = i32
+    lib.oracle_spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f64, i32, P, P, P, P, P,
+                                                i32]
+    lib.oracle_spec_verify_outcomes.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
     lib.oracle_spec_verify.restype = i32
@@ -213,5 +216,37 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
         _ptr(res["p_target"]), _ptr(res["p_draft"]), _ptr(res["residual_mass"]),
         _ptr(res["margin_accept"]), _ptr(res["margin_bonus"]), _ptr(res["seq_error"]),
         _ptr(res["draft_conf"]), _ptr(seq_ids), int(nthreads))
+    res["error"] = int(err)
+    return res
+
+
+def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: float = 1.0,
+             F: int = 4, nthreads: int = 0) -> dict:
+    """Verification-outcome distribution of every sequence (see the C source):
+    accept_rate [B, K], p_len [B, K+1], top_tokens [B, K+1, F] int32,
+    top_mass [B, K+1, F], seq_error [B], error (int)."""
+    lib = _load()
+    t_raw, dt = _as_raw(target)
+    B, K1, V = t_raw.shape
+    K = K1 - 1
+    d_raw = None
+    if draft is not None:
+        d_raw, dt2 = _as_raw(draft)
+        assert dt2 == dt and d_raw.shape == (B, K, V)
+    temp = np.asarray(temperature, dtype=np.float32)
+    if temp.ndim == 0:
+        temp = np.full(B, temp, dtype=np.float32)
+    temp = np.ascontiguousarray(temp)
+    res = {
+        "accept_rate": np.zeros((B, K), dtype=np.float64),
+        "p_len": np.zeros((B, K + 1), dtype=np.float64),
+        "top_tokens": np.zeros((B, K + 1, F), dtype=np.int32),
+        "top_mass": np.zeros((B, K + 1, F), dtype=np.float64),
+        "seq_error": np.zeros(B, dtype=np.int32),
+    }
+    err = lib.oracle_spec_verify_outcomes(
+        _ptr(t_raw), _ptr(d_raw), B, K, V, dt, _ptr(temp), float(beta), int(F), _ptr(res["accept_rate"]),
+        _ptr(res["p_len"]), _ptr(res["top_tokens"]), _ptr(res["top_mass"]), _ptr(res["seq_error"]),
+        int(nthreads))
     res["error"] = int(err)
     return res

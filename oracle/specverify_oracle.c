@@ -45,7 +45,13 @@
  *    exactly as for K = K_b; rows past K_b are never read;
  *  - the draft confidence of position i is max_v p_d(v) of draft row i at the
  *    sequence temperature, before the beta re-weighting (NaN for greedy
- *    sequences, whose draft rows are not read).
+ *    sequences, whose draft rows are not read);
+ *  - the verification-outcome distribution ("Speculative Speculative
+ *    Decoding", "Method") is taken over drafts drawn from the (beta-weighted)
+ *    draft law the verify step assumes, for all K positions whatever was
+ *    drafted; "the most likely bonus tokens" of a position are ranked by the
+ *    clamped residual mass max(p - q', 0) (target mass at position K), ties
+ *    to the lower token id; greedy sequences have no outcome law (NaN).
  */
 #include <math.h>
 #include <stdint.h>
@@ -497,6 +503,114 @@ int32_t oracle_spec_verify_ragged(const void *target, const void *draft, const i
 #endif
     for (int32_t b = 0; b < B; ++b) {
         int e = or_verify_sequence(&c, b);
+        if (seq_error) seq_error[b] = e;
+        all_err |= e;
+    }
+    return all_err;
+}
+
+/* ------------------------------------------------------------------ */
+/* Verification-outcome distribution ("Speculative Speculative Decoding",
+ * "Method": a verification outcome is the accepted prefix length plus the
+ * bonus token's identity; the speculator prepares the likeliest ones).
+ * Over drafts drawn from the draft law, position j accepts with probability
+ * alpha_j = sum_v min(p_j(v), q'_j(v)) and, on a rejection, emits v with
+ * probability r_j(v) / (1 - alpha_j), r_j = max(p_j - q'_j, 0); so
+ *   P(n = k) = (prod_{j<k} alpha_j) (1 - alpha_k),  P(n = K) = prod alpha_j,
+ *   P(n = k, bonus = v) = (prod_{j<k} alpha_j) r_k(v)   (k < K),
+ *   P(n = K, bonus = v) = (prod_j alpha_j) p_K(v).
+ * Per sampling sequence: accept_rate [K] = alpha, p_len [K+1] = P(n = k),
+ * and for each position k <= K the F tokens of largest r_k (p_K at k = K)
+ * by (mass desc, token asc), with those masses (token -1, mass 0 past the
+ * positive ones).  Greedy sequences (whose outcome their drafts fix) and
+ * failed ones get NaN, -1 and 0.                                              */
+static int or_outcome_sequence(const void *target, const void *draft, int32_t b, int32_t K,
+                               int32_t V, int dtype, double T, double beta, int32_t F,
+                               double *alpha, double *p_len, int32_t *top_tok, double *top_mass)
+{
+    for (int32_t j = 0; j < K; ++j) alpha[j] = NAN;
+    for (int32_t k = 0; k <= K; ++k) {
+        p_len[k] = NAN;
+        for (int32_t f = 0; f < F; ++f) {
+            top_tok[(size_t)k * F + f] = -1;
+            top_mass[(size_t)k * F + f] = 0.0;
+        }
+    }
+    if (!(T >= 0.0) || isinf(T)) return OR_ERR_TEMPERATURE;
+    if (T == 0.0) return 0;
+    if (K > 0 && draft == NULL) return OR_ERR_NO_DRAFT;
+    int weighted = beta < 1.0;
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    int err = 0;
+    for (int32_t k = 0; k <= K && !err; ++k) {
+        or_row rt, rd;
+        err = or_prepare(&rt, or_row_ptr(target, dtype, (size_t)b * (K + 1) + k, V), dtype, V, T, 0, 1.0);
+        if (k < K)
+            err |= or_prepare(&rd, or_row_ptr(draft, dtype, (size_t)b * K + k, V), dtype, V, T, weighted,
+                              beta);
+        if (err) break;
+        double amin = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            double pt = exp(or_logprob(&rt, v));
+            if (k < K) {
+                double q = exp(or_logprob(&rd, v));
+                amin += pt < q ? pt : q;
+                r[v] = pt > q ? pt - q : 0.0;
+            } else {
+                r[v] = pt;
+            }
+        }
+        if (k < K) alpha[k] = amin;
+        /* the F largest masses, ties to the lower token: F passes over V */
+        for (int32_t f = 0; f < F; ++f) {
+            int32_t best = -1;
+            for (int32_t v = 0; v < V; ++v) {
+                if (!(r[v] > 0.0)) continue;
+                int taken = 0;
+                for (int32_t g = 0; g < f; ++g)
+                    if (top_tok[(size_t)k * F + g] == v) taken = 1;
+                if (taken) continue;
+                if (best < 0 || r[v] > r[best]) best = v;
+            }
+            if (best < 0) break;
+            top_tok[(size_t)k * F + f] = best;
+            top_mass[(size_t)k * F + f] = r[best];
+        }
+    }
+    free(r);
+    if (err) {
+        for (int32_t j = 0; j < K; ++j) alpha[j] = NAN;
+        for (int32_t k = 0; k <= K; ++k)
+            for (int32_t f = 0; f < F; ++f) {
+                top_tok[(size_t)k * F + f] = -1;
+                top_mass[(size_t)k * F + f] = 0.0;
+            }
+        return err;
+    }
+    double reach = 1.0; /* prod_{j<k} alpha_j */
+    for (int32_t k = 0; k < K; ++k) {
+        p_len[k] = reach * (1.0 - alpha[k]);
+        reach *= alpha[k];
+    }
+    p_len[K] = reach;
+    return 0;
+}
+
+int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32_t B, int32_t K,
+                                    int32_t V, int32_t dtype, const float *temperature, double beta,
+                                    int32_t F, double *accept_rate, double *p_len, int32_t *top_tokens,
+                                    double *top_mass, int32_t *seq_error, int32_t nthreads)
+{
+    int32_t all_err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : all_err)
+#endif
+    for (int32_t b = 0; b < B; ++b) {
+        int e = or_outcome_sequence(target, draft, b, K, V, dtype, (double)temperature[b], beta, F,
+                                    accept_rate + (size_t)b * K, p_len + (size_t)b * (K + 1),
+                                    top_tokens + (size_t)b * (K + 1) * F,
+                                    top_mass + (size_t)b * (K + 1) * F);
         if (seq_error) seq_error[b] = e;
         all_err |= e;
     }
