@@ -523,7 +523,8 @@ int32_t oracle_spec_verify_ragged(const void *target, const void *draft, const i
  * and for each position k <= K the F tokens of largest r_k (p_K at k = K)
  * by (mass desc, token asc), with those masses (token -1, mass 0 past the
  * positive ones).  Greedy sequences (whose outcome their drafts fix) and
- * failed ones get NaN, -1 and 0.                                              */
+ * failed ones get NaN, -1 and 0; a failed sequence reports the failures of
+ * all its rows.                                                               */
 static int or_outcome_sequence(const void *target, const void *draft, int32_t b, int32_t K,
                                int32_t V, int dtype, double T, double beta, int32_t F,
                                double *alpha, double *p_len, int32_t *top_tok, double *top_mass)
@@ -541,14 +542,15 @@ static int or_outcome_sequence(const void *target, const void *draft, int32_t b,
     if (K > 0 && draft == NULL) return OR_ERR_NO_DRAFT;
     int weighted = beta < 1.0;
     double *r = (double *)malloc(sizeof(double) * (size_t)V);
-    int err = 0;
-    for (int32_t k = 0; k <= K && !err; ++k) {
+    int err = 0; /* the failures of every row of the sequence, OR-ed */
+    for (int32_t k = 0; k <= K; ++k) {
         or_row rt, rd;
-        err = or_prepare(&rt, or_row_ptr(target, dtype, (size_t)b * (K + 1) + k, V), dtype, V, T, 0, 1.0);
+        int e = or_prepare(&rt, or_row_ptr(target, dtype, (size_t)b * (K + 1) + k, V), dtype, V, T, 0, 1.0);
         if (k < K)
-            err |= or_prepare(&rd, or_row_ptr(draft, dtype, (size_t)b * K + k, V), dtype, V, T, weighted,
-                              beta);
-        if (err) break;
+            e |= or_prepare(&rd, or_row_ptr(draft, dtype, (size_t)b * K + k, V), dtype, V, T, weighted,
+                            beta);
+        err |= e;
+        if (err) continue;
         double amin = 0.0;
         for (int32_t v = 0; v < V; ++v) {
             double pt = exp(or_logprob(&rt, v));

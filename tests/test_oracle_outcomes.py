@@ -245,3 +245,19 @@ def test_ranked_bonus_tokens_break_ties_to_the_lower_token(oracle_mod):
             toks, vals = _ranked(mass, F)
             assert list(res["top_tokens"][0, k]) == list(toks), (trial, k)
             np.testing.assert_allclose(res["top_mass"][0, k], vals, rtol=1e-12, atol=1e-15)
+
+
+def test_outcome_row_failures_are_all_reported(oracle_mod):
+    """Pin: a sequence whose rows fail in several ways reports every failure
+    (a target row with no finite logit; a beta = 0 draft row with no mass
+    outside its top-4) and gets NaN / -1 / 0; other sequences are untouched."""
+    rng = np.random.default_rng(31)
+    V, K = 6, 2
+    tgt = rng.normal(size=(2, K + 1, V)).astype(np.float32)
+    drf = rng.normal(size=(2, K, V)).astype(np.float32)
+    tgt[0, 0, :] = -np.inf
+    drf[0, 1, 4:] = -np.inf
+    res = oracle_mod.outcomes(tgt, drf, np.float32(1.0), 0.0, F=2)
+    assert res["seq_error"][0] == oracle_mod.ERR_ROW | oracle_mod.ERR_DRAFT_MASS
+    assert np.all(np.isnan(res["p_len"][0])) and np.all(res["top_tokens"][0] == -1)
+    assert res["seq_error"][1] == 0 and abs(res["p_len"][1].sum() - 1.0) < 1e-12
