@@ -13,6 +13,11 @@ Prints one JSON line:
                  launch in every timed step), against 8 TB/s
   step_roofline  algorithmic bytes of the whole step / step time
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
+
+With --outcomes F a step is instead one spec_verify_outcomes call (the
+verification-outcome distribution with F ranked bonus tokens per position);
+its roofline is the outcome-pass kernel's, and its step roofline counts the
+two reads of every row the outcome law needs.
 """
 from __future__ import annotations
 
@@ -89,6 +94,107 @@ def cpu_baseline(inp, w, seconds: float) -> dict:
                       f"{min(threads, nseq)} busy (one sequence each at a time)"}
 
 
+def cpu_baseline_outcomes(inp, w, F: int, seconds: float) -> dict:
+    """Time the oracle's outcome distribution on host cores over a bounded sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workload import to_numpy_inputs
+
+    nseq = min(w.B, 16)
+    sub = {k: (v[:nseq] if torch.is_tensor(v) else v) for k, v in inp.items()}
+    h = to_numpy_inputs(sub)
+    threads = max(1, min(len(os.sched_getaffinity(0)), oracle.max_threads()))
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.outcomes(h["target"], h["draft"], h["temperature"], h["beta"], F=F, nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or calls >= 1000:
+            break
+    logits = calls * nseq * (w.K + 1) * w.V
+    return {"value": logits / el, "unit": "logits/s", "cores": min(threads, nseq),
+            "kind": "oracle",
+            "sample": f"{nseq} of {w.B} sequences of {w.tag()}, F={F}, {calls} calls in {el:.1f} s, "
+                      f"OpenMP over sequences, {threads} threads in the team, "
+                      f"{min(threads, nseq)} busy (one sequence each at a time)"}
+
+
+def bench_outcomes(args, sv, w, base, dev) -> dict:
+    """One step = one spec_verify_outcomes call (streaming pass, outcome pass,
+    finish) over the workload's full batch."""
+    import torch
+
+    F = args.outcomes
+    pass_bytes = w.stream_bytes()
+    # the outcome law needs every row twice: the clamp and the ranking of
+    # r = max(p - q', 0) depend on both rows' normalisers
+    alg_bytes = 2 * pass_bytes + 4 * w.B * (2 * (w.K + 1) + 2 * (w.K + 1) * F)
+    reps = max(2, math.ceil(2 * MALL_BYTES / pass_bytes))
+    replicas = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                         for _ in range(reps - 1)]
+    n = sv.outcomes_workspace_size(w.B, w.K, w.V, base["target"].dtype, F)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = [sv.Outcomes(r["target"], r["draft"], r["temperature"], r["beta"], F, workspace=ws,
+                         stream=stream) for r in replicas]
+    for k in range(args.warmup):
+        calls[k % reps]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        calls[(args.warmup + k) % reps]()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    res = calls[(args.warmup + args.steps - 1) % reps].out
+    mean_plen = float((res["p_len"] * torch.arange(w.K + 1, device=dev)).sum(1).mean().item())
+    # roofline: the outcome-pass kernel, stamped by its own dispatch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        calls[(args.warmup + args.steps + k) % reps](pass_events=ev[k])
+    torch.cuda.synchronize()
+    pass_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    logits_per_step = w.B * (w.K + 1) * w.V
+    pass_achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
+        "value": logits_per_step / (ms * 1e-3),
+        "unit": "logits/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.tag() + f"_outcomes_F{F}", "B": w.B, "K": w.K, "V": w.V,
+                   "F": F, "what": "verification-outcome distribution (spec_verify_outcomes)",
+                   "verified_logits_per_step": logits_per_step,
+                   "temperature": w.temperature if w.temperature is not None
+                   else f"U[{w.t_lo},{w.t_hi}] per sequence",
+                   "beta": w.beta, "replicas_rotated": reps,
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "expected_accepted_len": mean_plen,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "outcome_kernel (outcome pass)", "kernel_ms": pass_ms,
+                     "algorithmic_bytes_per_launch": pass_bytes},
+        "step_roofline": {"achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
+                          "scope": "two reads of every row (+ outputs) / call time"},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_outcomes(base, w, F, args.cpu_seconds)
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +206,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ragged", action="store_true",
                     help="ragged draft lengths K_b ~ U{0..K} per sequence (spec_verify_ragged)")
+    ap.add_argument("--outcomes", type=int, default=0, metavar="F",
+                    help="instead, time the verification-outcome distribution with F ranked "
+                         "bonus tokens per position (spec_verify_outcomes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="instead, run torch copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -132,6 +241,12 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
     base = make_inputs(w, seed=args.seed, device=dev)
+    if args.outcomes:
+        if w.greedy or args.ragged:
+            print("--outcomes needs a sampling workload without --ragged", file=sys.stderr)
+            return 2
+        print(json.dumps(bench_outcomes(args, sv, w, base, dev)), flush=True)
+        return 0
     alg_bytes = w.algorithmic_bytes()
     draft_len = None
     logits_per_step = w.B * (w.K + 1) * w.V

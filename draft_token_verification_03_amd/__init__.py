@@ -31,7 +31,9 @@ SV_ERR_NO_DRAFT = 16
 SV_ERR_DRAFT_LEN = 32
 
 EXPORTED = ("spec_verify", "spec_verify_ragged", "spec_verify_workspace_size", "spec_verify_row_stats",
-            "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_status_str")
+            "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_outcomes",
+            "spec_verify_outcomes_workspace_size", "spec_verify_status_str")
+MAX_OUTCOME_F = 32
 
 
 class SpecVerifyError(RuntimeError):
@@ -73,6 +75,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_uniforms.restype = i32
     lib.spec_verify_stream_probe.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
     lib.spec_verify_stream_probe.restype = i32
+    lib.spec_verify_outcomes_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.spec_verify_outcomes_workspace_size.restype = sz
+    lib.spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f32, i32, P, P, P, P, P, P, sz,
+                                         P, P, P]
+    lib.spec_verify_outcomes.restype = i32
     lib.spec_verify_status_str.argtypes = [i32]
     lib.spec_verify_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -281,3 +288,78 @@ def uniforms(seed: int, B: int, P: int, *, device="cuda", stream=None) -> torch.
     _check(load_library().spec_verify_uniforms(int(seed) & (2**64 - 1), B, P, _ptr(out),
                                                _stream(stream)))
     return out
+
+
+def outcomes_workspace_size(B: int, K: int, V: int, dtype: torch.dtype, F: int) -> int:
+    code = SV_F32 if dtype == torch.float32 else SV_BF16
+    return int(load_library().spec_verify_outcomes_workspace_size(B, K, V, code, F))
+
+
+class Outcomes:
+    """The verification-outcome distribution (spec_verify_outcomes) with its
+    buffers bound once, for repeated calls.
+
+    target [B, K+1, V] and draft [B, K, V] (or None) are contiguous float32 or
+    bfloat16 CUDA tensors; temperature a float or a [B] float32 tensor; beta in
+    [0, 1]; F ranked bonus tokens per position (0..32).  Each call returns a
+    dict of accept_rate [B, K], p_len [B, K+1], top_tokens [B, K+1, F] int32,
+    top_mass [B, K+1, F] (float32) and error_word [1] int32 (cleared before
+    every call).
+    """
+
+    def __init__(self, target: torch.Tensor, draft: torch.Tensor | None, temperature,
+                 beta: float = 1.0, F: int = 8, *, workspace: torch.Tensor | None = None,
+                 stream=None):
+        if target.dim() != 3 or not target.is_contiguous():
+            raise ValueError("target must be a contiguous [B, K+1, V] tensor")
+        B, K1, V = target.shape
+        K = K1 - 1
+        dev = target.device
+        code = _dtype_code(target)
+        if draft is not None:
+            if draft.shape != (B, K, V) or draft.dtype != target.dtype or not draft.is_contiguous():
+                raise ValueError("draft must be a contiguous [B, K, V] tensor of the target's dtype")
+        if not 0 <= F <= MAX_OUTCOME_F:
+            raise ValueError(f"F must be in [0, {MAX_OUTCOME_F}]")
+        if not torch.is_tensor(temperature):
+            temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
+        if temperature.shape != (B,) or temperature.dtype != torch.float32:
+            raise ValueError("temperature must be a [B] float32 tensor")
+        temperature = temperature.contiguous()
+        if workspace is None:
+            n = outcomes_workspace_size(max(B, 1), K, V, target.dtype, F)
+            if n == 0:
+                raise SpecVerifyError("invalid sizes for a workspace")
+            workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.out = {
+            "accept_rate": torch.empty((B, K), dtype=torch.float32, device=dev),
+            "p_len": torch.empty((B, K + 1), dtype=torch.float32, device=dev),
+            "top_tokens": torch.empty((B, K + 1, F), dtype=torch.int32, device=dev),
+            "top_mass": torch.empty((B, K + 1, F), dtype=torch.float32, device=dev),
+            "error_word": torch.zeros((1,), dtype=torch.int32, device=dev),
+        }
+        o = self.out
+        self._keep = (target, draft, temperature, workspace)
+        self._args = (_ptr(target), _ptr(draft), B, K, V, code, _ptr(temperature),
+                      ctypes.c_float(float(beta)), int(F), _ptr(o["accept_rate"]), _ptr(o["p_len"]),
+                      _ptr(o["top_tokens"]), _ptr(o["top_mass"]), _ptr(o["error_word"]),
+                      _ptr(workspace), workspace.numel())
+        self._stream = _stream(stream)
+
+    def __call__(self, pass_events=None) -> dict:
+        """Enqueue the call; pass_events, a pair of recorded torch.cuda.Event,
+        are stamped with the start and end of the outcome-pass kernel."""
+        self.out["error_word"].zero_()
+        b_ev = e_ev = None
+        if pass_events is not None:
+            b_ev, e_ev = pass_events[0].cuda_event, pass_events[1].cuda_event
+        _check(load_library().spec_verify_outcomes(*self._args, b_ev, e_ev, self._stream))
+        return self.out
+
+
+def outcomes(target: torch.Tensor, draft: torch.Tensor | None, temperature, beta: float = 1.0,
+             F: int = 8, *, workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Verification-outcome distribution of every sequence: accept rates
+    alpha_j, the law of the accepted length and the F likeliest bonus tokens
+    of each position with their residual masses (see Outcomes)."""
+    return Outcomes(target, draft, temperature, beta, F, workspace=workspace, stream=stream)()

@@ -73,6 +73,36 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     return true;
 }
 
+// The outcome distribution: the streaming pass's plan, then ~kFillBlocks
+// outcome workgroups (two chunks per position when the positions alone fill
+// the grid and a row pair is long), and the outcome pass's records, sums and
+// keys after the streaming pass's regions.
+bool make_outcome_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F, OutPlan *op)
+{
+    if (F < 0 || F > kMaxOutcomeF) return false;
+    *op = OutPlan{};
+    if (!make_plan(B, K, V, dtype, &op->p)) return false;
+    const Plan &p = op->p;
+    op->F = F;
+    const int64_t pos = (int64_t)p.sB * (K + 1);
+    int64_t nc2 = (kFillBlocks + pos - 1) / pos;
+    if (nc2 == 1 && 2 * p.row_bytes >= kSplitRowBytes) nc2 = 2;
+    const int64_t nc_max = std::max<int64_t>(1, p.nvec / (kBlock * kOutLoads));
+    nc2 = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(nc2, nc_max), kMaxOutChunks));
+    op->cvec2 = (int32_t)((p.nvec + nc2 - 1) / nc2);
+    op->nc2 = (p.nvec + op->cvec2 - 1) / op->cvec2;
+    if (pos * op->nc2 >= ((int64_t)1 << 31)) return false;
+    size_t off = p.bytes;
+    op->off_rec = off;
+    off = align256(off + sizeof(OutRow) * (size_t)pos);
+    op->off_asum = off;
+    off = align256(off + sizeof(double) * (size_t)pos * op->nc2);
+    op->off_keys = off;
+    off = align256(off + sizeof(uint64_t) * (size_t)pos * op->nc2 * F);
+    op->bytes = off;
+    return true;
+}
+
 // Arguments of the sub-batch of sequences [b0, b0 + nb).
 static Args sub_args(const Plan &p, void *ws, int32_t b0, int32_t nb)
 {
@@ -198,6 +228,66 @@ int32_t spec_verify_ragged(const void *target_logits, const void *draft_logits,
     return sv::verify(target_logits, draft_logits, draft_tokens, draft_len, B, K, V, dtype, seed,
                       temperature, beta, accepted_len, out_tokens, workspace, workspace_bytes, aux,
                       stream);
+}
+
+size_t spec_verify_outcomes_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F)
+{
+    sv::OutPlan op;
+    if (B < 0 || !sv::make_outcome_plan(B, K, V, dtype, F, &op)) return 0;
+    return op.bytes;
+}
+
+int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
+                             int32_t V, int32_t dtype, const float *temperature, float beta, int32_t F,
+                             float *accept_rate, float *p_len, int32_t *top_tokens, float *top_mass,
+                             int32_t *error_word, void *workspace, size_t workspace_bytes,
+                             void *pass_begin, void *pass_end, void *stream)
+{
+    if (B < 0 || K < 0 || K > sv::kMaxK || V < 1) return SV_EINVAL;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
+    if (!(beta >= 0.f && beta <= 1.f) || F < 0 || F > sv::kMaxOutcomeF) return SV_EINVAL;
+    if ((int64_t)B * (K + 1) * (int64_t)V > ((int64_t)1 << 40)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !temperature || !p_len || (K > 0 && !accept_rate) ||
+        (F > 0 && (!top_tokens || !top_mass)))
+        return SV_EINVAL;
+    const size_t elt = dtype == SV_F32 ? 4 : 2;
+    if (((uintptr_t)target_logits % elt) || (draft_logits && ((uintptr_t)draft_logits % elt)))
+        return SV_EINVAL;
+    sv::OutPlan op;
+    if (!sv::make_outcome_plan(B, K, V, dtype, F, &op)) return SV_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < op.bytes) return SV_EWORKSPACE;
+    const sv::Plan &p = op.p;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    for (int32_t b0 = 0; b0 < B; b0 += p.sB) {
+        const int32_t nb = std::min(p.sB, B - b0);
+        sv::OutArgs o = {};
+        o.a = sv::sub_args(p, workspace, b0, nb);
+        sv::Args &a = o.a;
+        a.target = static_cast<const char *>(target_logits) + (int64_t)b0 * (K + 1) * p.row_bytes;
+        a.draft = draft_logits ? static_cast<const char *>(draft_logits) + (int64_t)b0 * K * p.row_bytes
+                               : nullptr;
+        a.temperature = temperature + b0;
+        a.beta = beta;
+        a.log2_beta = std::log2((double)beta);
+        a.weighted = (beta < 1.f && K > 0) ? 1 : 0;
+        a.sampling_only = 1;
+        a.error_word = error_word;
+        o.F = F;
+        o.nc2 = op.nc2;
+        o.cvec2 = op.cvec2;
+        o.rec = reinterpret_cast<sv::OutRow *>(w + op.off_rec);
+        o.asum = reinterpret_cast<double *>(w + op.off_asum);
+        o.keys = reinterpret_cast<uint64_t *>(w + op.off_keys);
+        o.accept_rate = accept_rate ? accept_rate + (int64_t)b0 * K : nullptr;
+        o.p_len = p_len + (int64_t)b0 * (K + 1);
+        o.top_tokens = top_tokens ? top_tokens + (int64_t)b0 * (K + 1) * F : nullptr;
+        o.top_mass = top_mass ? top_mass + (int64_t)b0 * (K + 1) * F : nullptr;
+        sv::launch_outcomes(o, s, b0 == 0 ? static_cast<hipEvent_t>(pass_begin) : nullptr,
+                            b0 == 0 ? static_cast<hipEvent_t>(pass_end) : nullptr);
+    }
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,

@@ -79,6 +79,7 @@ struct Args {
     float beta;
     double log2_beta;       // log2(beta), -inf for beta == 0
     int32_t weighted;
+    int32_t sampling_only;  // the streaming pass skips the rows of greedy sequences
     int32_t *accepted_len;
     int32_t *out_tokens;
     RowPart *part;          // [sB][R][nc]
@@ -94,9 +95,48 @@ struct Args {
     int32_t *rs_argmax;
 };
 
+// ---------------------------------------------------------------------------
+// Verification-outcome distribution: per (sequence, position) records and
+// per (sequence, position, chunk) partial sums and best-F residual keys.
+
+constexpr int kMaxOutcomeF = 32;     // ranked bonus tokens per position
+constexpr int kMaxOutChunks = 128;   // outcome-pass chunks per position
+constexpr int kOutLoads = 2;         // 16-byte vectors per thread per row per tile
+
+struct OutRow {
+    double norm;     // position j < K: draft normaliser D; j == K: target sum S_t
+    float o;         // j == K: offset fp32(m_t c) of target row K
+    int32_t status;  // SV_ERR_ROW / SV_ERR_DRAFT_MASS bits of the position's rows
+};
+
+struct OutPlan {
+    Plan p;                   // the streaming pass (its part/top/tope regions)
+    int32_t F, nc2, cvec2;    // ranked tokens; outcome chunks per position, vectors per chunk
+    size_t off_rec, off_asum, off_keys;
+    size_t bytes;
+};
+
+bool make_outcome_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F, OutPlan *p);
+
+struct OutArgs {
+    Args a;                   // rows, temperatures, beta and the streaming-pass partials
+    int32_t F, nc2, cvec2;
+    OutRow *rec;              // [sB][K+1]
+    double *asum;             // [sB][K+1][nc2] sum of min(p, q') D over the chunk (j < K)
+    uint64_t *keys;           // [sB][K+1][nc2][F] the chunk's best keys, descending, 0 = none
+    float *accept_rate;       // [sB][K]
+    float *p_len;             // [sB][K+1]
+    int32_t *top_tokens;      // [sB][K+1][F]
+    float *top_mass;          // [sB][K+1][F]
+};
+
 // Launchers of one sub-batch: the verify step (non-null events are recorded
-// around the streaming launch), the row-statistics entry point, the uniforms.
+// around the streaming launch), the streaming pass alone, the outcome
+// distribution (events around the outcome pass), the row-statistics entry
+// point, the uniforms.
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end);
+void launch_stats(const Args &a, hipStream_t s);
+void launch_outcomes(const OutArgs &o, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 void launch_rowstats(const Args &a, hipStream_t s);
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s);
 void launch_stream_probe(const Args &a, uint32_t *sink, hipStream_t s, hipEvent_t begin, hipEvent_t end);

@@ -175,7 +175,8 @@ __device__ __forceinline__ const char *draft_row(const Args &a, int b, int i)
 // round trip earlier; a draft row of a greedy sequence (whose draft logits
 // were passed anyway) wastes that one tile.  Rows a sequence does not use
 // (draft rows in greedy mode or without draft logits, rows of a sequence with
-// an invalid temperature) publish nothing.
+// an invalid temperature, every row of a greedy sequence when only sampling
+// sequences are wanted) publish nothing.
 
 // One (row, chunk) of the streaming pass; the first tile is requested before
 // the temperature is looked at.
@@ -193,13 +194,13 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
     // a sampling row's logit at its drafted token, read while the first tile
     // is in flight, saves the accept step a dependent gather
     float zx = 0.f;
-    if (chunk == 0 && i < kb && threadIdx.x == 0) {
+    if (chunk == 0 && i < kb && a.tokens && threadIdx.x == 0) {
         const int x = a.tokens[(int64_t)b * a.K + i];
         if (x >= 0 && x < a.V) zx = Elt<DT>::scalar(row, x);
     }
 
     const bool greedy = T == 0.f;
-    if (!temperature_ok(T) || (is_draft && greedy)) return;
+    if (!temperature_ok(T) || (greedy && (is_draft || a.sampling_only))) return;
     RowPart part;
     Top4 ct;
     const bool track_top = TOP && is_draft;
@@ -1117,6 +1118,18 @@ void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t en
     } else {
         if (a.weighted) launch_all<1, true>(a, s, begin, end);
         else launch_all<1, false>(a, s, begin, end);
+    }
+}
+
+void launch_stats(const Args &a, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((int64_t)a.B * (a.draft ? a.R : a.K + 1) * a.nc);
+    if (a.dtype == SV_F32) {
+        if (a.weighted) stats_kernel<0, true><<<grid, kBlock, 0, s>>>(a);
+        else stats_kernel<0, false><<<grid, kBlock, 0, s>>>(a);
+    } else {
+        if (a.weighted) stats_kernel<1, true><<<grid, kBlock, 0, s>>>(a);
+        else stats_kernel<1, false><<<grid, kBlock, 0, s>>>(a);
     }
 }
 

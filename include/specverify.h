@@ -185,6 +185,51 @@ int32_t spec_verify_stream_probe(const void *target_logits, const void *draft_lo
                                  int32_t V, int32_t dtype, uint32_t *sink, void *begin, void *end,
                                  void *stream);
 
+/*
+ * The verification-outcome distribution ("Speculative Speculative Decoding",
+ * "Method": a verification outcome is the accepted prefix length together
+ * with the bonus token, and the speculator prepares drafts for the likeliest
+ * outcomes).  For each sequence with T > 0, over drafts drawn from the
+ * (beta-weighted) draft law q'_j the verify step assumes:
+ *   accept_rate [B, K]      alpha_j = sum_v min(p_j(v), q'_j(v))
+ *   p_len       [B, K+1]    P(n = k) = (prod_{j<k} alpha_j)(1 - alpha_k),
+ *                           P(n = K) = prod_j alpha_j
+ *   top_tokens  [B, K+1, F] int32: per position k, the F tokens of largest
+ *                           r_k(v) = max(p_k(v) - q'_k(v), 0) (k < K) or
+ *                           p_K(v) (k = K), in descending order, ties to the
+ *                           lower token id; -1 past the positive ones
+ *   top_mass    [B, K+1, F] those r_k(v) (p_K(v)), 0 past the positive ones;
+ *                           P(n = k, bonus = v) = prod_{j<k} alpha_j * r_k(v)
+ * p, q' and beta as in spec_verify; all K positions of every sequence are
+ * used, whatever was drafted.  Outputs are float32 (alpha clamped to [0, 1]);
+ * the r values are ranked as computed in fp32, so tokens whose masses agree
+ * to ~1e-6 may appear in either order.  Greedy sequences (T == 0, whose
+ * outcome their drafts fix) get NaN, -1 and 0; so do failed ones, whose
+ * failures (SV_ERR_TEMPERATURE, SV_ERR_ROW, SV_ERR_DRAFT_MASS, and
+ * SV_ERR_NO_DRAFT when T > 0, K > 0 and draft_logits is NULL) are OR-ed into
+ * *error_word when error_word is not NULL.
+ *   target_logits  [B, K+1, V] dtype;  draft_logits [B, K, V] dtype or NULL
+ *   temperature    [B] float;  beta host float in [0, 1]
+ *   F              ranked tokens per position, 0..32 (top_tokens and
+ *                  top_mass may be NULL when F == 0; accept_rate when K == 0)
+ *   workspace      device buffer of >= spec_verify_outcomes_workspace_size()
+ *                  bytes, 256-byte aligned (scratch)
+ *   pass_begin, pass_end  hipEvent_t or NULL: stamped with the start and end
+ *                  of the outcome-pass kernel of the first sub-batch
+ * Device pointers, stream ordering and ownership as for spec_verify.
+ * Three kernel launches per sub-batch of at most 8192 sequences: the
+ * streaming pass of spec_verify, the outcome pass (a second read of every
+ * row: the clamp and the ranking need both rows' normalisers), and a
+ * per-sequence finish.  Returns SV_OK after enqueuing the work.
+ */
+size_t spec_verify_outcomes_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F);
+
+int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
+                             int32_t V, int32_t dtype, const float *temperature, float beta, int32_t F,
+                             float *accept_rate, float *p_len, int32_t *top_tokens, float *top_mass,
+                             int32_t *error_word, void *workspace, size_t workspace_bytes,
+                             void *pass_begin, void *pass_end, void *stream);
+
 /* Static description of a status code. */
 const char *spec_verify_status_str(int32_t status);
 

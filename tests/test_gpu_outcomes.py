@@ -1,0 +1,313 @@
+"""GPU parity of the verification-outcome distribution (spec_verify_outcomes)
+against the oracle's, through the C-ABI.
+
+Rule: accept rates, the length law and the ranked masses agree within `tol`
+(absolute) position by position and slot by slot.  Tokens at position K rank
+by the target logits and must match exactly.  Tokens at j < K rank by the
+residual r computed in fp32, so two tokens whose oracle masses agree within
+`tol` may trade places; a slot's token must then be one the oracle ranks with
+a mass within `tol` of that slot's (the oracle is asked for 8 extra slots to
+see such near-ties), and a slot the GPU leaves empty must have an oracle mass
+within `tol` of zero (a slot whose masses on both sides are within `tol` of
+zero may hold any token or none: p = q' exactly leaves fp32 rounding noise of
+~1e-7 in r).  Greedy and failed sequences: NaN / -1 / 0 exactly.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from workload import WORKLOADS, make_inputs, to_numpy_inputs
+
+pytestmark = pytest.mark.gpu
+
+_SKIP = not torch.cuda.is_available()
+EXTRA = 8
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if _SKIP:
+        pytest.skip("no GPU")
+    import draft_token_verification_03_amd as sv
+    sv.load_library()
+    return sv
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(sv, inp: dict, F: int, draft_none: bool = False, workspace=None) -> dict:
+    res = sv.outcomes(inp["target"], None if draft_none else inp["draft"], inp["temperature"],
+                      inp["beta"], F, workspace=workspace)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    g["error_word"] = int(g["error_word"][0])
+    return g
+
+
+def run_oracle(oracle_mod, h: dict, F: int) -> dict:
+    return oracle_mod.outcomes(h["target"], h.get("draft"), h["temperature"], h["beta"], F=F + EXTRA)
+
+
+def check(g: dict, o: dict, F: int, tol: float = 1e-5) -> dict:
+    """Compare GPU outputs g (F slots) with oracle outputs o (F + EXTRA slots)."""
+    B, K1 = o["p_len"].shape
+    K = K1 - 1
+    fails = []
+    swaps = 0
+    max_err = 0.0
+    for b in range(B):
+        if np.isnan(o["p_len"][b, 0]):
+            ok = (np.all(np.isnan(g["p_len"][b])) and np.all(np.isnan(g["accept_rate"][b]))
+                  and np.all(g["top_tokens"][b] == -1) and np.all(g["top_mass"][b] == 0.0))
+            if not ok:
+                fails.append(f"seq {b}: expected NaN/-1/0 outputs")
+            continue
+        ea = np.abs(g["accept_rate"][b].astype(np.float64) - o["accept_rate"][b])
+        ep = np.abs(g["p_len"][b].astype(np.float64) - o["p_len"][b])
+        max_err = max(max_err, float(ea.max(initial=0.0)), float(ep.max()))
+        if ea.max(initial=0.0) > tol or ep.max() > tol:
+            fails.append(f"seq {b}: alpha err {ea.max(initial=0.0):.3g} p_len err {ep.max():.3g}")
+        for k in range(K + 1):
+            gt = g["top_tokens"][b, k]
+            gm = g["top_mass"][b, k].astype(np.float64)
+            ot = o["top_tokens"][b, k]
+            om = o["top_mass"][b, k]
+            em = np.abs(gm - om[:F])
+            max_err = max(max_err, float(em.max(initial=0.0)))
+            if em.max(initial=0.0) > tol:
+                fails.append(f"seq {b} pos {k}: ranked masses differ by {em.max():.3g}")
+            live = gt[gt >= 0]
+            if len(set(live.tolist())) != live.size or np.any(gt[live.size:] != -1):
+                fails.append(f"seq {b} pos {k}: tokens not distinct-then-empty {gt}")
+            omap = {int(t): float(m) for t, m in zip(ot, om) if t >= 0}
+            for f in range(F):
+                if gt[f] == ot[f]:
+                    continue
+                if om[f] <= tol and gm[f] <= tol:
+                    continue  # masses at the level of rounding noise: listed or not
+                if k == K:
+                    fails.append(f"seq {b} pos K slot {f}: token {gt[f]} vs {ot[f]}")
+                elif gt[f] < 0:
+                    fails.append(f"seq {b} pos {k} slot {f}: empty, oracle mass {om[f]:.3g}")
+                elif int(gt[f]) not in omap or abs(omap[int(gt[f])] - om[f]) > tol:
+                    fails.append(f"seq {b} pos {k} slot {f}: token {gt[f]} is no near-tie of {ot[f]}")
+                else:
+                    swaps += 1
+    assert not fails, "\n".join(fails[:20])
+    return {"swaps": swaps, "max_err": max_err}
+
+
+def _inputs(tgt, drf, temps, beta, dtype):
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    return {"target": torch.from_numpy(np.ascontiguousarray(tgt)).to("cuda").to(dt),
+            "draft": None if drf is None else torch.from_numpy(np.ascontiguousarray(drf)).to("cuda").to(dt),
+            "temperature": torch.from_numpy(np.asarray(temps, dtype=np.float32)).to("cuda"),
+            "beta": float(beta)}
+
+
+def _host(inp):
+    h = {}
+    for k in ("target", "draft"):
+        x = inp[k]
+        if x is None:
+            h[k] = None
+        elif x.dtype == torch.bfloat16:
+            h[k] = x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        else:
+            h[k] = x.contiguous().cpu().numpy()
+    h["temperature"] = inp["temperature"].cpu().numpy()
+    h["beta"] = inp["beta"]
+    return h
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,B,V,F", [
+    ("C1", 1, 32000, 8), ("C2", 8, 128256, 8), ("C4", 12, 152064, 8), ("C5", 10, 128256, 4),
+    ("C5", 6, 30011, 16), ("C4", 6, 30011, 1), ("C2", 5, 7001, 32),
+])
+def test_outcomes_match_oracle(sv, oracle_mod, name, B, V, F):
+    """Named workloads (full vocabulary, reduced batch) and odd vocabularies
+    (unaligned rows, ragged tails) with 1 to 32 ranked tokens."""
+    w = WORKLOADS[name].sized(B=B, V=V)
+    for s in range(2):
+        _say(f"outcomes {name} B={B} V={V} F={F} seed={s}")
+        inp = make_inputs(w, seed=400 + s, device="cuda")
+        g = run_gpu(sv, inp, F)
+        h = to_numpy_inputs(inp)
+        o = run_oracle(oracle_mod, h, F)
+        st = check(g, o, F)
+        _say(f"  swaps {st['swaps']} max err {st['max_err']:.2e}")
+        assert g["error_word"] == 0
+
+
+def test_greedy_sequences_have_no_outcome_law(sv, oracle_mod):
+    w = WORKLOADS["C3"].sized(B=6, V=9001)
+    inp = make_inputs(w, seed=3, device="cuda")
+    for draft_none in (False, True):
+        g = run_gpu(sv, inp, 4, draft_none=draft_none)
+        assert np.all(np.isnan(g["p_len"])) and np.all(g["top_tokens"] == -1)
+        assert g["error_word"] == 0
+
+
+@pytest.mark.parametrize("name", ["C4", "C5"])
+def test_outcomes_full_size_sampled(sv, oracle_mod, name):
+    """Full-size batch in one call; 6 sequences re-derived by the oracle."""
+    w = WORKLOADS[name]
+    F = 8
+    _say(f"outcomes full-size {name} {w.tag()}")
+    inp = make_inputs(w, seed=9, device="cuda")
+    g = run_gpu(sv, inp, F)
+    rng = np.random.default_rng(5)
+    ids = np.sort(rng.choice(w.B, size=6, replace=False))
+    if w.identical_every:
+        ids[0] = 0
+    sub = {k: (v[torch.from_numpy(ids).to(v.device)] if torch.is_tensor(v) else v)
+           for k, v in inp.items()}
+    h = to_numpy_inputs(sub)
+    o = run_oracle(oracle_mod, h, F)
+    gs = {k: (v[ids] if isinstance(v, np.ndarray) else v) for k, v in g.items()}
+    check(gs, o, F)
+    # properties that hold at any size
+    assert g["error_word"] == 0
+    np.testing.assert_allclose(g["p_len"].sum(axis=1), 1.0, atol=1e-5)
+    assert np.all((g["accept_rate"] >= 0) & (g["accept_rate"] <= 1))
+    tm = g["top_mass"]
+    assert np.all(np.diff(tm, axis=2) <= 0)
+    assert np.all(tm[:, :w.K].sum(axis=2) <= 1.0 - g["accept_rate"] + 1e-5)
+    if w.identical_every:
+        same = np.arange(w.B) % w.identical_every == 0
+        np.testing.assert_allclose(g["accept_rate"][same], 1.0, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 9, 31, 257, 2049])
+def test_tiny_and_odd_vocabularies(sv, oracle_mod, dtype, V):
+    rng = np.random.default_rng(V)
+    B, K = 5, 3
+    tgt = rng.normal(size=(B, K + 1, V)).astype(np.float32) * 2
+    drf = (tgt[:, :K] + rng.normal(size=(B, K, V)).astype(np.float32)).astype(np.float32)
+    temps = np.array([1.0, 0.6, 1.7, 0.3, 1.0], np.float32)
+    for beta in (1.0, 0.5):
+        _say(f"tiny V={V} dtype={dtype} beta={beta}")
+        inp = _inputs(tgt, drf, temps, beta, dtype)
+        F = min(32, V + 2)
+        g = run_gpu(sv, inp, F)
+        o = run_oracle(oracle_mod, _host(inp), F)
+        check(g, o, F)
+        assert g["error_word"] == int(np.bitwise_or.reduce(o["seq_error"]))
+
+
+def test_rising_rows_and_ties(sv, oracle_mod):
+    """Rows whose logits rise with the token id (every tile brings new
+    candidates), rows of many equal logits (ties resolved to the lower id),
+    and masked tokens."""
+    B, K, V = 6, 2, 20011
+    tgt = np.zeros((B, K + 1, V), np.float32)
+    drf = np.zeros((B, K, V), np.float32)
+    ramp = np.linspace(-8, 8, V, dtype=np.float32)
+    tgt[0] = ramp
+    drf[0] = ramp[::-1]
+    tgt[1] = np.round(ramp)               # 17 levels: long runs of equal logits
+    drf[1] = np.round(ramp[::-1] / 2)
+    rng = np.random.default_rng(4)
+    tgt[2] = rng.integers(-2, 3, size=(K + 1, V))
+    drf[2] = rng.integers(-2, 3, size=(K, V))
+    tgt[3] = rng.normal(size=(K + 1, V))
+    drf[3] = tgt[3, :K]
+    tgt[3, :, ::3] = -np.inf              # masked tokens
+    drf[3, :, ::5] = -np.inf
+    tgt[4] = -ramp
+    drf[4] = ramp
+    tgt[5] = rng.normal(size=(K + 1, V)) * 6
+    drf[5] = rng.normal(size=(K, V)) * 6
+    for dtype in ("fp32", "bf16"):
+        for beta in (1.0, 0.25, 0.0):
+            _say(f"rising/ties dtype={dtype} beta={beta}")
+            inp = _inputs(tgt, drf, np.full(B, 0.9, np.float32), beta, dtype)
+            for F in (3, 32):
+                g = run_gpu(sv, inp, F)
+                o = run_oracle(oracle_mod, _host(inp), F)
+                check(g, o, F)
+                assert g["error_word"] == int(np.bitwise_or.reduce(o["seq_error"]))
+
+
+def test_outcome_error_paths(sv, oracle_mod):
+    rng = np.random.default_rng(6)
+    B, K, V = 6, 2, 4001
+    tgt = rng.normal(size=(B, K + 1, V)).astype(np.float32)
+    drf = rng.normal(size=(B, K, V)).astype(np.float32)
+    tgt[1, 2, :] = -np.inf                 # a target row with no finite logit
+    drf[2, 0, 4:] = -np.inf                # beta = 0 leaves no draft mass
+    temps = np.array([1.0, 1.0, 1.0, np.nan, -1.0, 0.0], np.float32)
+    inp = _inputs(tgt, drf, temps, 0.0, "fp32")
+    g = run_gpu(sv, inp, 5)
+    o = run_oracle(oracle_mod, _host(inp), 5)
+    check(g, o, 5)
+    assert g["error_word"] == int(np.bitwise_or.reduce(o["seq_error"]))
+    assert g["error_word"] == sv.SV_ERR_ROW | sv.SV_ERR_DRAFT_MASS | sv.SV_ERR_TEMPERATURE
+    # no draft logits while sequences sample
+    g = run_gpu(sv, inp, 5, draft_none=True)
+    assert g["error_word"] & sv.SV_ERR_NO_DRAFT
+    assert np.all(np.isnan(g["p_len"]))
+
+
+def test_no_drafts_and_no_ranked_tokens(sv, oracle_mod):
+    """K = 0 (all mass on n = 0, the target's top tokens) and F = 0 (only the
+    accept rates and the length law)."""
+    rng = np.random.default_rng(12)
+    tgt = rng.normal(size=(4, 1, 9001)).astype(np.float32)
+    inp = _inputs(tgt, None, np.full(4, 0.8, np.float32), 1.0, "bf16")
+    g = run_gpu(sv, inp, 6, draft_none=True)
+    o = run_oracle(oracle_mod, _host(inp), 6)
+    check(g, o, 6)
+    w = WORKLOADS["C5"].sized(B=5, V=20011)
+    inp = make_inputs(w, seed=8, device="cuda")
+    g = run_gpu(sv, inp, 0)
+    o = run_oracle(oracle_mod, to_numpy_inputs(inp), 0)
+    check(g, o, 0)
+
+
+@pytest.mark.parametrize("name,B,V", [("C5", 9000, 301), ("C4", 300, 20011)])
+def test_outcomes_beyond_one_sub_batch_and_scratch(sv, oracle_mod, name, B, V):
+    """More sequences than one sub-batch (8192), and a full-vocabulary-like
+    batch, on a workspace filled with garbage first; a second call on a
+    cleared workspace gives the same tokens, and the same bits when beta = 1.
+    (With beta < 1 the streaming pass adds the entries that leave a draft
+    row's shared top-4 slots to its fp64 sum in an order set by timing, so D
+    and the outputs formed from it may differ in the last bit.)"""
+    w = WORKLOADS[name].sized(B=B, V=V)
+    inp = make_inputs(w, seed=72, device="cuda")
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    n = sv.outcomes_workspace_size(w.B, w.K, w.V, dt, 4)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    g = run_gpu(sv, inp, 4, workspace=ws)
+    o = run_oracle(oracle_mod, to_numpy_inputs(inp), 4)
+    check(g, o, 4)
+    ws.fill_(0x00)
+    g2 = run_gpu(sv, inp, 4, workspace=ws)
+    assert np.array_equal(g["top_tokens"], g2["top_tokens"])
+    for k in ("accept_rate", "p_len", "top_mass"):
+        if w.beta < 1.0:
+            np.testing.assert_allclose(g2[k], g[k], rtol=1e-6, atol=2e-7)
+        else:
+            assert np.array_equal(g[k], g2[k], equal_nan=True), k
+
+
+def test_outcome_pass_is_timed(sv):
+    w = WORKLOADS["C4"].sized(B=16, V=20011)
+    inp = make_inputs(w, seed=2, device="cuda")
+    run = sv.Outcomes(inp["target"], inp["draft"], inp["temperature"], inp["beta"], 8)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    run(pass_events=ev)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0.0
