@@ -40,7 +40,7 @@ DEFAULT_WORKLOAD = "C2"
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = "draft_token_verification_03_amd/csrc/"
-    for rel in (csrc + "sv_api.hip", csrc + "sv_verify.hip",
+    for rel in (csrc + "sv_api.hip", csrc + "sv_verify.hip", csrc + "sv_outcome.hip",
                 csrc + "sv_device.h", csrc + "sv_internal.h", csrc + "sv_accept.h", csrc + "sv_tile.h",
                 "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -49,7 +49,8 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(tag: str) -> float | None:
-    """HBM bytes per launch of the streaming pass from the committed rocprofv3
+    """HBM bytes per launch of the timed kernel (the streaming pass, or the
+    outcome pass for an outcome workload tag) from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the reading of a
     plain copy of known size), if it was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
@@ -184,7 +185,8 @@ def bench_outcomes(args, sv, w, base, dev) -> dict:
                    "expected_accepted_len": mean_plen,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic(f"{args.workload}_outcomes_F{F}"),
                      "kernel": "outcome_kernel (outcome pass)", "kernel_ms": pass_ms,
                      "algorithmic_bytes_per_launch": pass_bytes},
         "step_roofline": {"achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
