@@ -78,7 +78,7 @@ def _load():
                                               P, P, P, P, P, P, P, P, P, P, i32]
     lib.oracle_spec_verify_ragged.restype = i32
     lib.oracle_spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f64, i32, P, P, P, P, P,
-                                                i32]
+                                                P, i32]
     lib.oracle_spec_verify_outcomes.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
@@ -224,7 +224,8 @@ def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: fl
              F: int = 4, nthreads: int = 0) -> dict:
     """Verification-outcome distribution of every sequence (see the C source):
     accept_rate [B, K], p_len [B, K+1], top_tokens [B, K+1, F] int32,
-    top_mass [B, K+1, F], seq_error [B], error (int)."""
+    top_mass [B, K+1, F], draft_top_mass [B, K] (residual mass on each draft
+    row's top-4), seq_error [B], error (int)."""
     lib = _load()
     t_raw, dt = _as_raw(target)
     B, K1, V = t_raw.shape
@@ -242,11 +243,15 @@ def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: fl
         "p_len": np.zeros((B, K + 1), dtype=np.float64),
         "top_tokens": np.zeros((B, K + 1, F), dtype=np.int32),
         "top_mass": np.zeros((B, K + 1, F), dtype=np.float64),
+        "draft_top_mass": np.zeros((B, K), dtype=np.float64),
         "seq_error": np.zeros(B, dtype=np.int32),
     }
     err = lib.oracle_spec_verify_outcomes(
         _ptr(t_raw), _ptr(d_raw), B, K, V, dt, _ptr(temp), float(beta), int(F), _ptr(res["accept_rate"]),
-        _ptr(res["p_len"]), _ptr(res["top_tokens"]), _ptr(res["top_mass"]), _ptr(res["seq_error"]),
+        _ptr(res["p_len"]), _ptr(res["top_tokens"]), _ptr(res["top_mass"]),
+        _ptr(res["draft_top_mass"]) if K > 0 and d_raw is not None else None, _ptr(res["seq_error"]),
         int(nthreads))
+    if K > 0 and d_raw is None:
+        res["draft_top_mass"][:] = np.nan
     res["error"] = int(err)
     return res

@@ -522,14 +522,21 @@ int32_t oracle_spec_verify_ragged(const void *target, const void *draft, const i
  * Per sampling sequence: accept_rate [K] = alpha, p_len [K+1] = P(n = k),
  * and for each position k <= K the F tokens of largest r_k (p_K at k = K)
  * by (mass desc, token asc), with those masses (token -1, mass 0 past the
- * positive ones).  Greedy sequences (whose outcome their drafts fix) and
+ * positive ones).  Optionally draft_top_mass [K]: the residual mass r_k on
+ * the 4 largest logits of draft row k (the tokens beta down-weights), so
+ * that P(bonus among them | n = k) = draft_top_mass_k / (1 - alpha_k)
+ * ("Key claims": Saguaro sampling concentrates the residual on the draft's
+ * likeliest tokens, raising the speculation cache's hit rate).  Greedy sequences (whose outcome their drafts fix) and
  * failed ones get NaN, -1 and 0; a failed sequence reports the failures of
  * all its rows.                                                               */
 static int or_outcome_sequence(const void *target, const void *draft, int32_t b, int32_t K,
                                int32_t V, int dtype, double T, double beta, int32_t F,
-                               double *alpha, double *p_len, int32_t *top_tok, double *top_mass)
+                               double *alpha, double *p_len, int32_t *top_tok, double *top_mass,
+                               double *d4_mass)
 {
     for (int32_t j = 0; j < K; ++j) alpha[j] = NAN;
+    if (d4_mass)
+        for (int32_t j = 0; j < K; ++j) d4_mass[j] = NAN;
     for (int32_t k = 0; k <= K; ++k) {
         p_len[k] = NAN;
         for (int32_t f = 0; f < F; ++f) {
@@ -563,6 +570,13 @@ static int or_outcome_sequence(const void *target, const void *draft, int32_t b,
             }
         }
         if (k < K) alpha[k] = amin;
+        if (k < K && d4_mass) { /* residual mass on the draft row's top-4 */
+            int32_t t4[4];
+            int32_t n4 = oracle_row_top4(or_row_ptr(draft, dtype, (size_t)b * K + k, V), dtype, V, t4);
+            double m4 = 0.0;
+            for (int32_t q = 0; q < n4; ++q) m4 += r[t4[q]];
+            d4_mass[k] = m4;
+        }
         /* the F largest masses, ties to the lower token: F passes over V */
         for (int32_t f = 0; f < F; ++f) {
             int32_t best = -1;
@@ -582,6 +596,8 @@ static int or_outcome_sequence(const void *target, const void *draft, int32_t b,
     free(r);
     if (err) {
         for (int32_t j = 0; j < K; ++j) alpha[j] = NAN;
+        if (d4_mass)
+            for (int32_t j = 0; j < K; ++j) d4_mass[j] = NAN;
         for (int32_t k = 0; k <= K; ++k)
             for (int32_t f = 0; f < F; ++f) {
                 top_tok[(size_t)k * F + f] = -1;
@@ -601,7 +617,8 @@ static int or_outcome_sequence(const void *target, const void *draft, int32_t b,
 int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32_t B, int32_t K,
                                     int32_t V, int32_t dtype, const float *temperature, double beta,
                                     int32_t F, double *accept_rate, double *p_len, int32_t *top_tokens,
-                                    double *top_mass, int32_t *seq_error, int32_t nthreads)
+                                    double *top_mass, double *draft_top_mass, int32_t *seq_error,
+                                    int32_t nthreads)
 {
     int32_t all_err = 0;
 #ifdef _OPENMP
@@ -612,7 +629,8 @@ int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32
         int e = or_outcome_sequence(target, draft, b, K, V, dtype, (double)temperature[b], beta, F,
                                     accept_rate + (size_t)b * K, p_len + (size_t)b * (K + 1),
                                     top_tokens + (size_t)b * (K + 1) * F,
-                                    top_mass + (size_t)b * (K + 1) * F);
+                                    top_mass + (size_t)b * (K + 1) * F,
+                                    draft_top_mass ? draft_top_mass + (size_t)b * K : NULL);
         if (seq_error) seq_error[b] = e;
         all_err |= e;
     }

@@ -14,7 +14,7 @@ import itertools
 import numpy as np
 import pytest
 
-from pins import (chi2_pvalue, draft_law, exact_values, sample_categorical, softmax,
+from pins import (binom_pvalue, chi2_pvalue, draft_law, exact_values, sample_categorical, softmax,
                   to_bf16_bits)
 
 
@@ -261,3 +261,60 @@ def test_outcome_row_failures_are_all_reported(oracle_mod):
     assert res["seq_error"][0] == oracle_mod.ERR_ROW | oracle_mod.ERR_DRAFT_MASS
     assert np.all(np.isnan(res["p_len"][0])) and np.all(res["top_tokens"][0] == -1)
     assert res["seq_error"][1] == 0 and abs(res["p_len"][1].sum() - 1.0) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Residual mass on the draft's top-4 (the tokens beta down-weights), the
+# quantity behind the hit rate of SSD's speculation cache ("Key claims":
+# Saguaro sampling concentrates the residual on the draft's likeliest tokens).
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_draft_top_mass_closed_forms_and_monotone_in_beta(oracle_mod, dtype):
+    """Pin: sum over the draft row's top-4 of max(p - q'_beta, 0), with q'_beta
+    from the pins' own draft law; at beta = 0 it is p(top-4) (q' vanishes
+    there); and it never grows with beta (q'_beta on the top-4 is
+    beta q / (1 - (1 - beta) q(top-4)), increasing in beta)."""
+    rng = np.random.default_rng(41)
+    V, K, T = 3000, 3, 0.8
+    tgt, drf = _rows(rng, V, K, noise=0.7)
+    traw, draw_ = (to_bf16_bits(tgt), to_bf16_bits(drf)) if dtype == "bf16" else (tgt, drf)
+    prev = None
+    for beta in (1.0, 0.8, 0.5, 0.2, 0.05, 0.0):
+        res = oracle_mod.outcomes(traw[None], draw_[None], np.float32(T), beta, F=2)
+        assert res["error"] == 0
+        p, q = _laws(traw, draw_, T, beta)
+        dz = exact_values(draw_)
+        for k in range(K):
+            top = np.lexsort((np.arange(V), -dz[k]))[:4]
+            want = np.maximum(p[k] - q[k], 0.0)[top].sum()
+            assert abs(res["draft_top_mass"][0, k] - want) < 1e-12
+            if beta == 0.0:
+                assert abs(res["draft_top_mass"][0, k] - p[k][top].sum()) < 1e-12
+        if prev is not None:
+            assert np.all(res["draft_top_mass"][0] >= prev - 1e-15)
+        prev = res["draft_top_mass"][0]
+
+
+def test_draft_top_mass_is_the_sampler_hit_rate(oracle_mod):
+    """Pin: the oracle's sampler, with drafts from the beta-weighted draft
+    law, emits its bonus among the draft row's top-4 with probability
+    sum_k P(n = k) draft_top_mass_k / (1 - alpha_k) over rejections."""
+    rng = np.random.default_rng(43)
+    V, K, T, beta = 40, 2, 1.0, 0.3
+    tgt, drf = _rows(rng, V, K, noise=0.8)
+    p, q = _laws(tgt, drf, T, beta)
+    ntrials = 200_000
+    tokens = np.stack([sample_categorical(rng, q[i], ntrials) for i in range(K)], axis=1)
+    target = np.ascontiguousarray(np.broadcast_to(tgt, (ntrials,) + tgt.shape))
+    draft = np.ascontiguousarray(np.broadcast_to(drf, (ntrials,) + drf.shape))
+    run = oracle_mod.spec_verify(target, draft, tokens.astype(np.int32), 5, np.float32(T), beta)
+    n = run["accepted_len"]
+    bonus = run["out_tokens"][np.arange(ntrials), n]
+    res = oracle_mod.outcomes(tgt[None], drf[None], np.float32(T), beta, F=1)
+    reach = np.concatenate(([1.0], np.cumprod(res["accept_rate"][0])))
+    for k in range(K):
+        top = set(np.lexsort((np.arange(V), -drf[k].astype(np.float64)))[:4].tolist())
+        hit = np.array([b in top for b in bonus[n == k]])
+        want = min(1.0, res["draft_top_mass"][0, k] / (1.0 - res["accept_rate"][0, k]))
+        assert binom_pvalue(int(hit.sum()), int(hit.size), want) > 0.01, k
+        assert abs((n == k).mean() - reach[k] * (1 - res["accept_rate"][0, k])) < 5e-3
