@@ -17,7 +17,8 @@ Prints one JSON line:
 With --outcomes F a step is instead one spec_verify_outcomes call (the
 verification-outcome distribution with F ranked bonus tokens per position);
 its roofline is the outcome-pass kernel's, and its step roofline counts the
-two reads of every row the outcome law needs.
+two reads of every row the outcome law needs.  --beta-sweep prints the exact
+acceptance and bonus-in-draft-top-4 rates over a grid of beta instead.
 """
 from __future__ import annotations
 
@@ -197,6 +198,72 @@ def bench_outcomes(args, sv, w, base, dev) -> dict:
     return rec
 
 
+BETA_GRID = (1.0, 0.9, 0.75, 0.5, 0.3, 0.2, 0.1, 0.05, 0.0)
+
+
+def bench_beta_sweep(args, sv, w, base, dev) -> dict:
+    """The acceptance / cache-hit trade-off of beta ("Speculative Speculative
+    Decoding", Key claims and Results: lower beta raises the chance that the
+    bonus token is one the draft ranks highest, at some cost in acceptance).
+    For each beta the draft law is q'_beta and spec_verify_outcomes gives, per
+    sequence, the exact accept rates, the length law and the residual mass on
+    each draft row's top-4 (the tokens beta down-weights); from them:
+      mean_accept        mean alpha over positions and sequences
+      tokens_per_verify  E[n] + 1 (accepted drafts plus the bonus)
+      hit_given_reject   P(bonus among the draft's top-4 | a rejection)
+    No sampling: these are the exact expectations for the synthetic logits."""
+    import torch
+
+    F = 4
+    n = sv.outcomes_workspace_size(w.B, w.K, w.V, base["target"].dtype, F)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ks = torch.arange(w.K + 1, device=dev, dtype=torch.float64)
+    rows = []
+    total_ms = 0.0
+    for beta in BETA_GRID:
+        call = sv.Outcomes(base["target"], base["draft"], base["temperature"], beta, F, workspace=ws,
+                           stream=stream, draft_top=True)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        total_ms += ms
+        o = call.out
+        alpha = o["accept_rate"].double()
+        plen = o["p_len"].double()
+        reach = torch.cat([torch.ones_like(alpha[:, :1]), torch.cumprod(alpha, 1)], 1)[:, :w.K]
+        hit = (reach * o["draft_top_mass"].double()).sum()
+        rej = plen[:, :w.K].sum()
+        rows.append({"beta": beta, "mean_accept": float(alpha.mean()),
+                     "tokens_per_verify": float((plen * ks).sum(1).mean() + 1.0),
+                     "p_reject": float(rej / w.B),
+                     "hit_given_reject": float(hit / rej),
+                     "call_us": ms * 1e3,
+                     "error_word": int(o["error_word"].item())})
+    logits = w.B * (w.K + 1) * w.V
+    ms_mean = total_ms / len(BETA_GRID)
+    return {
+        "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
+        "value": logits / (ms_mean * 1e-3), "unit": "logits/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_mean,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.tag() + "_beta_sweep", "B": w.B, "K": w.K, "V": w.V,
+                   "what": "beta sweep of spec_verify_outcomes (hit set: each draft row's top-4)",
+                   "temperature": w.temperature if w.temperature is not None
+                   else f"U[{w.t_lo},{w.t_hi}] per sequence",
+                   "parallelism": "single GPU"},
+        "sweep": rows,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +278,9 @@ def main() -> int:
     ap.add_argument("--outcomes", type=int, default=0, metavar="F",
                     help="instead, time the verification-outcome distribution with F ranked "
                          "bonus tokens per position (spec_verify_outcomes)")
+    ap.add_argument("--beta-sweep", action="store_true",
+                    help="instead, the exact acceptance / bonus-in-draft-top-4 trade-off over a "
+                         "grid of beta (spec_verify_outcomes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="instead, run torch copies of MB megabytes (counter calibration)")
     args = ap.parse_args()
@@ -243,6 +313,12 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
     base = make_inputs(w, seed=args.seed, device=dev)
+    if args.beta_sweep:
+        if w.greedy or args.ragged:
+            print("--beta-sweep needs a sampling workload without --ragged", file=sys.stderr)
+            return 2
+        print(json.dumps(bench_beta_sweep(args, sv, w, base, dev)), flush=True)
+        return 0
     if args.outcomes:
         if w.greedy or args.ragged:
             print("--outcomes needs a sampling workload without --ragged", file=sys.stderr)

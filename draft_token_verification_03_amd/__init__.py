@@ -77,8 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_stream_probe.restype = i32
     lib.spec_verify_outcomes_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.spec_verify_outcomes_workspace_size.restype = sz
-    lib.spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f32, i32, P, P, P, P, P, P, sz,
-                                         P, P, P]
+    lib.spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f32, i32, P, P, P, P, P, P, P,
+                                         sz, P, P, P]
     lib.spec_verify_outcomes.restype = i32
     lib.spec_verify_status_str.argtypes = [i32]
     lib.spec_verify_status_str.restype = ctypes.c_char_p
@@ -304,12 +304,13 @@ class Outcomes:
     [0, 1]; F ranked bonus tokens per position (0..32).  Each call returns a
     dict of accept_rate [B, K], p_len [B, K+1], top_tokens [B, K+1, F] int32,
     top_mass [B, K+1, F] (float32) and error_word [1] int32 (cleared before
-    every call).
+    every call); with draft_top=True also draft_top_mass [B, K], the residual
+    mass on each draft row's top-4.
     """
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor | None, temperature,
                  beta: float = 1.0, F: int = 8, *, workspace: torch.Tensor | None = None,
-                 stream=None):
+                 stream=None, draft_top: bool = False):
         if target.dim() != 3 or not target.is_contiguous():
             raise ValueError("target must be a contiguous [B, K+1, V] tensor")
         B, K1, V = target.shape
@@ -338,12 +339,14 @@ class Outcomes:
             "top_mass": torch.empty((B, K + 1, F), dtype=torch.float32, device=dev),
             "error_word": torch.zeros((1,), dtype=torch.int32, device=dev),
         }
+        if draft_top:
+            self.out["draft_top_mass"] = torch.empty((B, K), dtype=torch.float32, device=dev)
         o = self.out
         self._keep = (target, draft, temperature, workspace)
         self._args = (_ptr(target), _ptr(draft), B, K, V, code, _ptr(temperature),
                       ctypes.c_float(float(beta)), int(F), _ptr(o["accept_rate"]), _ptr(o["p_len"]),
-                      _ptr(o["top_tokens"]), _ptr(o["top_mass"]), _ptr(o["error_word"]),
-                      _ptr(workspace), workspace.numel())
+                      _ptr(o["top_tokens"]), _ptr(o["top_mass"]), _ptr(o.get("draft_top_mass")),
+                      _ptr(o["error_word"]), _ptr(workspace), workspace.numel())
         self._stream = _stream(stream)
 
     def __call__(self, pass_events=None) -> dict:
@@ -358,8 +361,11 @@ class Outcomes:
 
 
 def outcomes(target: torch.Tensor, draft: torch.Tensor | None, temperature, beta: float = 1.0,
-             F: int = 8, *, workspace: torch.Tensor | None = None, stream=None) -> dict:
+             F: int = 8, *, workspace: torch.Tensor | None = None, stream=None,
+             draft_top: bool = False) -> dict:
     """Verification-outcome distribution of every sequence: accept rates
     alpha_j, the law of the accepted length and the F likeliest bonus tokens
-    of each position with their residual masses (see Outcomes)."""
-    return Outcomes(target, draft, temperature, beta, F, workspace=workspace, stream=stream)()
+    of each position with their residual masses, and with draft_top=True the
+    residual mass on each draft row's top-4 (see Outcomes)."""
+    return Outcomes(target, draft, temperature, beta, F, workspace=workspace, stream=stream,
+                    draft_top=draft_top)()

@@ -97,6 +97,8 @@ bool make_outcome_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F
     off = align256(off + sizeof(OutRow) * (size_t)pos);
     op->off_asum = off;
     off = align256(off + sizeof(double) * (size_t)pos * op->nc2);
+    op->off_tsum = off;
+    off = align256(off + sizeof(double) * (size_t)pos * op->nc2);
     op->off_keys = off;
     off = align256(off + sizeof(uint64_t) * (size_t)pos * op->nc2 * F);
     op->bytes = off;
@@ -240,8 +242,8 @@ size_t spec_verify_outcomes_workspace_size(int32_t B, int32_t K, int32_t V, int3
 int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
                              int32_t V, int32_t dtype, const float *temperature, float beta, int32_t F,
                              float *accept_rate, float *p_len, int32_t *top_tokens, float *top_mass,
-                             int32_t *error_word, void *workspace, size_t workspace_bytes,
-                             void *pass_begin, void *pass_end, void *stream)
+                             float *draft_top_mass, int32_t *error_word, void *workspace,
+                             size_t workspace_bytes, void *pass_begin, void *pass_end, void *stream)
 {
     if (B < 0 || K < 0 || K > sv::kMaxK || V < 1) return SV_EINVAL;
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EINVAL;
@@ -271,7 +273,8 @@ int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits
         a.temperature = temperature + b0;
         a.beta = beta;
         a.log2_beta = std::log2((double)beta);
-        a.weighted = (beta < 1.f && K > 0) ? 1 : 0;
+        // the draft rows' top-4 are tracked for beta < 1, and for their residual mass
+        a.weighted = ((beta < 1.f || draft_top_mass) && K > 0) ? 1 : 0;
         a.sampling_only = 1;
         a.error_word = error_word;
         o.F = F;
@@ -279,11 +282,13 @@ int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits
         o.cvec2 = op.cvec2;
         o.rec = reinterpret_cast<sv::OutRow *>(w + op.off_rec);
         o.asum = reinterpret_cast<double *>(w + op.off_asum);
+        o.tsum = reinterpret_cast<double *>(w + op.off_tsum);
         o.keys = reinterpret_cast<uint64_t *>(w + op.off_keys);
         o.accept_rate = accept_rate ? accept_rate + (int64_t)b0 * K : nullptr;
         o.p_len = p_len + (int64_t)b0 * (K + 1);
         o.top_tokens = top_tokens ? top_tokens + (int64_t)b0 * (K + 1) * F : nullptr;
         o.top_mass = top_mass ? top_mass + (int64_t)b0 * (K + 1) * F : nullptr;
+        o.draft_top_mass = draft_top_mass ? draft_top_mass + (int64_t)b0 * K : nullptr;
         sv::launch_outcomes(o, s, b0 == 0 ? static_cast<hipEvent_t>(pass_begin) : nullptr,
                             b0 == 0 ? static_cast<hipEvent_t>(pass_end) : nullptr);
     }

@@ -112,7 +112,7 @@ struct OutRow {
 struct OutPlan {
     Plan p;                   // the streaming pass (its part/top/tope regions)
     int32_t F, nc2, cvec2;    // ranked tokens; outcome chunks per position, vectors per chunk
-    size_t off_rec, off_asum, off_keys;
+    size_t off_rec, off_asum, off_tsum, off_keys;
     size_t bytes;
 };
 
@@ -123,11 +123,13 @@ struct OutArgs {
     int32_t F, nc2, cvec2;
     OutRow *rec;              // [sB][K+1]
     double *asum;             // [sB][K+1][nc2] sum of min(p, q') D over the chunk (j < K)
+    double *tsum;             // [sB][K+1][nc2] r D summed over the draft's top-4 in the chunk (j < K)
     uint64_t *keys;           // [sB][K+1][nc2][F] the chunk's best keys, descending, 0 = none
     float *accept_rate;       // [sB][K]
     float *p_len;             // [sB][K+1]
     int32_t *top_tokens;      // [sB][K+1][F]
     float *top_mass;          // [sB][K+1][F]
+    float *draft_top_mass;    // [sB][K] r summed over each draft row's top-4, or null
 };
 
 // Launchers of one sub-batch: the verify step (non-null events are recorded

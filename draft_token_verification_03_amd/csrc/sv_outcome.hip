@@ -198,7 +198,7 @@ struct PosConst {
 // exact path).  The exact path keys every token whose p D reaches the floor.
 template <int DT, bool TOP>
 __device__ __forceinline__ void pair_tile(const PairTile &tl, int qb, int V, const PosConst &pc,
-                                          uint64_t *slots, double &run)
+                                          uint64_t *slots, double &run, double &tmass)
 {
     constexpr int VEC = Elt<DT>::kVec;
     const uint64_t fkey = pc.F ? slot_read(&slots[pc.F - 1]) : 0;
@@ -246,9 +246,9 @@ __device__ __forceinline__ void pair_tile(const PairTile &tl, int qb, int V, con
             const float B = __builtin_fmaf(y[k], pc.e.c, -pc.od);
             const bool mem = TOP && y[k] >= pc.z4 && top_has(pc.top, idx);
             if (mem) {  // replace the unweighted term summed above by the weighted one
-                const float ea = __builtin_amdgcn_exp2f(A);
-                corr += (double)fminf(ea, __builtin_amdgcn_exp2f(B + pc.lbeta)) -
-                        (double)fminf(ea, __builtin_amdgcn_exp2f(B));
+                const float ea = __builtin_amdgcn_exp2f(A), ew = __builtin_amdgcn_exp2f(B + pc.lbeta);
+                corr += (double)fminf(ea, ew) - (double)fminf(ea, __builtin_amdgcn_exp2f(B));
+                tmass += (double)fmaxf(ea - ew, 0.f);  // r D of a top-4 token
             }
             if (A != -INFINITY && A >= lf) {
                 const float rD = __builtin_amdgcn_exp2f(A) - __builtin_amdgcn_exp2f(mem ? B + pc.lbeta : B);
@@ -430,12 +430,17 @@ __device__ __forceinline__ void outcome_position(const OutArgs &o, const char *t
         pc.top = ps.top;
         pc.z4 = TOP ? pc.top.v[3] : INFINITY;
         pc.F = F;
-        double run = 0.0;
+        double run = 0.0, tmass = 0.0;
         stream_pair<DT, ALIGNED, true>(trow, drow, q0, q1, a.V, ra, [&](PairTile &t, int qb) {
-            pair_tile<DT, TOP>(t, qb, a.V, pc, slots, run);
+            pair_tile<DT, TOP>(t, qb, a.V, pc, slots, run, tmass);
         });
         const double s = block_sum(run, lds_d);  // its barrier orders every insert before the reads
         if (tid == 0) o.asum[posi * o.nc2 + chunk] = s;
+        if (TOP) {
+            __syncthreads();  // lds_d is reused
+            const double tsum = block_sum(tmass, lds_d);
+            if (tid == 0) o.tsum[posi * o.nc2 + chunk] = tsum;
+        }
     } else {
         stream_pair<DT, ALIGNED, false>(trow, nullptr, q0, q1, a.V, ra, [&](PairTile &t, int qb) {
             last_tile<DT>(t, qb, F, slots);
@@ -511,7 +516,10 @@ __global__ __launch_bounds__(kBlock) void outcome_finish_kernel(const OutArgs o)
     }
     if (err || none) {
         if (err && tid == 0 && a.error_word) atomicOr(a.error_word, err);
-        for (int j = tid; j < K; j += kBlock) ar[j] = NAN;
+        for (int j = tid; j < K; j += kBlock) {
+            ar[j] = NAN;
+            if (o.draft_top_mass) o.draft_top_mass[(int64_t)b * K + j] = NAN;
+        }
         for (int j = tid; j < P; j += kBlock) pl[j] = NAN;
         for (int j = tid; j < P * F; j += kBlock) {
             tt[j] = -1;
@@ -528,6 +536,12 @@ __global__ __launch_bounds__(kBlock) void outcome_finish_kernel(const OutArgs o)
             for (int c = lane; c < o.nc2; c += 64) s += o.asum[base + c];
             s = wave_sum(s);
             if (lane == 0) alpha_s[j] = fmin(fmax(s / rr.norm, 0.0), 1.0);
+            if (o.draft_top_mass) {
+                double t = 0.0;
+                for (int c = lane; c < o.nc2; c += 64) t += o.tsum[base + c];
+                t = wave_sum(t);
+                if (lane == 0) o.draft_top_mass[(int64_t)b * K + j] = (float)(t / rr.norm);
+            }
         }
         const bool own0 = lane < o.nc2, own1 = lane + 64 < o.nc2;
         const uint64_t *k0 = o.keys + (base + lane) * F;

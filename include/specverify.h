@@ -200,6 +200,13 @@ int32_t spec_verify_stream_probe(const void *target_logits, const void *draft_lo
  *                           lower token id; -1 past the positive ones
  *   top_mass    [B, K+1, F] those r_k(v) (p_K(v)), 0 past the positive ones;
  *                           P(n = k, bonus = v) = prod_{j<k} alpha_j * r_k(v)
+ *   draft_top_mass [B, K]   optional (NULL: not formed): sum of r_k(v) over
+ *                           the 4 largest logits of draft row k (ties to the
+ *                           lower id), the tokens beta down-weights; the bonus
+ *                           of a rejection at k is one of them with probability
+ *                           draft_top_mass_k / (1 - alpha_k) ("Key claims":
+ *                           Saguaro sampling concentrates the residual there
+ *                           to raise the speculation cache's hit rate)
  * p, q' and beta as in spec_verify; all K positions of every sequence are
  * used, whatever was drafted.  Outputs are float32 (alpha clamped to [0, 1]);
  * the r values are ranked as computed in fp32, so tokens whose masses agree
@@ -227,8 +234,8 @@ size_t spec_verify_outcomes_workspace_size(int32_t B, int32_t K, int32_t V, int3
 int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits, int32_t B, int32_t K,
                              int32_t V, int32_t dtype, const float *temperature, float beta, int32_t F,
                              float *accept_rate, float *p_len, int32_t *top_tokens, float *top_mass,
-                             int32_t *error_word, void *workspace, size_t workspace_bytes,
-                             void *pass_begin, void *pass_end, void *stream);
+                             float *draft_top_mass, int32_t *error_word, void *workspace,
+                             size_t workspace_bytes, void *pass_begin, void *pass_end, void *stream);
 
 /* Static description of a status code. */
 const char *spec_verify_status_str(int32_t status);

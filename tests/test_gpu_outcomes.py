@@ -42,9 +42,10 @@ def _say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(sv, inp: dict, F: int, draft_none: bool = False, workspace=None) -> dict:
+def run_gpu(sv, inp: dict, F: int, draft_none: bool = False, workspace=None,
+            draft_top: bool = False) -> dict:
     res = sv.outcomes(inp["target"], None if draft_none else inp["draft"], inp["temperature"],
-                      inp["beta"], F, workspace=workspace)
+                      inp["beta"], F, workspace=workspace, draft_top=draft_top)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in res.items()}
     g["error_word"] = int(g["error_word"][0])
@@ -65,10 +66,15 @@ def check(g: dict, o: dict, F: int, tol: float = 1e-5) -> dict:
     for b in range(B):
         if np.isnan(o["p_len"][b, 0]):
             ok = (np.all(np.isnan(g["p_len"][b])) and np.all(np.isnan(g["accept_rate"][b]))
-                  and np.all(g["top_tokens"][b] == -1) and np.all(g["top_mass"][b] == 0.0))
+                  and np.all(g["top_tokens"][b] == -1) and np.all(g["top_mass"][b] == 0.0)
+                  and ("draft_top_mass" not in g or np.all(np.isnan(g["draft_top_mass"][b]))))
             if not ok:
                 fails.append(f"seq {b}: expected NaN/-1/0 outputs")
             continue
+        if "draft_top_mass" in g:
+            et = np.abs(g["draft_top_mass"][b].astype(np.float64) - o["draft_top_mass"][b])
+            if et.max(initial=0.0) > tol:
+                fails.append(f"seq {b}: draft top-4 residual mass err {et.max():.3g}")
         ea = np.abs(g["accept_rate"][b].astype(np.float64) - o["accept_rate"][b])
         ep = np.abs(g["p_len"][b].astype(np.float64) - o["p_len"][b])
         max_err = max(max_err, float(ea.max(initial=0.0)), float(ep.max()))
@@ -311,3 +317,35 @@ def test_outcome_pass_is_timed(sv):
     run(pass_events=ev)
     torch.cuda.synchronize()
     assert ev[0].elapsed_time(ev[1]) > 0.0
+
+
+@pytest.mark.parametrize("name,B,V", [("C4", 10, 152064), ("C5", 8, 128256), ("C2", 6, 30011),
+                                      ("C5", 40, 2053)])
+def test_draft_top_mass_across_beta(sv, oracle_mod, name, B, V):
+    """The residual mass on each draft row's top-4 (and every other output)
+    for beta from 1 (the top-4 tracked only for this output) to 0, with one
+    and several chunks a row."""
+    w = WORKLOADS[name].sized(B=B, V=V)
+    inp = make_inputs(w, seed=31, device="cuda")
+    h = to_numpy_inputs(inp)
+    for beta in (1.0, 0.7, 0.3, 0.0):
+        _say(f"draft top-4 mass {name} B={B} V={V} beta={beta}")
+        inp["beta"] = h["beta"] = beta
+        g = run_gpu(sv, inp, 4, draft_top=True)
+        o = run_oracle(oracle_mod, h, 4)
+        check(g, o, 4)
+        assert g["error_word"] == int(np.bitwise_or.reduce(o["seq_error"]))
+
+
+def test_draft_top_mass_error_paths(sv, oracle_mod):
+    rng = np.random.default_rng(9)
+    B, K, V = 4, 2, 3001
+    tgt = rng.normal(size=(B, K + 1, V)).astype(np.float32)
+    drf = rng.normal(size=(B, K, V)).astype(np.float32)
+    tgt[1, 0, :] = -np.inf
+    temps = np.array([1.0, 1.0, 0.0, np.inf], np.float32)
+    inp = _inputs(tgt, drf, temps, 1.0, "bf16")
+    g = run_gpu(sv, inp, 3, draft_top=True)
+    o = run_oracle(oracle_mod, _host(inp), 3)
+    check(g, o, 3)
+    assert np.all(np.isnan(g["draft_top_mass"][1:]))
