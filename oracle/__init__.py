@@ -32,6 +32,7 @@ ERR_ROW = 4
 ERR_DRAFT_MASS = 8
 ERR_NO_DRAFT = 16
 ERR_DRAFT_LEN = 32
+ERR_TREE = 64
 
 _lib = None
 
@@ -80,6 +81,9 @@ def _load():
     lib.oracle_spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f64, i32, P, P, P, P, P,
                                                 P, i32]
     lib.oracle_spec_verify_outcomes.restype = i32
+    lib.oracle_spec_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P, P, P, P,
+                                            i32]
+    lib.oracle_spec_verify_tree.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
     lib.oracle_spec_verify.restype = i32
@@ -253,5 +257,40 @@ def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: fl
         int(nthreads))
     if K > 0 and d_raw is None:
         res["draft_top_mass"][:] = np.nan
+    res["error"] = int(err)
+    return res
+
+
+def spec_verify_tree(target: np.ndarray, draft: np.ndarray | None, parent: np.ndarray,
+                     tokens: np.ndarray, seed: int, temperature, seq_ids=None,
+                     nthreads: int = 0) -> dict:
+    """Tree verification of every sequence (see the C source): target
+    [B, N+1, V], draft [B, N, V] (row c: the law the children of context c
+    were drawn from), parent and tokens [B, N] int32.  Returns accepted_len
+    [B], out_tokens [B, N+1], path [B, N], margin [B], seq_error [B], error."""
+    lib = _load()
+    t_raw, dt = _as_raw(target)
+    B, N1, V = t_raw.shape
+    N = N1 - 1
+    d_raw = None
+    if draft is not None:
+        d_raw, dt2 = _as_raw(draft)
+        assert dt2 == dt and d_raw.shape == (B, N, V)
+    parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, N)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, N)
+    temp = np.asarray(temperature, dtype=np.float32)
+    if temp.ndim == 0:
+        temp = np.full(B, temp, dtype=np.float32)
+    temp = np.ascontiguousarray(temp)
+    ids = None if seq_ids is None else np.ascontiguousarray(seq_ids, dtype=np.int32)
+    res = {"accepted_len": np.zeros(B, dtype=np.int32),
+           "out_tokens": np.zeros((B, N + 1), dtype=np.int32),
+           "path": np.zeros((B, N), dtype=np.int32),
+           "margin": np.zeros(B, dtype=np.float64),
+           "seq_error": np.zeros(B, dtype=np.int32)}
+    err = lib.oracle_spec_verify_tree(
+        _ptr(t_raw), _ptr(d_raw), _ptr(parent), _ptr(tokens), B, N, V, dt, int(seed) & (2**64 - 1),
+        _ptr(temp), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["path"]),
+        _ptr(res["margin"]), _ptr(res["seq_error"]), _ptr(ids), int(nthreads))
     res["error"] = int(err)
     return res

@@ -51,7 +51,12 @@
  *    draft law the verify step assumes, for all K positions whatever was
  *    drafted; "the most likely bonus tokens" of a position are ranked by the
  *    clamped residual mass max(p - q', 0) (target mass at position K), ties
- *    to the lower token id; greedy sequences have no outcome law (NaN).
+ *    to the lower token id; greedy sequences have no outcome law (NaN);
+ *  - tree verification (named on the pages without a rule) follows the
+ *    published recursive rejection sampling: children of a context are tried
+ *    in node order against the current law, which a rejection replaces by
+ *    its normalised residual; node j's test uses u(b, j, 0), the bonus
+ *    u(b, d, 1) with d the accepted depth, so a chain is the verify step.
  */
 #include <math.h>
 #include <stdint.h>
@@ -73,6 +78,7 @@
 #define OR_ERR_DRAFT_MASS 8  /* beta re-weighting left zero draft mass    */
 #define OR_ERR_NO_DRAFT 16   /* T > 0 and K > 0 but no draft logits given */
 #define OR_ERR_DRAFT_LEN 32  /* a ragged draft length outside [0, K]       */
+#define OR_ERR_TREE 64       /* a tree parent outside [-1, i-1]           */
 
 /* ------------------------------------------------------------------ */
 /* Philox4x32-10 (SC'11): 10 rounds of a multiply/xor S-box; the 2-word key
@@ -631,6 +637,206 @@ int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32
                                     top_tokens + (size_t)b * (K + 1) * F,
                                     top_mass + (size_t)b * (K + 1) * F,
                                     draft_top_mass ? draft_top_mass + (size_t)b * K : NULL);
+        if (seq_error) seq_error[b] = e;
+        all_err |= e;
+    }
+    return all_err;
+}
+
+/* ------------------------------------------------------------------ */
+/* Tree (multi-draft) verification.  The pages name tree-based speculative
+ * decoding ("Speculative Speculative Decoding", Key claims: SSD composes with
+ * Medusa-style trees) but give no verify rule for it; this is the published
+ * recursive rejection sampling over a token tree (Miao et al., "SpecInfer",
+ * ASPLOS'24, multi-step speculative sampling), which keeps the output law
+ * the target's when the children of a context are drawn i.i.d. from its
+ * draft law.
+ *  - Node i in [0, N) has parent[i] in [-1, i-1] (-1: the root) and token x_i.
+ *    Context 0 is the root and context i + 1 is node i: target row c holds
+ *    the target logits after context c (N + 1 rows), draft row c (c < N) the
+ *    draft logits the children of context c were drawn from.
+ *  - At the current context the law is r = p_t (its target row).  Its
+ *    children are tried in ascending node index: child j with token x is
+ *    accepted iff u(b, j, 0) <= r(x) / q(x); on a rejection
+ *    r <- max(r - q, 0) / sum_v max(r - q, 0) (kept as it is if that sum is
+ *    zero).  An accepted child becomes the current context.  When no child
+ *    is left (none, or all rejected) the bonus is the smallest v with
+ *    C(v) >= u(b, d, 1) C(V-1), C the running sum of r in token order, d the
+ *    number of accepted nodes.
+ *  - Greedy (T == 0): the first child whose token is the target argmax is
+ *    accepted; the bonus is the final context's argmax.
+ * A chain (parent[i] = i - 1) is the verify step with K = N, uniforms
+ * included.  Outputs: accepted_len[b] = d, out_tokens[b, 0..d-1] the accepted
+ * tokens and out_tokens[b, d] the bonus (-1 after), path[b, 0..d-1] the
+ * accepted nodes (-1 after), margin[b] the smallest |u - ratio| or |u - C/Z|
+ * over the decisions taken (for parity checks).  Only the rows the walk
+ * visits are checked for finite maxima.                                      */
+static double or_nested(double r, double q, const double *Z, int32_t nZ)
+{
+    for (int32_t i = 0; i < nZ; ++i) {
+        double d = r - q;
+        r = (d > 0.0 ? d : 0.0) / Z[i];
+    }
+    return r;
+}
+
+static int or_tree_sequence(const void *target, const void *draft, const int32_t *parent,
+                            const int32_t *tokens, int32_t N, int32_t V, int dtype, uint64_t seed,
+                            uint32_t gb, double T, int32_t *acc, int32_t *out, int32_t *path,
+                            double *margin)
+{
+    *acc = 0;
+    for (int32_t j = 0; j <= N; ++j) out[j] = -1;
+    for (int32_t j = 0; j < N; ++j) path[j] = -1;
+    *margin = NAN;
+    for (int32_t i = 0; i < N; ++i)
+        if (parent[i] < -1 || parent[i] >= i) return OR_ERR_TREE;
+    if (!(T >= 0.0) || isinf(T)) return OR_ERR_TEMPERATURE;
+    int err = 0;
+    int32_t cur = -1, d = 0;
+    if (T == 0.0) {
+        for (;;) {
+            const void *row = or_row_ptr(target, dtype, (size_t)(cur + 1), V);
+            if (!isfinite(oracle_row_max(row, dtype, V))) {
+                for (int32_t j = 0; j <= N; ++j) out[j] = -1;
+                for (int32_t j = 0; j < N; ++j) path[j] = -1;
+                *acc = 0;
+                return err | OR_ERR_ROW;
+            }
+            const int32_t a = oracle_row_argmax(row, dtype, V);
+            int32_t next = -1;
+            for (int32_t j = cur + 1; j < N && next < 0; ++j) {
+                if (parent[j] != cur) continue;
+                if (tokens[j] < 0 || tokens[j] >= V) err |= OR_ERR_TOKEN;
+                if (tokens[j] == a) next = j;
+            }
+            if (next < 0) {
+                out[d] = a;
+                *acc = d;
+                return err;
+            }
+            out[d] = a;
+            path[d] = next;
+            ++d;
+            cur = next;
+        }
+    }
+    if (N > 0 && draft == NULL) return OR_ERR_NO_DRAFT;
+    double *Z = (double *)malloc(sizeof(double) * (size_t)(N + 1));
+    double mg = INFINITY;
+    or_row rt, rd;
+    int32_t nZ = 0;
+    for (;;) {
+        int e = or_prepare(&rt, or_row_ptr(target, dtype, (size_t)(cur + 1), V), dtype, V, T, 0, 1.0);
+        int have_child = 0;
+        for (int32_t j = cur + 1; j < N; ++j) have_child |= parent[j] == cur;
+        if (!e && have_child) e = or_prepare(&rd, or_row_ptr(draft, dtype, (size_t)(cur + 1), V), dtype, V, T, 0, 1.0);
+        if (e) {
+            free(Z);
+            for (int32_t j = 0; j <= N; ++j) out[j] = -1;
+            for (int32_t j = 0; j < N; ++j) path[j] = -1;
+            *acc = 0;
+            *margin = NAN;
+            return err | e;
+        }
+        nZ = 0;
+        int32_t next = -1;
+        for (int32_t j = cur + 1; j < N && next < 0; ++j) {
+            if (parent[j] != cur) continue;
+            const int32_t x = tokens[j];
+            double ratio;
+            double qx = 0.0;
+            if (x < 0 || x >= V) {
+                err |= OR_ERR_TOKEN;
+                ratio = 0.0;
+            } else {
+                const double lq = or_logprob(&rd, x);
+                qx = exp(lq);
+                const double rx = or_nested(exp(or_logprob(&rt, x)), qx, Z, nZ);
+                ratio = (lq == -INFINITY) ? INFINITY : rx / qx;
+            }
+            const double u = oracle_uniform(seed, gb, (uint32_t)j, OR_ACCEPT);
+            const double m = fabs(u - ratio);
+            if (m < mg) mg = m;
+            if (u <= ratio) {
+                next = j;
+                break;
+            }
+            /* the law after this rejection */
+            double z = 0.0;
+            for (int32_t v = 0; v < V; ++v) {
+                const double qv = exp(or_logprob(&rd, v));
+                const double dv = or_nested(exp(or_logprob(&rt, v)), qv, Z, nZ) - qv;
+                z += dv > 0.0 ? dv : 0.0;
+            }
+            if (z > 0.0) Z[nZ++] = z;
+        }
+        if (next >= 0) {
+            out[d] = tokens[next];
+            path[d] = next;
+            ++d;
+            cur = next;
+            continue;
+        }
+        /* bonus from the current law */
+        double *w = (double *)malloc(sizeof(double) * (size_t)V);
+        double S = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            const double pv = exp(or_logprob(&rt, v));
+            w[v] = nZ ? or_nested(pv, exp(or_logprob(&rd, v)), Z, nZ) : pv;
+            S += w[v];
+        }
+        const double uB = oracle_uniform(seed, gb, (uint32_t)d, OR_BONUS);
+        const double thr = uB * S;
+        double C = 0.0, Cprev = 0.0;
+        int32_t bonus = -1;
+        for (int32_t v = 0; v < V; ++v) {
+            Cprev = C;
+            C += w[v];
+            if (C >= thr) {
+                bonus = v;
+                break;
+            }
+        }
+        if (bonus < 0) {
+            for (int32_t v = V - 1; v >= 0; --v)
+                if (w[v] > 0.0) {
+                    bonus = v;
+                    break;
+                }
+            C = S;
+        }
+        const double m1 = fabs(uB - Cprev / S), m2 = fabs(uB - C / S);
+        if (m1 < mg) mg = m1;
+        if (m2 < mg) mg = m2;
+        free(w);
+        free(Z);
+        out[d] = bonus;
+        *acc = d;
+        *margin = mg;
+        return err;
+    }
+}
+
+int32_t oracle_spec_verify_tree(const void *target, const void *draft, const int32_t *parent,
+                                const int32_t *tokens, int32_t B, int32_t N, int32_t V, int32_t dtype,
+                                uint64_t seed, const float *temperature, int32_t *accepted_len,
+                                int32_t *out_tokens, int32_t *path, double *margin, int32_t *seq_error,
+                                const int32_t *seq_ids, int32_t nthreads)
+{
+    int32_t all_err = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : all_err)
+#endif
+    for (int32_t b = 0; b < B; ++b) {
+        const size_t tr = (size_t)b * (N + 1), dr = (size_t)b * N;
+        int e = or_tree_sequence(or_row_ptr(target, dtype, tr, V),
+                                 draft ? or_row_ptr(draft, dtype, dr, V) : NULL,
+                                 parent + (size_t)b * N, tokens + (size_t)b * N, N, V, dtype, seed,
+                                 seq_ids ? (uint32_t)seq_ids[b] : (uint32_t)b,
+                                 (double)temperature[b], accepted_len + b, out_tokens + (size_t)b * (N + 1),
+                                 path + (size_t)b * N, margin + b);
         if (seq_error) seq_error[b] = e;
         all_err |= e;
     }
