@@ -18,7 +18,9 @@ With --outcomes F a step is instead one spec_verify_outcomes call (the
 verification-outcome distribution with F ranked bonus tokens per position);
 its roofline is the outcome-pass kernel's, and its step roofline counts the
 two reads of every row the outcome law needs.  --beta-sweep prints the exact
-acceptance and bonus-in-draft-top-4 rates over a grid of beta instead.
+acceptance and bonus-in-draft-top-4 rates over a grid of beta instead, and
+--tree K1,K2,... times tree verification (spec_verify_tree) of trees with
+that branching per depth.
 """
 from __future__ import annotations
 
@@ -41,8 +43,9 @@ DEFAULT_WORKLOAD = "C2"
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = "draft_token_verification_03_amd/csrc/"
-    for rel in (csrc + "sv_api.hip", csrc + "sv_verify.hip", csrc + "sv_outcome.hip",
+    for rel in (csrc + "sv_api.hip", csrc + "sv_verify.hip", csrc + "sv_outcome.hip", csrc + "sv_tree.hip",
                 csrc + "sv_device.h", csrc + "sv_internal.h", csrc + "sv_accept.h", csrc + "sv_tile.h",
+                csrc + "sv_stream.h",
                 "include/specverify.h"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
@@ -198,6 +201,127 @@ def bench_outcomes(args, sv, w, base, dev) -> dict:
     return rec
 
 
+def tree_rows_read(parent, path, acc, greedy) -> int:
+    """Logit rows the tree walk streams for one sequence: at every visited
+    context one pass over its target row (and draft row when it has
+    children), one pass over both rows per rejected child, and at the final
+    context a target-row pass for the bonus when no child was rejected
+    there (greedy: one target-row pass per visited context)."""
+    N = parent.size
+    rows = 0
+    cur = -1
+    for k in range(acc + 1):
+        kids = [j for j in range(cur + 1, N) if parent[j] == cur]
+        if greedy:
+            rows += 1
+        else:
+            rows += 1 + (1 if kids else 0)
+            if k < acc:
+                rejected = kids.index(int(path[k]))
+            else:
+                rejected = len(kids)
+                if rejected == 0:
+                    rows += 1
+            rows += 2 * rejected
+        if k < acc:
+            cur = int(path[k])
+    return rows
+
+
+def bench_tree(args, sv, w, dev) -> dict:
+    """One step = one spec_verify_tree call over a batch of token trees of
+    the given branching (one workgroup per sequence)."""
+    import numpy as np
+    import torch
+
+    import oracle  # noqa: F401  (cpu_baseline below)
+    from workload import make_tree_inputs
+
+    shape = tuple(int(x) for x in args.tree.split(",") if x)
+    base = make_tree_inputs(w, shape, seed=args.seed, device=dev)
+    N = base["parent"].shape[1]
+    row_bytes = w.V * w.elt_bytes
+    all_bytes = w.B * (2 * N + 1) * row_bytes
+    reps = max(2, math.ceil(2 * MALL_BYTES / all_bytes))
+    replicas = [base] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in base.items()}
+                         for _ in range(reps - 1)]
+    stream = torch.cuda.current_stream()
+    calls = [sv.TreeVerifier(r["target"], None if w.greedy else r["draft"], r["parent"], r["tokens"],
+                             r["temperature"], stream=stream) for r in replicas]
+    for k in range(args.warmup):
+        calls[k % reps](args.seed + k)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        calls[(args.warmup + k) % reps](args.seed + args.warmup + k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # rows read, from one call's outcome per replica (every replica holds the same values)
+    acc, out, path, ew = calls[0](args.seed)
+    torch.cuda.synchronize()
+    par = base["parent"][0].cpu().numpy()
+    acc_np, path_np = acc.cpu().numpy(), path.cpu().numpy()
+    rows = sum(tree_rows_read(par, path_np[b], int(acc_np[b]), w.greedy) for b in range(w.B))
+    read_bytes = rows * row_bytes
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        calls[k % reps](args.seed, pass_events=ev[k])
+    torch.cuda.synchronize()
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    achieved = read_bytes / (kern_ms * 1e-3) / 1e9
+    logits = w.B * (N + 1) * w.V
+    rec = {
+        "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
+        "value": logits / (ms * 1e-3), "unit": "logits/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.tag() + f"_tree{'x'.join(map(str, shape))}", "B": w.B, "N": N,
+                   "V": w.V, "tree_branching": list(shape),
+                   "what": "tree verification (spec_verify_tree); value counts the B*(N+1)*V "
+                           "target logits offered per step",
+                   "temperature": w.temperature if w.temperature is not None
+                   else f"U[{w.t_lo},{w.t_hi}] per sequence",
+                   "mean_accepted_len": float(acc_np.mean()),
+                   "rows_read_per_step": rows, "rows_offered_per_step": w.B * (2 * N + 1),
+                   "replicas_rotated": reps, "parallelism": "single GPU, one workgroup per sequence"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tree_kernel", "kernel_ms": kern_ms,
+                     "algorithmic_bytes_per_launch": read_bytes,
+                     "what": "logit rows the walk must stream (counted from the outcome) / kernel time"},
+    }
+    if not args.no_cpu_baseline:
+        import time as _t
+        nseq = min(w.B, 16)
+        h = {k: v[:nseq] for k, v in base.items()}
+        raw = lambda x: (x.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+                         if x.dtype == torch.bfloat16 else x.contiguous().cpu().numpy())
+        threads = max(1, min(len(os.sched_getaffinity(0)), oracle.max_threads()))
+        calls_n, t0 = 0, _t.perf_counter()
+        while True:
+            oracle.spec_verify_tree(raw(h["target"]), None if w.greedy else raw(h["draft"]),
+                                    h["parent"].cpu().numpy(), h["tokens"].cpu().numpy(), 0,
+                                    h["temperature"].cpu().numpy(), nthreads=threads)
+            calls_n += 1
+            el = _t.perf_counter() - t0
+            if el >= args.cpu_seconds or calls_n >= 1000:
+                break
+        rec["cpu_baseline"] = {"value": calls_n * nseq * (N + 1) * w.V / el, "unit": "logits/s",
+                               "cores": min(threads, nseq), "kind": "oracle",
+                               "sample": f"{nseq} of {w.B} trees of {rec['config']['workload']}, {calls_n} "
+                                         f"calls in {el:.1f} s, OpenMP over sequences, {threads} threads"}
+    return rec
+
+
 BETA_GRID = (1.0, 0.9, 0.75, 0.5, 0.3, 0.2, 0.1, 0.05, 0.0)
 
 
@@ -278,6 +402,9 @@ def main() -> int:
     ap.add_argument("--outcomes", type=int, default=0, metavar="F",
                     help="instead, time the verification-outcome distribution with F ranked "
                          "bonus tokens per position (spec_verify_outcomes)")
+    ap.add_argument("--tree", default="", metavar="K1,K2,...",
+                    help="instead, time tree verification (spec_verify_tree) of trees with this "
+                         "branching per depth, e.g. 4,2,1")
     ap.add_argument("--beta-sweep", action="store_true",
                     help="instead, the exact acceptance / bonus-in-draft-top-4 trade-off over a "
                          "grid of beta (spec_verify_outcomes)")
@@ -312,6 +439,13 @@ def main() -> int:
     sv.load_library()
     w = WORKLOADS[args.workload]
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
+    if args.tree:
+        if args.ragged:
+            print("--tree takes no --ragged", file=sys.stderr)
+            return 2
+        # trees carry no beta re-weighting
+        print(json.dumps(bench_tree(args, sv, w.sized(beta=1.0), dev)), flush=True)
+        return 0
     base = make_inputs(w, seed=args.seed, device=dev)
     if args.beta_sweep:
         if w.greedy or args.ragged:

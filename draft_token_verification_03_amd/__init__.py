@@ -29,10 +29,12 @@ SV_ERR_ROW = 4
 SV_ERR_DRAFT_MASS = 8
 SV_ERR_NO_DRAFT = 16
 SV_ERR_DRAFT_LEN = 32
+SV_ERR_TREE = 64
+MAX_TREE_NODES = 128
 
 EXPORTED = ("spec_verify", "spec_verify_ragged", "spec_verify_workspace_size", "spec_verify_row_stats",
             "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_outcomes",
-            "spec_verify_outcomes_workspace_size", "spec_verify_status_str")
+            "spec_verify_outcomes_workspace_size", "spec_verify_tree", "spec_verify_status_str")
 MAX_OUTCOME_F = 32
 
 
@@ -80,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f32, i32, P, P, P, P, P, P, P,
                                          sz, P, P, P]
     lib.spec_verify_outcomes.restype = i32
+    lib.spec_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P, P, P, P, P]
+    lib.spec_verify_tree.restype = i32
     lib.spec_verify_status_str.argtypes = [i32]
     lib.spec_verify_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -369,3 +373,57 @@ def outcomes(target: torch.Tensor, draft: torch.Tensor | None, temperature, beta
     residual mass on each draft row's top-4 (see Outcomes)."""
     return Outcomes(target, draft, temperature, beta, F, workspace=workspace, stream=stream,
                     draft_top=draft_top)()
+
+
+class TreeVerifier:
+    """Tree (multi-draft) verification (spec_verify_tree) with its buffers
+    bound once.  target [B, N+1, V] (row c: target logits after context c,
+    context 0 the root and context i + 1 node i), draft [B, N, V] (row c: the
+    draft logits the children of context c were drawn from; None if every
+    temperature is 0), parent and tokens [B, N] int32 (parent[i] in
+    [-1, i-1]), temperature a float or [B] float32 tensor.  Each call returns
+    (accepted_len [B], out_tokens [B, N+1], path [B, N], error_word [1]);
+    error_word is cleared before every call."""
+
+    def __init__(self, target: torch.Tensor, draft: torch.Tensor | None, parent: torch.Tensor,
+                 tokens: torch.Tensor, temperature, *, stream=None):
+        if target.dim() != 3 or not target.is_contiguous():
+            raise ValueError("target must be a contiguous [B, N+1, V] tensor")
+        B, N1, V = target.shape
+        N = N1 - 1
+        dev = target.device
+        code = _dtype_code(target)
+        if draft is not None and (draft.shape != (B, N, V) or draft.dtype != target.dtype
+                                  or not draft.is_contiguous()):
+            raise ValueError("draft must be a contiguous [B, N, V] tensor of the target's dtype")
+        for name, x in (("parent", parent), ("tokens", tokens)):
+            if x.shape != (B, N) or x.dtype != torch.int32 or not x.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [B, N] int32 tensor")
+        if not torch.is_tensor(temperature):
+            temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
+        temperature = temperature.contiguous()
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        self.path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.error_word = torch.zeros((1,), dtype=torch.int32, device=dev)
+        self._keep = (target, draft, parent, tokens, temperature)
+        self._head = (_ptr(target), _ptr(draft), _ptr(parent), _ptr(tokens), B, N, V, code)
+        self._tail = (_ptr(temperature), _ptr(self.accepted_len), _ptr(self.out_tokens), _ptr(self.path),
+                      _ptr(self.error_word))
+        self._stream = _stream(stream)
+
+    def __call__(self, seed: int, pass_events=None):
+        self.error_word.zero_()
+        b_ev = e_ev = None
+        if pass_events is not None:
+            b_ev, e_ev = pass_events[0].cuda_event, pass_events[1].cuda_event
+        _check(load_library().spec_verify_tree(*self._head, int(seed) & (2**64 - 1), *self._tail, b_ev,
+                                               e_ev, self._stream))
+        return self.accepted_len, self.out_tokens, self.path, self.error_word
+
+
+def spec_verify_tree(target: torch.Tensor, draft: torch.Tensor | None, parent: torch.Tensor,
+                     tokens: torch.Tensor, seed: int, temperature, *, stream=None):
+    """Verify a token tree per sequence (see TreeVerifier); returns
+    (accepted_len, out_tokens, path, error_word)."""
+    return TreeVerifier(target, draft, parent, tokens, temperature, stream=stream)(seed)

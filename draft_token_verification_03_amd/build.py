@@ -7,8 +7,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("sv_api.hip", "sv_verify.hip", "sv_outcome.hip")]
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("sv_device.h", "sv_internal.h", "sv_accept.h", "sv_tile.h")] + [
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("sv_api.hip", "sv_verify.hip", "sv_outcome.hip", "sv_tree.hip")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("sv_device.h", "sv_internal.h", "sv_accept.h", "sv_tile.h", "sv_stream.h")] + [
     os.path.join(ROOT, "include", "specverify.h")]
 LIB = os.path.join(HERE, "libspecverify.so")
 

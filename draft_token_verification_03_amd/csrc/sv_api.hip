@@ -295,6 +295,43 @@ int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+int32_t spec_verify_tree(const void *target_logits, const void *draft_logits, const int32_t *parent,
+                         const int32_t *tokens, int32_t B, int32_t N, int32_t V, int32_t dtype,
+                         uint64_t seed, const float *temperature, int32_t *accepted_len,
+                         int32_t *out_tokens, int32_t *path, int32_t *error_word, void *pass_begin,
+                         void *pass_end, void *stream)
+{
+    if (B < 0 || N < 0 || N > sv::kMaxK || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return SV_EINVAL;
+    const int64_t elt = dtype == SV_F32 ? 4 : 2;
+    const int64_t nvec = ((int64_t)V * elt + 15) / 16;
+    if (nvec > (int64_t)sv::kMaxTreeSteps * sv::kTreeStepVecs) return SV_EINVAL;
+    if ((int64_t)B * (N + 1) * (int64_t)V > ((int64_t)1 << 40) || B >= (1 << 30)) return SV_EINVAL;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !temperature || !accepted_len || !out_tokens || (N > 0 && (!parent || !tokens || !path)))
+        return SV_EINVAL;
+    if (((uintptr_t)target_logits % elt) || (draft_logits && ((uintptr_t)draft_logits % elt))) return SV_EINVAL;
+    sv::TreeArgs t = {};
+    t.target = static_cast<const char *>(target_logits);
+    t.draft = static_cast<const char *>(draft_logits);
+    t.parent = parent;
+    t.tokens = tokens;
+    t.temperature = temperature;
+    t.N = N;
+    t.V = V;
+    t.nvec = (int32_t)nvec;
+    t.dtype = dtype;
+    t.b0 = 0;
+    t.row_bytes = (int64_t)V * elt;
+    t.seed = seed;
+    t.accepted_len = accepted_len;
+    t.out_tokens = out_tokens;
+    t.path = path;
+    t.error_word = error_word;
+    sv::launch_tree(t, B, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(pass_begin),
+                    static_cast<hipEvent_t>(pass_end));
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 int32_t spec_verify_row_stats(const void *logits, int32_t rows, int32_t V, int32_t dtype,
                               const float *temperature, float *row_max, double *row_logsum,
                               int32_t *row_argmax, void *workspace, size_t workspace_bytes,

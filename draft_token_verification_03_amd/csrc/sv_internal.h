@@ -132,6 +132,28 @@ struct OutArgs {
     float *draft_top_mass;    // [sB][K] r summed over each draft row's top-4, or null
 };
 
+// ---------------------------------------------------------------------------
+// Tree verification: one workgroup walks one sequence's token tree.
+
+constexpr int kMaxTreeSteps = 2048;  // tile steps per row whose masses the bonus search keeps
+constexpr int kTreeStepVecs = 1024;     // 16-byte vectors per tile step of the tree walk
+
+struct TreeArgs {
+    const char *target;        // the sub-batch's first target row: [sB][N+1][V]
+    const char *draft;         // [sB][N][V] or null
+    const int32_t *parent;     // [sB][N]
+    const int32_t *tokens;     // [sB][N]
+    const float *temperature;  // [sB]
+    int32_t N, V, nvec, dtype;
+    int32_t b0;                // index of the sub-batch's first sequence in the call
+    int64_t row_bytes;
+    uint64_t seed;
+    int32_t *accepted_len;     // [sB]
+    int32_t *out_tokens;       // [sB][N+1]
+    int32_t *path;             // [sB][N]
+    int32_t *error_word;
+};
+
 // Launchers of one sub-batch: the verify step (non-null events are recorded
 // around the streaming launch), the streaming pass alone, the outcome
 // distribution (events around the outcome pass), the row-statistics entry
@@ -139,6 +161,7 @@ struct OutArgs {
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 void launch_stats(const Args &a, hipStream_t s);
 void launch_outcomes(const OutArgs &o, hipStream_t s, hipEvent_t begin, hipEvent_t end);
+void launch_tree(const TreeArgs &t, int32_t nb, hipStream_t s, hipEvent_t begin, hipEvent_t end);
 void launch_rowstats(const Args &a, hipStream_t s);
 void launch_uniforms(uint64_t seed, int32_t B, int32_t P, float *out, hipStream_t s);
 void launch_stream_probe(const Args &a, uint32_t *sink, hipStream_t s, hipEvent_t begin, hipEvent_t end);

@@ -34,95 +34,10 @@
 #include <hip/hip_ext.h>
 
 #include "sv_accept.h"
+#include "sv_stream.h"
 #include "sv_tile.h"
 
 namespace sv {
-
-// ---------------------------------------------------------------------------
-// Tiles of the outcome pass: kOutLoads vectors q = qb + u*kBlock + tid of the
-// target row and, for j < K, of the draft row, loaded as the streaming pass
-// loads its tiles (see issue_tile / fix_tile there).
-
-struct PairTile {
-    uint4 t[kOutLoads], d[kOutLoads];
-};
-
-template <int DT, bool ALIGNED, bool PAIR>
-__device__ __forceinline__ void issue_pair(const char *trow, const char *drow, int qb, int q1, int V,
-                                           PairTile &r)
-{
-    constexpr int VEC = Elt<DT>::kVec;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < kOutLoads; ++u) {
-        if (ALIGNED) {
-            const int q = min(qb + u * kBlock + tid, q1 - 1);
-            r.t[u] = load16_stream(trow + (size_t)q * 16);
-            if (PAIR) r.d[u] = load16_stream(drow + (size_t)q * 16);
-        } else {
-            const int q = qb + u * kBlock + tid;
-            if (q < q1) {
-                const int valid = min(VEC, V - q * VEC);
-                const char *pt = trow + (size_t)q * 16;
-                r.t[u] = load16_unaligned(pt, ((uint32_t)((uintptr_t)pt & 15)) +
-                                                  (uint32_t)valid * Elt<DT>::kBytes > 16u);
-                if (PAIR) {
-                    const char *pd = drow + (size_t)q * 16;
-                    r.d[u] = load16_unaligned(pd, ((uint32_t)((uintptr_t)pd & 15)) +
-                                                      (uint32_t)valid * Elt<DT>::kBytes > 16u);
-                }
-            } else {
-                r.t[u] = neg_inf_raw<DT>();
-                if (PAIR) r.d[u] = neg_inf_raw<DT>();
-            }
-        }
-    }
-}
-
-template <int DT, bool PAIR>
-__device__ __forceinline__ void fix_pair(int qb, int q1, int V, PairTile &r)
-{
-    constexpr int VEC = Elt<DT>::kVec;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < kOutLoads; ++u)
-        if (qb + u * kBlock + tid >= q1) {
-            r.t[u] = neg_inf_raw<DT>();
-            if (PAIR) r.d[u] = neg_inf_raw<DT>();
-        }
-    if (V % VEC) {
-        const int last = (V - 1) / VEC;
-#pragma unroll
-        for (int u = 0; u < kOutLoads; ++u)
-            if (qb + u * kBlock + tid == last) {
-                mask_raw<DT>(r.t[u], V - last * VEC);
-                if (PAIR) mask_raw<DT>(r.d[u], V - last * VEC);
-            }
-    }
-}
-
-// Stream [q0, q1) through consume(tile, qb) with two tiles in flight; `ra`
-// holds the already requested tile at q0.
-template <int DT, bool ALIGNED, bool PAIR, class Consume>
-__device__ __forceinline__ void stream_pair(const char *trow, const char *drow, int q0, int q1, int V,
-                                            PairTile &ra, Consume &&consume)
-{
-    constexpr int kStep = kBlock * kOutLoads;
-    PairTile rb;
-    for (int qb = q0;;) {
-        const int qn = qb + kStep;
-        if (qn < q1) issue_pair<DT, ALIGNED, PAIR>(trow, drow, qn, q1, V, rb);
-        if (qn >= q1) fix_pair<DT, PAIR>(qb, q1, V, ra);
-        consume(ra, qb);
-        if (qn >= q1) return;
-        const int qn2 = qn + kStep;
-        if (qn2 < q1) issue_pair<DT, ALIGNED, PAIR>(trow, drow, qn2, q1, V, ra);
-        if (qn2 >= q1) fix_pair<DT, PAIR>(qn, q1, V, rb);
-        consume(rb, qn);
-        if (qn2 >= q1) return;
-        qb = qn2;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // F shared slots of 64-bit keys (top_key order: value, then lower index),

@@ -1,0 +1,477 @@
+// sv_tree.hip -- tree (multi-draft) verification.
+//
+// The pages name tree-based speculative decoding ("Speculative Speculative
+// Decoding", Key claims: SSD composes with Medusa-style trees) without a
+// verify rule; this is the published recursive rejection sampling over a
+// token tree (Miao et al., "SpecInfer", ASPLOS'24), which keeps the output
+// law the target's when the children of every context are drawn i.i.d. from
+// its draft law.  Node i < N has a parent in [-1, i-1] (-1: the root) and a
+// token; context 0 is the root and context i + 1 is node i.  Target row c
+// holds the target logits after context c, draft row c (c < N) the draft
+// logits the children of context c were drawn from.  At a context the law
+// starts as its target law p; its children are tried in node order, child j
+// with token x being accepted iff u(b, j, 0) <= r(x) / q(x), and a rejection
+// replaces r by max(r - q, 0) normalised.  An accepted child becomes the
+// current context; when none is left the bonus is drawn from r by the
+// inverse CDF in token order with u(b, d, 1), d the accepted depth.  Greedy
+// sequences (T = 0) take the first child whose token is the target argmax.
+// A chain (parent[i] = i - 1) is the verify step with K = N.
+//
+// One workgroup walks one sequence and reads only the rows of the contexts
+// it visits: per context one pass over its target and draft rows for their
+// statistics (the running-max sums of the streaming pass), one more pass per
+// rejection for the mass of the next law (kept per tile step for the bonus
+// search), and at the end the one tile step the bonus lies in.  Decisions
+// are taken by thread 0 in fp64 from the two logits gathered at the token.
+#include <hip/hip_ext.h>
+
+#include "sv_accept.h"
+#include "sv_stream.h"
+#include "sv_tile.h"
+
+namespace sv {
+
+// One workgroup streams a sequence's rows on its own: 1024 threads (four
+// waves per SIMD to hide each other's latencies) with two tiles of one
+// vector of each row in flight per thread.  Two vectors a row per tile need
+// more than the 128 registers a thread of a 1024-thread group has, and the
+// spills cost more than the extra loads gain.
+constexpr int kTreeBlock = 1024;
+constexpr int kTreeWaves = kTreeBlock / 64;
+constexpr int kTreeLoads = 1;
+using TreeTile = PairTileU<kTreeLoads>;
+static_assert(kTreeBlock * kTreeLoads == kTreeStepVecs, "tile step of the tree walk");
+
+// How the mass w(v) of a law is formed per element (fp32), the same way in
+// every pass that sums it and in the bonus search that re-reads one step:
+//   kLawTarget  w = exp2(z_t c - o_t)                (p * S_t)
+//   kLawNested  w = r_L(v), r_0 = p, r_{i+1} = max(r_i - q, 0) / Z_i
+//   kLawNext    w = max(r_L(v) - q(v), 0)            (the mass after a rejection)
+constexpr int kLawTarget = 0, kLawNested = 1, kLawNext = 2;
+
+struct Law {
+    ExpScale e;
+    float ot, od;          // row offsets fp32(m c)
+    float inv_st, inv_sd;  // 1 / S_t, 1 / S_d
+    int levels;            // L
+    const float *inv_z;    // [L] in LDS
+};
+
+template <int MODE>
+__device__ __forceinline__ float law_mass(float zt, float zd, const Law &w)
+{
+    const float pt = exp_scaled(zt, w.ot, w.e);
+    if (MODE == kLawTarget) return pt;
+    const float q = exp_scaled(zd, w.od, w.e) * w.inv_sd;
+    float r = pt * w.inv_st;
+    for (int i = 0; i < w.levels; ++i) r = fmaxf(r - q, 0.f) * w.inv_z[i];
+    return MODE == kLawNested ? r : fmaxf(r - q, 0.f);
+}
+
+// Sum of w over the vector pair (fp32, pairwise).
+template <int DT, int MODE>
+__device__ __forceinline__ float law_vec(uint4 rt, uint4 rd, const Law &w, float (&m)[Elt<DT>::kVec])
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    float xt[VEC], xd[VEC];
+    Elt<DT>::unpack(rt, xt);
+    if (MODE != kLawTarget) Elt<DT>::unpack(rd, xd);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) m[k] = law_mass<MODE>(xt[k], MODE != kLawTarget ? xd[k] : 0.f, w);
+    float s[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) s[k] = m[k];
+#pragma unroll
+    for (int h = VEC / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int k = 0; k < h; ++k) s[k] += s[k + h];
+    return s[0];
+}
+
+// A whole-row pass of the workgroup, with the row pair's alignment as a
+// template parameter of the streaming.
+template <int DT, bool PAIR, class Consume>
+__device__ __forceinline__ void row_pass(const char *trow, const char *drow, int nvec, int V, Consume &&consume)
+{
+    const bool aligned = ((uintptr_t)trow & 15) == 0 && (!PAIR || ((uintptr_t)drow & 15) == 0);
+    TreeTile ra;
+    if (aligned) {
+        issue_pair<DT, true, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra);
+        stream_pair<DT, true, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra, consume);
+    } else {
+        issue_pair<DT, false, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra);
+        stream_pair<DT, false, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra, consume);
+    }
+}
+
+// Mass of a law per tile step into ssum[] (fp64 step sums of the threads'
+// fp32 vector sums); returns the total.
+template <int DT, int MODE>
+__device__ __forceinline__ double law_pass(const char *trow, const char *drow, int nvec, int V, const Law &w,
+                                           double *ssum, double *lds_d)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    constexpr int kStep = kTreeBlock * kTreeLoads;
+    double total = 0.0;
+    auto consume = [&](TreeTile &tl, int qb) {
+        double part = 0.0;
+#pragma unroll
+        for (int u = 0; u < kTreeLoads; ++u) {
+            float m[VEC];
+            part += (double)law_vec<DT, MODE>(tl.t[u], tl.d[u], w, m);
+        }
+        const double s = block_sum<kTreeWaves>(part, lds_d);
+        if (threadIdx.x == 0) ssum[qb / kStep] = s;
+        total += s;
+    };
+    if (MODE == kLawTarget) row_pass<DT, false>(trow, nullptr, nvec, V, consume);
+    else row_pass<DT, true>(trow, drow, nvec, V, consume);
+    return total;
+}
+
+// Greedy rows: the lane's (max, lowest index) over a tile of the walk.
+template <int DT>
+__device__ __forceinline__ void tree_argmax_tile(const uint4 (&r)[kTreeLoads], int q0, float &best, int &bi)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+#pragma unroll
+    for (int u = 0; u < kTreeLoads; ++u) {
+        float x[VEC];
+        Elt<DT>::unpack(r[u], x);
+        float mx = x[0];
+#pragma unroll
+        for (int k = 1; k < VEC; ++k) mx = fmaxf(mx, x[k]);
+        if (mx > best) {
+            int kk = VEC - 1;
+#pragma unroll
+            for (int k = VEC - 1; k >= 0; --k)
+                if (x[k] == mx) kk = k;
+            best = mx;
+            bi = (q0 + u * kTreeBlock + (int)threadIdx.x) * VEC + kk;
+        }
+    }
+}
+
+// (max M, fp64 sum of exp2((z - M) c)) of a row from the threads' runs.
+__device__ __forceinline__ void tree_run_finish(const RowRun &run, const ExpScale &e, float *lds_f, double *lds_d,
+                                                float &M, double &S)
+{
+    M = block_max<kTreeWaves>(run.m, lds_f);
+    const double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - (double)row_offset(M, e));
+    S = block_sum<kTreeWaves>(sc, lds_d);
+}
+
+// Vector q (< nvec) of a row, elements at or beyond V as -inf.
+template <int DT>
+__device__ __forceinline__ uint4 tree_load(const char *row, int q, int nvec, int V)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    const char *p = row + (size_t)q * 16;
+    uint4 r;
+    if (((uintptr_t)row & 15) == 0) {
+        r = *reinterpret_cast<const uint4 *>(p);
+    } else {
+        const int valid = min(VEC, V - q * VEC);
+        r = load16_unaligned(p, ((uint32_t)((uintptr_t)p & 15)) + (uint32_t)valid * Elt<DT>::kBytes > 16u);
+    }
+    if ((V % VEC) && q == nvec - 1) mask_raw<DT>(r, V - q * VEC);
+    return r;
+}
+
+// The bonus: smallest v with C(v) >= thr, C the running sum of w in token
+// order, from the step sums of the pass that formed them and one re-read
+// step.  Within a step, token order is vector slot u first, then thread,
+// then element.
+template <int DT, int MODE>
+__device__ __forceinline__ int law_draw(const char *trow, const char *drow, int nvec, int V, const Law &w,
+                                        const double *ssum, double thr, double *lds_d, int *lds_i)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    constexpr int kStep = kTreeBlock * kTreeLoads;
+    const int nsteps = (nvec + kStep - 1) / kStep;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        double c = 0.0, c_last = 0.0;
+        int s = -1, s_last = 0;
+        for (int k = 0; k < nsteps; ++k) {
+            if (ssum[k] > 0.0) {
+                if (c + ssum[k] >= thr) {
+                    s = k;
+                    break;
+                }
+                s_last = k;
+                c_last = c;
+            }
+            c += ssum[k];
+        }
+        if (s < 0) {  // rounding left thr above the total: the last step with mass, at its end
+            s = s_last;
+            c = c_last;
+            thr = c_last + ssum[s_last];
+        }
+        lds_i[0] = s;
+        lds_d[0] = thr - c;  // the threshold within the step
+    }
+    __syncthreads();
+    const int s = lds_i[0];
+    double rem = lds_d[0];
+    __syncthreads();
+    const int qb = s * kStep;
+    int found = INT_MAX;  // lowest token whose running sum reaches rem, per thread
+    int last = -1;        // the step's last token with mass (rounding fallback)
+    for (int u = 0; u < kTreeLoads; ++u) {
+        const int q = qb + u * kTreeBlock + tid;
+        uint4 rt = neg_inf_raw<DT>(), rd = neg_inf_raw<DT>();
+        const bool live = q < nvec;
+        if (live) {
+            rt = tree_load<DT>(trow, q, nvec, V);
+            if (MODE != kLawTarget) rd = tree_load<DT>(drow, q, nvec, V);
+        }
+        float m[VEC];
+        const float vs = law_vec<DT, MODE>(rt, rd, w, m);
+        double tot;
+        const double exc = block_exclusive_scan<kTreeWaves>((double)vs, tot, lds_d);
+        if (rem <= tot) {  // the threshold lies in this slot
+            if (found == INT_MAX && exc < rem && rem <= exc + (double)vs) {
+                double c = exc;
+                for (int k = 0; k < VEC; ++k) {
+                    c += (double)m[k];
+                    if (c >= rem && m[k] > 0.f) {
+                        found = q * VEC + k;
+                        break;
+                    }
+                }
+                if (found == INT_MAX)  // rounding: the vector's last token with mass
+                    for (int k = VEC - 1; k >= 0; --k)
+                        if (m[k] > 0.f) {
+                            found = q * VEC + k;
+                            break;
+                        }
+            }
+            rem = -1.0;  // found (or fall back below)
+        } else {
+            rem -= tot;
+        }
+        for (int k = 0; k < VEC; ++k)
+            if (m[k] > 0.f) last = max(last, q * VEC + k);
+    }
+    const int f = block_min_int<kTreeWaves>(found, lds_i);
+    const int l = block_max_int<kTreeWaves>(last, lds_i);
+    return f != INT_MAX ? f : l;
+}
+
+// Decision data kept in LDS by thread 0 and read by all threads.
+struct TreeShared {
+    int32_t par[kMaxK], tok[kMaxK];
+    int32_t path[kMaxK], out[kMaxK + 1];
+    float inv_z[kMaxK];
+    double z[kMaxK];
+    double ssum[kMaxTreeSteps];
+    int32_t next, err;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
+{
+    __shared__ TreeShared sh;
+    __shared__ float lds_f[4 + kTreeWaves * 4];
+    __shared__ int lds_i[4 + kTreeWaves * 4];
+    __shared__ double lds_d[kTreeWaves];
+    const int b = blockIdx.x, N = t.N, V = t.V, tid = threadIdx.x;
+    const float T = t.temperature[b];
+    const char *tbase = t.target + (int64_t)b * (N + 1) * t.row_bytes;
+    const char *dbase = t.draft ? t.draft + (int64_t)b * N * t.row_bytes : nullptr;
+    if (tid < N) {
+        sh.par[tid] = t.parent[(int64_t)b * N + tid];
+        sh.tok[tid] = t.tokens[(int64_t)b * N + tid];
+    }
+    if (tid == 0) sh.err = 0;
+    __syncthreads();
+    if (tid == 0) {
+        int e = 0;
+        for (int i = 0; i < N; ++i)
+            if (sh.par[i] < -1 || sh.par[i] >= i) e = SV_ERR_TREE;
+        if (!e && !temperature_ok(T)) e = SV_ERR_TEMPERATURE;
+        if (!e && T != 0.f && N > 0 && !dbase) e = SV_ERR_NO_DRAFT;
+        sh.err = e;
+    }
+    __syncthreads();
+    int fail = sh.err;
+    int cur = -1, d = 0, bonus = -1;
+    const bool greedy = T == 0.f;
+    const ExpScale e = make_scale(greedy ? 1.f : T);
+    int tok_err = 0;
+    while (!fail) {
+        const int ctx = cur + 1;
+        const char *trow = tbase + (int64_t)ctx * t.row_bytes;
+        // the context's first child (children are the later nodes with this parent)
+        int first = -1;
+        for (int j = ctx; j < N; ++j)
+            if (sh.par[j] == cur) {
+                first = j;
+                break;
+            }
+        if (greedy) {
+            float best = -INFINITY;
+            int bi = INT_MAX;
+            row_pass<DT, false>(trow, nullptr, t.nvec, V, [&](TreeTile &tl, int qb) {
+                tree_argmax_tile<DT>(tl.t, qb, best, bi);
+            });
+            block_argmax<kTreeWaves>(best, bi, lds_f, lds_i);
+            if (!isfinite(best)) {
+                fail = SV_ERR_ROW;
+                break;
+            }
+            int next = -1;
+            for (int j = ctx; j < N && next < 0; ++j) {
+                if (sh.par[j] != cur) continue;
+                const int x = sh.tok[j];
+                if (x < 0 || x >= V) tok_err = SV_ERR_TOKEN;
+                if (x == bi) next = j;
+            }
+            if (next < 0) {
+                bonus = bi;
+                break;
+            }
+            if (tid == 0) {
+                sh.out[d] = bi;
+                sh.path[d] = next;
+            }
+            ++d;
+            cur = next;
+            continue;
+        }
+        const char *drow = first >= 0 ? dbase + (int64_t)ctx * t.row_bytes : nullptr;
+        // statistics of the context's rows: one pass over both
+        RowRun rt, rd;
+        run_clear(rt);
+        run_clear(rd);
+        if (drow) {
+            row_pass<DT, true>(trow, drow, t.nvec, V, [&](TreeTile &tl, int) {
+                run_sum_tile<DT, kTreeLoads>(tl.t, e, rt);
+                run_sum_tile<DT, kTreeLoads>(tl.d, e, rd);
+            });
+        } else {
+            row_pass<DT, false>(trow, nullptr, t.nvec, V, [&](TreeTile &tl, int) {
+                run_sum_tile<DT, kTreeLoads>(tl.t, e, rt);
+            });
+        }
+        float Mt, Md = 0.f;
+        double St, Sd = 1.0;
+        tree_run_finish(rt, e, lds_f, lds_d, Mt, St);
+        if (drow) tree_run_finish(rd, e, lds_f, lds_d, Md, Sd);
+        if (!isfinite(Mt) || (drow && !isfinite(Md))) {
+            fail = SV_ERR_ROW;
+            break;
+        }
+        Law w;
+        w.e = e;
+        w.ot = row_offset(Mt, e);
+        w.od = drow ? row_offset(Md, e) : 0.f;
+        w.inv_st = (float)(1.0 / St);
+        w.inv_sd = (float)(1.0 / Sd);
+        w.levels = 0;
+        w.inv_z = sh.inv_z;
+        int levels = 0;         // laws after rejections with a positive mass
+        int ssum_mode = -1;     // how ssum[] was last filled (-1: not for this law)
+        double ssum_total = 0.0;
+        int next = -1;
+        for (int j = ctx; j < N && next < 0; ++j) {
+            if (sh.par[j] != cur) continue;
+            if (tid == 0) {
+                const int x = sh.tok[j];
+                double ratio = 0.0;
+                if (x < 0 || x >= V) {
+                    sh.err |= SV_ERR_TOKEN;
+                } else {
+                    const double px = exp_scaled64(Elt<DT>::scalar(trow, x), (double)w.ot, e.c64) / St;
+                    const double lq = Elt<DT>::scalar(drow, x) * e.c64 - (double)w.od;
+                    const double qx = exp2(lq) / Sd;
+                    double r = px;
+                    for (int i = 0; i < levels; ++i) r = fmax(r - qx, 0.0) / sh.z[i];
+                    ratio = lq == -INFINITY ? INFINITY : r / qx;
+                }
+                const float u = philox_uniform(t.seed, (uint32_t)(t.b0 + b), (uint32_t)j, kPurposeAccept);
+                sh.next = (double)u <= ratio ? 1 : 0;
+            }
+            __syncthreads();
+            const bool acc = sh.next != 0;
+            __syncthreads();
+            if (acc) {
+                next = j;
+                break;
+            }
+            // rejected: the mass of the next law, kept per step for the bonus
+            w.levels = levels;
+            const double z = law_pass<DT, kLawNext>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            if (z > 0.0) {
+                if (tid == 0) {
+                    sh.z[levels] = z;
+                    sh.inv_z[levels] = (float)(1.0 / z);
+                }
+                __syncthreads();
+                ssum_mode = kLawNext;
+                ssum_total = z;
+                ++levels;
+            } else {
+                ssum_mode = -1;  // the law stays; its masses are formed again below
+            }
+        }
+        if (next >= 0) {
+            if (tid == 0) {
+                sh.out[d] = sh.tok[next];
+                sh.path[d] = next;
+            }
+            ++d;
+            cur = next;
+            continue;
+        }
+        // no child left: the bonus from the current law
+        const float uB = philox_uniform(t.seed, (uint32_t)(t.b0 + b), (uint32_t)d, kPurposeBonus);
+        if (levels == 0) {
+            w.levels = 0;
+            const double tot = law_pass<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, lds_d);
+            bonus = law_draw<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
+        } else if (ssum_mode == kLawNext) {
+            w.levels = levels - 1;  // the pass that formed ssum[] ran before the last level
+            bonus = law_draw<DT, kLawNext>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * ssum_total, lds_d,
+                                           lds_i);
+        } else {
+            w.levels = levels;
+            const double tot = law_pass<DT, kLawNested>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            bonus = law_draw<DT, kLawNested>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
+        }
+        break;
+    }
+    __syncthreads();
+    const int err = fail | tok_err | sh.err;
+    int32_t *out = t.out_tokens + (int64_t)b * (N + 1);
+    int32_t *path = t.path + (int64_t)b * N;
+    if (fail) {
+        for (int j = tid; j <= N; j += kTreeBlock) out[j] = -1;
+        for (int j = tid; j < N; j += kTreeBlock) path[j] = -1;
+        if (tid == 0) t.accepted_len[b] = 0;
+    } else {
+        for (int j = tid; j <= N; j += kTreeBlock) out[j] = j < d ? sh.out[j] : j == d ? bonus : -1;
+        for (int j = tid; j < N; j += kTreeBlock) path[j] = j < d ? sh.path[j] : -1;
+        if (tid == 0) t.accepted_len[b] = d;
+    }
+    if (err && tid == 0 && t.error_word) atomicOr(t.error_word, err);
+}
+
+void launch_tree(const TreeArgs &t, int32_t nb, hipStream_t s, hipEvent_t begin, hipEvent_t end)
+{
+    if (t.dtype == SV_F32) {
+        if (begin || end)
+            hipExtLaunchKernelGGL(tree_kernel<0>, dim3((unsigned)nb), dim3(kTreeBlock), 0, s, begin, end, 0, t);
+        else
+            tree_kernel<0><<<(unsigned)nb, kTreeBlock, 0, s>>>(t);
+    } else {
+        if (begin || end)
+            hipExtLaunchKernelGGL(tree_kernel<1>, dim3((unsigned)nb), dim3(kTreeBlock), 0, s, begin, end, 0, t);
+        else
+            tree_kernel<1><<<(unsigned)nb, kTreeBlock, 0, s>>>(t);
+    }
+}
+
+}  // namespace sv

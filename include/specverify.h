@@ -82,6 +82,7 @@ extern "C" {
 #define SV_ERR_DRAFT_MASS 8     /* beta == 0 left a draft row with zero mass: outputs -1 */
 #define SV_ERR_NO_DRAFT 16      /* T > 0 but draft_logits is NULL: outputs are -1       */
 #define SV_ERR_DRAFT_LEN 32     /* a ragged draft length outside [0, K]: outputs are -1 */
+#define SV_ERR_TREE 64          /* a tree parent outside [-1, i-1]: outputs are -1      */
 
 /* Optional per-call diagnostics; every field may be NULL. */
 typedef struct sv_aux {
@@ -236,6 +237,48 @@ int32_t spec_verify_outcomes(const void *target_logits, const void *draft_logits
                              float *accept_rate, float *p_len, int32_t *top_tokens, float *top_mass,
                              float *draft_top_mass, int32_t *error_word, void *workspace,
                              size_t workspace_bytes, void *pass_begin, void *pass_end, void *stream);
+
+/*
+ * Tree (multi-draft) verification.  The pages name tree-based speculative
+ * decoding ("Speculative Speculative Decoding", Key claims: SSD composes with
+ * Medusa-style trees) without its verify rule; this is the published
+ * recursive rejection sampling over a token tree (Miao et al., "SpecInfer",
+ * ASPLOS'24), lossless when the children of every context are drawn i.i.d.
+ * from that context's draft law.
+ *   parent        [B, N] int32: parent of node i in [-1, i-1] (-1: the root);
+ *                 otherwise SV_ERR_TREE and the sequence's outputs are -1
+ *   tokens        [B, N] int32: the token of node i
+ *   target_logits [B, N+1, V] dtype: row c = target logits after context c
+ *                 (context 0: the root, context i + 1: node i)
+ *   draft_logits  [B, N, V] dtype: row c = the draft logits the children of
+ *                 context c were drawn from (rows of contexts without
+ *                 children are never read); NULL when every temperature is 0
+ *   temperature   [B] float; 0 = greedy
+ *   accepted_len  [B] int32 out: d, the number of accepted nodes
+ *   out_tokens    [B, N+1] int32 out: the accepted tokens, the bonus, then -1
+ *   path          [B, N] int32 out: the accepted nodes, then -1
+ *   error_word    device int32 or NULL: SV_ERR_* bits OR-ed in (TOKEN, TEMPERATURE,
+ *                 ROW, NO_DRAFT, TREE as for spec_verify)
+ *   pass_begin, pass_end  hipEvent_t or NULL, stamped with the kernel's start and end
+ * At the current context (first the root) the law r starts as its target
+ * law p = softmax(target row / T).  Its children are tried in ascending node
+ * index: child j with token x is accepted iff u(b, j, 0) <= r(x) / q(x),
+ * q = softmax(draft row / T); a rejection replaces r by max(r - q, 0)
+ * normalised (unchanged if that has no mass).  An accepted child becomes the
+ * current context.  When no child is left, the bonus is the smallest v with
+ * C(v) >= u(b, d, 1) C(V-1), C the running sum of r in token order.  Greedy
+ * sequences accept the first child whose token is the target argmax and emit
+ * the final context's argmax.  u as for spec_verify; a chain (parent[i] =
+ * i - 1) gives exactly spec_verify with K = N.  Only the rows of the
+ * contexts the walk visits are read.  N <= 128; V up to 2048 * 1024 16-byte
+ * vectors.  One kernel launch (one workgroup per sequence); no workspace.
+ * Returns SV_OK after enqueuing the work.
+ */
+int32_t spec_verify_tree(const void *target_logits, const void *draft_logits, const int32_t *parent,
+                         const int32_t *tokens, int32_t B, int32_t N, int32_t V, int32_t dtype,
+                         uint64_t seed, const float *temperature, int32_t *accepted_len,
+                         int32_t *out_tokens, int32_t *path, int32_t *error_word, void *pass_begin,
+                         void *pass_end, void *stream);
 
 /* Static description of a status code. */
 const char *spec_verify_status_str(int32_t status);

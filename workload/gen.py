@@ -205,3 +205,54 @@ def to_numpy_inputs(inp: dict, b0: int = 0, b1: int | None = None) -> dict:
         "draft_len": (inp["draft_len"][b0:b1].contiguous().cpu().numpy()
                       if inp.get("draft_len") is not None else None),
     }
+
+
+def tree_parents(shape) -> np.ndarray:
+    """Parents of a token tree given its branching per depth, nodes numbered
+    breadth-first: shape (4, 2, 1) is a root with 4 children, each with 2
+    children, each with 1 child (N = 4 + 8 + 8 = 20)."""
+    parents = []
+    level = [-1]
+    for k in shape:
+        nxt = []
+        for p in level:
+            for _ in range(k):
+                parents.append(p)
+                nxt.append(len(parents) - 1)
+        level = nxt
+    return np.array(parents, dtype=np.int32)
+
+
+@torch.no_grad()
+def make_tree_inputs(w: Workload, shape, seed: int = 0, device: str | torch.device = "cpu",
+                     rows_per_batch: int = 256) -> dict:
+    """One batch of tree-verification inputs: every context c (the root and
+    each node) has base logits with the workload's recipe; target row c =
+    base + sigma_b N(0, 1), draft row c = base (contexts 0..N-1); the children
+    of context c get tokens drawn i.i.d. from its draft law at the sequence
+    temperature (argmax where it is 0).  Returns dict(target [B, N+1, V],
+    draft [B, N, V], parent [B, N], tokens [B, N], temperature [B])."""
+    device = torch.device(device)
+    parent_np = tree_parents(shape)
+    N = parent_np.size
+    chain = w.sized(K=N)
+    inp = make_inputs(chain, seed=seed, device=device, rows_per_batch=rows_per_batch)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 7919 + 3)
+    B, V = w.B, w.V
+    parent = torch.from_numpy(parent_np).to(device).unsqueeze(0).repeat(B, 1).contiguous()
+    # node i's token comes from the draft row of its parent's context
+    ctx = torch.from_numpy(parent_np.astype(np.int64) + 1).to(device)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=device)
+    temp = inp["temperature"].to(torch.float64)
+    for i in range(N):
+        z = inp["draft"][:, int(ctx[i])].to(torch.float64)
+        greedy = temp == 0.0
+        u = torch.rand(z.shape, generator=g, device=device, dtype=torch.float64)
+        gumbel = -torch.log(-torch.log(u.clamp_min(1e-300)))
+        t = torch.where(greedy, torch.ones_like(temp), temp).unsqueeze(1)
+        pick = torch.argmax(z / t + gumbel, dim=1)
+        pick = torch.where(greedy, torch.argmax(z, dim=1), pick)
+        tokens[:, i] = pick.to(torch.int32)
+    return {"target": inp["target"], "draft": inp["draft"], "parent": parent, "tokens": tokens,
+            "temperature": inp["temperature"]}
