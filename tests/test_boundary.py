@@ -138,3 +138,51 @@ def test_binding_fails_loudly_without_library(tmp_path):
             sv.load_library(str(tmp_path / "missing.so"))
     finally:
         sv._lib = saved
+
+
+def test_outcomes_validation(lib):
+    """spec_verify_outcomes and its workspace size reject bad arguments
+    before any launch."""
+    import draft_token_verification_03_amd as sv
+    P = ctypes.c_void_p
+    ws = lib.spec_verify_outcomes_workspace_size
+    assert ws(8, 5, 1000, 1, 8) > 0 and ws(8, 5, 1000, 1, 8) % 256 == 0
+    assert ws(8, 5, 1000, 1, 32) > ws(8, 5, 1000, 1, 0) > 0
+    assert ws(8, 5, 1000, 1, 33) == 0 and ws(8, 5, 1000, 1, -1) == 0 and ws(-1, 5, 1000, 1, 8) == 0
+
+    def call(**kw):
+        a = dict(t=P(A), d=P(A + 0x100000), B=2, K=3, V=1000, dt=1, temp=P(A + 0x200000), beta=1.0, F=4,
+                 ar=P(A + 0x300000), pl=P(A + 0x400000), tt=P(A + 0x500000), tm=P(A + 0x600000), dtm=None,
+                 ew=None, w=P(A + 0x700000), wb=1 << 30)
+        a.update(kw)
+        return lib.spec_verify_outcomes(a["t"], a["d"], a["B"], a["K"], a["V"], a["dt"], a["temp"],
+                                        ctypes.c_float(a["beta"]), a["F"], a["ar"], a["pl"], a["tt"], a["tm"],
+                                        a["dtm"], a["ew"], a["w"], a["wb"], None, None, None)
+    for bad in (dict(F=33), dict(F=-1), dict(beta=float("nan")), dict(beta=2.0), dict(K=129), dict(V=0),
+                dict(dt=3), dict(t=None), dict(temp=None), dict(pl=None), dict(ar=None), dict(tt=None),
+                dict(tm=None), dict(t=P(A + 1))):
+        assert call(**bad) == sv.SV_EINVAL, bad
+    assert call(w=None) == sv.SV_EWORKSPACE
+    assert call(wb=64) == sv.SV_EWORKSPACE
+    assert call(B=0, t=None, temp=None, pl=None, ar=None, tt=None, tm=None, w=None, wb=0) == sv.SV_OK
+    # F == 0 needs no ranked outputs; K == 0 needs no accept rates (stops at the workspace check)
+    assert call(F=0, tt=None, tm=None, w=None) == sv.SV_EWORKSPACE
+    assert call(K=0, ar=None, d=None, w=None) == sv.SV_EWORKSPACE
+
+
+def test_tree_validation(lib):
+    """spec_verify_tree rejects bad arguments before any launch."""
+    import draft_token_verification_03_amd as sv
+    P = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(t=P(A), d=P(A + 0x100000), par=P(A + 0x200000), tok=P(A + 0x300000), B=2, N=5, V=1000, dt=1,
+                 temp=P(A + 0x400000), acc=P(A + 0x500000), out=P(A + 0x600000), path=P(A + 0x700000))
+        a.update(kw)
+        return lib.spec_verify_tree(a["t"], a["d"], a["par"], a["tok"], a["B"], a["N"], a["V"], a["dt"], 0,
+                                    a["temp"], a["acc"], a["out"], a["path"], None, None, None, None)
+    for bad in (dict(B=-1), dict(N=-1), dict(N=129), dict(V=0), dict(dt=2), dict(t=None), dict(temp=None),
+                dict(acc=None), dict(out=None), dict(par=None), dict(tok=None), dict(path=None),
+                dict(t=P(A + 1)), dict(d=P(A + 0x100001)), dict(V=1 << 25)):
+        assert call(**bad) == sv.SV_EINVAL, bad
+    assert call(B=0, t=None, temp=None, acc=None, out=None, par=None, tok=None, path=None) == sv.SV_OK
