@@ -74,9 +74,10 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
 }
 
 // The outcome distribution: the streaming pass's plan, then ~kFillBlocks
-// outcome workgroups (two chunks per position when the positions alone fill
-// the grid and a row pair is long), and the outcome pass's records, sums and
-// keys after the streaming pass's regions.
+// outcome workgroups (one chunk per position once the positions fill the
+// grid: a longer chunk lets its slots' floor rise further before most of its
+// elements arrive, so fewer of them are inserted), and the outcome pass's
+// records, sums and keys after the streaming pass's regions.
 bool make_outcome_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F, OutPlan *op)
 {
     if (F < 0 || F > kMaxOutcomeF) return false;
@@ -86,7 +87,6 @@ bool make_outcome_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F
     op->F = F;
     const int64_t pos = (int64_t)p.sB * (K + 1);
     int64_t nc2 = (kFillBlocks + pos - 1) / pos;
-    if (nc2 == 1 && 2 * p.row_bytes >= kSplitRowBytes) nc2 = 2;
     const int64_t nc_max = std::max<int64_t>(1, p.nvec / (kBlock * kOutLoads));
     nc2 = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(nc2, nc_max), kMaxOutChunks));
     op->cvec2 = (int32_t)((p.nvec + nc2 - 1) / nc2);

@@ -386,20 +386,59 @@ __global__ __launch_bounds__(kBlock) void outcome_kernel(const OutArgs o)
 
 // ---------------------------------------------------------------------------
 // 3. Per sequence: alpha_j = (sum of the chunks' sums) / D, P(n = k), and the
-// best F keys of each position from the chunks' sorted lists (a merge: each
-// lane follows the heads of its chunks' lists, the wave takes the largest
-// head F times).  Keys of one position are distinct (they carry the token).
+// best F keys of each position from the chunks' sorted lists (one list: read
+// as it is; several: a merge in which each lane follows the heads of its
+// chunks' lists and the wave takes the largest head F times).  Keys of one
+// position are distinct (they carry the token).
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)dpp_int<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_int<CTRL>((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int SPAN>
+__device__ __forceinline__ uint64_t swap_max_u64(uint64_t v)
+{
+    const IntPair lo = swap_halves<SPAN>((int)(uint32_t)v);
+    const IntPair hi = swap_halves<SPAN>((int)(uint32_t)(v >> 32));
+    const uint64_t a = ((uint64_t)(uint32_t)hi.a << 32) | (uint32_t)lo.a;
+    const uint64_t b = ((uint64_t)(uint32_t)hi.b << 32) | (uint32_t)lo.b;
+    return a > b ? a : b;
+}
+
+// Wave maximum of 64-bit keys with the DPP and permlane butterflies of the
+// float reductions (every lane gets it).  All 64 lanes must be active.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-        const uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
+    uint64_t w = dpp_u64<kDppQuadXor1>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<kDppQuadXor2>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<kDppRowHalfMirror>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<kDppRowMirror>(v);
+    v = w > v ? w : v;
+    v = swap_max_u64<16>(v);
+    return swap_max_u64<32>(v);
+}
+
+// Ranked slot f of position j from key `best` (0: none): the token and its
+// mass, r D / D for j < K, exp2(z c - o_t) / S_t for j = K.
+__device__ __forceinline__ void write_slot(const OutRow &rr, int j, int K, int f, int F, uint64_t best,
+                                           const ExpScale &e, int32_t *tt, float *tm)
+{
+    int tok = -1;
+    float mass = 0.f;
+    if (best != 0) {
+        tok = key_index(best);
+        const double v = (double)key_value(best);
+        mass = j < K ? (float)(v / rr.norm) : (float)(exp2(v * e.c64 - (double)rr.o) / rr.norm);
     }
-    return v;
+    tt[j * F + f] = tok;
+    tm[j * F + f] = mass;
 }
 
 __global__ __launch_bounds__(kBlock) void outcome_finish_kernel(const OutArgs o)
@@ -458,6 +497,12 @@ __global__ __launch_bounds__(kBlock) void outcome_finish_kernel(const OutArgs o)
                 if (lane == 0) o.draft_top_mass[(int64_t)b * K + j] = (float)(t / rr.norm);
             }
         }
+        if (o.nc2 == 1) {  // one sorted list: lane f holds slot f
+            const uint64_t *k0 = o.keys + base * F;
+            for (int f = lane; f < F; f += 64) write_slot(rr, j, K, f, F, k0[f], e, tt, tm);
+            continue;
+        }
+        // several lists: each lane follows the heads of its chunks' sorted lists
         const bool own0 = lane < o.nc2, own1 = lane + 64 < o.nc2;
         const uint64_t *k0 = o.keys + (base + lane) * F;
         const uint64_t *k1 = o.keys + (base + lane + 64) * F;
@@ -471,18 +516,7 @@ __global__ __launch_bounds__(kBlock) void outcome_finish_kernel(const OutArgs o)
                 if (c0 == best) ++h0;
                 else ++h1;
             }
-            if (lane == 0) {
-                int tok = -1;
-                float mass = 0.f;
-                if (best != 0) {
-                    tok = key_index(best);
-                    const double v = (double)key_value(best);
-                    mass = j < K ? (float)(v / rr.norm)
-                                 : (float)(exp2(v * e.c64 - (double)rr.o) / rr.norm);
-                }
-                tt[j * F + f] = tok;
-                tm[j * F + f] = mass;
-            }
+            if (lane == 0) write_slot(rr, j, K, f, F, best, e, tt, tm);
         }
     }
     __syncthreads();
