@@ -349,3 +349,18 @@ def test_draft_top_mass_error_paths(sv, oracle_mod):
     o = run_oracle(oracle_mod, _host(inp), 3)
     check(g, o, 3)
     assert np.all(np.isnan(g["draft_top_mass"][1:]))
+
+
+def test_outcomes_at_the_largest_sizes(sv, oracle_mod):
+    """K = 128 positions (the maximum) and F = 32 ranked tokens."""
+    rng = np.random.default_rng(3)
+    B, K, V = 3, 128, 301
+    base = rng.normal(size=(B, K + 1, V)).astype(np.float32) * 2
+    tgt = base + 0.3 * rng.normal(size=base.shape).astype(np.float32)
+    drf = np.ascontiguousarray(base[:, :K])
+    for beta in (1.0, 0.5):
+        inp = _inputs(tgt, drf, np.array([1.0, 0.7, 1.3], np.float32), beta, "fp32")
+        g = run_gpu(sv, inp, 32, draft_top=True)
+        o = run_oracle(oracle_mod, _host(inp), 32)
+        check(g, o, 32)
+        assert g["error_word"] == 0

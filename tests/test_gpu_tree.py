@@ -201,3 +201,35 @@ def test_tree_full_size_sampled(sv, oracle_mod):
             prev = node
         assert 0 <= g["out_tokens"][b, d] < w.V and np.all(g["out_tokens"][b, d + 1:] == -1)
     assert g["error_word"] == 0
+
+
+def test_largest_trees_and_mixed_modes(sv, oracle_mod):
+    """N = 128 nodes (the maximum): a random tree (each node's parent drawn
+    from the earlier nodes and the root) and a 128-deep chain, with greedy
+    and sampling sequences in one batch."""
+    rng = np.random.default_rng(77)
+    B, N, V = 12, 128, 257
+    for kind in ("random", "chain"):
+        if kind == "random":
+            par = np.array([[rng.integers(-1, i) for i in range(N)] for _ in range(B)], dtype=np.int32)
+        else:
+            par = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+        base = rng.normal(size=(B, N + 1, V)) * 1.2
+        tgt = (base + 0.3 * rng.normal(size=base.shape)).astype(np.float32)
+        drf = base[:, :N].astype(np.float32)
+        tok = np.empty((B, N), dtype=np.int32)
+        for b in range(B):
+            for i in range(N):
+                q = np.exp(drf[b, par[b, i] + 1] - drf[b, par[b, i] + 1].max())
+                tok[b, i] = rng.choice(V, p=q / q.sum())
+        temps = np.where(np.arange(B) % 3 == 0, 0.0, 0.9).astype(np.float32)
+        inp = {"target": torch.from_numpy(tgt).cuda(), "draft": torch.from_numpy(drf).cuda(),
+               "parent": torch.from_numpy(par).cuda(), "tokens": torch.from_numpy(tok).cuda(),
+               "temperature": torch.from_numpy(temps).cuda()}
+        _say(f"largest trees {kind}")
+        g = run_gpu(sv, inp, seed=5)
+        o = run_oracle(oracle_mod, inp, seed=5)
+        check(g, o, temps, max_flip_frac=0.1)
+        assert g["error_word"] == o["error"]
+        if kind == "chain":
+            assert g["accepted_len"].max() > 8
