@@ -753,11 +753,12 @@ __device__ __forceinline__ float residual_vec(uint4 rt, uint4 rd, int q, const S
 // kSlotVec consecutive vectors (1 KiB of each row) per load.  Item f = t*gs +
 // j of a wave is unit j of its t-th slot, kResLoads items per batch (a second
 // batch in flight measured slower: it costs occupancy).  FAST (aligned rows
-// of whole vectors) loads without any
-// branch (indices clamped into the row; items that are not live add
-// nothing), so that no loaded register passes a branch join, which would
-// make it wait for its load.  Each slot is summed by one wave in a fixed
-// order (fp32 within a vector, fp64 across vectors and lanes).
+// of whole vectors) loads without any branch (indices clamped into the row;
+// items that are not live add nothing and load the batch's first vector
+// again, so they cost no HBM traffic), so that no loaded register passes a
+// branch join, which would make it wait for its load.  Each slot is summed
+// by one wave in a fixed order (fp32 within a vector, fp64 across vectors
+// and lanes).
 template <int DT, int MODE>
 struct ResBatch {
     uint4 rt[kResLoads], rd[kResLoads];
@@ -786,11 +787,12 @@ __device__ __forceinline__ void residual_issue(ResBatch<DT, MODE> &B, const char
     if (FAST) {
         // the re-read streams too: nontemporal loads
 #pragma unroll
-        for (int u = 0; u < kResLoads; ++u) B.rt[u] = load16_stream(trow + (size_t)min(B.q[u], nvec - 1) * 16);
+        for (int u = 0; u < kResLoads; ++u)
+            B.rt[u] = load16_stream(trow + (size_t)min(B.live[u] ? B.q[u] : B.q[0], nvec - 1) * 16);
         if (MODE == 1) {
 #pragma unroll
             for (int u = 0; u < kResLoads; ++u)
-                B.rd[u] = load16_stream(drow + (size_t)min(B.q[u], nvec - 1) * 16);
+                B.rd[u] = load16_stream(drow + (size_t)min(B.live[u] ? B.q[u] : B.q[0], nvec - 1) * 16);
         }
     } else {
         load_units<DT, kResLoads>(trow, ta, B.q, B.live, nvec, V, B.rt);
