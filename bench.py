@@ -564,7 +564,9 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": pass_achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "stats_kernel (streaming pass)", "kernel_ms": pass_ms,
+                     "kernel": ("argmax_kernel (streaming pass, no draft rows)"
+                                if w.greedy and draft_len is None else "stats_kernel (streaming pass)"),
+                     "kernel_ms": pass_ms,
                      "algorithmic_bytes_per_launch": pass_bytes,
                      "read_floor": None if floor_ms is None else {"kernel_ms": floor_ms,
                                     "achieved": pass_bytes / (floor_ms * 1e-3) / 1e9,

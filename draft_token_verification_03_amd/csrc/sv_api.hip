@@ -10,7 +10,7 @@ namespace sv {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
+bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only)
 {
     if (B < 0 || K < 0 || K > kMaxK || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return false;
     *p = Plan{};
@@ -26,10 +26,12 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     p->nvec = (int32_t)(((int64_t)V + p->vec - 1) / p->vec);
 
     // streaming: ~kFillBlocks workgroups per sub-batch (one round of resident
-    // workgroups), >= one vector per thread, and one sequence's partials and
-    // top-4 lists within the accept scan's LDS staging
-    const int64_t rows = (int64_t)p->sB * p->R;
-    int64_t nc = (kFillBlocks + rows - 1) / rows;
+    // workgroups; kArgmaxFill for the lighter greedy-only kernel, which
+    // launches only target rows), >= one vector per thread, and one
+    // sequence's partials and top-4 lists within the accept scan's LDS staging
+    const int64_t rows = (int64_t)p->sB * (greedy_only ? K + 1 : p->R);
+    const int64_t fill = greedy_only ? kArgmaxFill : kFillBlocks;
+    int64_t nc = (fill + rows - 1) / rows;
     // rows enough to cover the chip with a few chunks each: at most as many as
     // the accept scan merges per thread
     if (rows * kThreadMerge >= kCUs) nc = std::min<int64_t>(nc, kThreadMerge);
@@ -56,11 +58,11 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p)
     p->ng = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ng_fill, p->nslot));
     p->spg = (p->nslot + p->ng - 1) / p->ng;
     p->ng = (p->nslot + p->spg - 1) / p->spg;
-    if (rows * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ng >= ((int64_t)1 << 31))
+    if ((int64_t)p->sB * p->R * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ng >= ((int64_t)1 << 31))
         return false;
     size_t off = 0;
     p->off_part = off;
-    off = align256(off + sizeof(RowPart) * (size_t)rows * p->nc);
+    off = align256(off + sizeof(RowPart) * (size_t)p->sB * p->R * p->nc);
     p->off_top = off;
     off = align256(off + sizeof(Top4) * (size_t)p->sB * K * p->nc);
     p->off_tope = off;
@@ -162,7 +164,7 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
                                temperature, beta, accepted_len, out_tokens);
     if (v != SV_OK || B == 0) return v;
     Plan p;
-    if (!make_plan(B, K, V, dtype, &p)) return SV_EINVAL;
+    if (!make_plan(B, K, V, dtype, &p, !draft_logits && K > 0 && !draft_len)) return SV_EINVAL;
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
         return SV_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -204,9 +206,9 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype)
 {
-    sv::Plan p;
-    if (B < 0 || !sv::make_plan(B, K, V, dtype, &p)) return 0;
-    return p.bytes;
+    sv::Plan p, pg;
+    if (B < 0 || !sv::make_plan(B, K, V, dtype, &p) || !sv::make_plan(B, K, V, dtype, &pg, true)) return 0;
+    return std::max(p.bytes, pg.bytes);
 }
 
 int32_t spec_verify(const void *target_logits, const void *draft_logits,
@@ -370,7 +372,7 @@ int32_t spec_verify_stream_probe(const void *target_logits, const void *draft_lo
     if (((uintptr_t)target_logits % elt) || (draft_logits && ((uintptr_t)draft_logits % elt)))
         return SV_EINVAL;
     sv::Plan p;
-    if (!sv::make_plan(B, K, V, dtype, &p)) return SV_EINVAL;
+    if (!sv::make_plan(B, K, V, dtype, &p, !draft_logits && K > 0)) return SV_EINVAL;
     for (int32_t b0 = 0; b0 < B; b0 += p.sB) {
         const int32_t nb = std::min(p.sB, B - b0);
         sv::Args a = {};

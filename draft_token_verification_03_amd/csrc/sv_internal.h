@@ -15,6 +15,7 @@ constexpr int kMaxK = 128;               // drafted positions per sequence
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kMaxChunks = 1024;         // streaming chunks per row
 constexpr int kFillBlocks = 768;         // workgroups the streaming grid aims for (one round)
+constexpr int kArgmaxFill = 1280;        // the same for the greedy-only grid (five per CU)
 constexpr int kCUs = 256;                // compute units of the chip
 constexpr int64_t kSplitRowBytes = 256 * 1024;  // rows this long take at least two chunks
 constexpr int kMaxSeqPerLaunch = 8192;   // sequences per sub-batch of launches
@@ -64,7 +65,9 @@ struct Plan {
     size_t bytes;           // total workspace
 };
 
-bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p);
+// greedy_only: a call without draft rows (and K > 0, no ragged lengths),
+// whose streaming pass launches only target rows 0..K (argmax_kernel)
+bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only = false);
 
 struct Args {
     const char *target;     // the sub-batch's first target row

@@ -281,6 +281,46 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
     else stats_chunk<DT, TOP, false>(a, row, b, i, kb, is_draft, slot_row, chunk, T);
 }
 
+// Calls without draft rows and with K > 0 drafts for every sequence (no
+// ragged lengths): only greedy sequences can verify (a sampling sequence
+// fails without its draft rows), so only the argmax of target rows 0..K is
+// needed.  The kernel holds none of the sampling code's registers.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void argmax_chunk(const Args &a, const char *row, int b, int slot_row, int chunk)
+{
+    __shared__ float lds_f[4 + kWaves * 4];
+    __shared__ int lds_i[4 + kWaves * 4];
+    const int q0 = chunk * a.cvec;
+    const int q1 = min(a.nvec, q0 + a.cvec);
+    uint4 r[kLoads];
+    issue_tile<DT, ALIGNED>(row, q0, q1, a.V, r);
+    if (a.temperature[b] != 0.f) return;  // checked while the first tile is in flight
+    float best = -INFINITY;
+    int bi = INT_MAX;
+    stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
+        run_argmax_tile<DT, kLoads>(t, qb, best, bi);
+    });
+    block_argmax(best, bi, lds_f, lds_i);
+    if (threadIdx.x == 0) {
+        RowPart part;
+        part.m = best;
+        part.idx = bi;
+        part.s = 0.0;
+        a.part[(int64_t)slot_row * a.nc + chunk] = part;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void argmax_kernel(const Args a)
+{
+    const int chunk = blockIdx.x % a.nc;
+    const int b = (blockIdx.x / a.nc) / (a.K + 1);
+    const int j = blockIdx.x / a.nc - b * (a.K + 1);
+    const char *row = target_row(a, b, j);
+    if (((uintptr_t)row & 15) == 0) argmax_chunk<DT, true>(a, row, b, b * a.R + j, chunk);
+    else argmax_chunk<DT, false>(a, row, b, b * a.R + j, chunk);
+}
+
 // ---------------------------------------------------------------------------
 // 2. Accept scan of one sequence ("Kangaroo: Self-Speculative Decoding via
 // Shallow Sub-Networks", "3. Lossless Speculative Verification"; greedy:
@@ -1102,10 +1142,17 @@ template <int DT, bool TOP>
 static void launch_all(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)
 {
     const unsigned grid = (unsigned)((int64_t)a.B * (a.draft ? a.R : a.K + 1) * a.nc);
-    if (begin || end)  // the dispatch itself stamps the kernel's start and end
+    const bool greedy_only = !a.draft && a.K > 0 && !a.draft_len;
+    if (greedy_only) {
+        if (begin || end)  // the dispatch itself stamps the kernel's start and end
+            hipExtLaunchKernelGGL(argmax_kernel<DT>, dim3(grid), dim3(kBlock), 0, s, begin, end, 0, a);
+        else
+            argmax_kernel<DT><<<grid, kBlock, 0, s>>>(a);
+    } else if (begin || end) {
         hipExtLaunchKernelGGL(stats_kernel<DT, TOP>, dim3(grid), dim3(kBlock), 0, s, begin, end, 0, a);
-    else
+    } else {
         stats_kernel<DT, TOP><<<grid, kBlock, 0, s>>>(a);
+    }
     const size_t lds = accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, nullptr, nullptr);
     residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ng), kBlock, lds, s>>>(a);
     // without draft logits (K > 0) every sequence is greedy or fails: no bonus draw
