@@ -342,6 +342,31 @@ def test_ragged_without_draft_logits(sv, oracle_mod):
         assert np.all(g["out_tokens"][5] == -1)
 
 
+@pytest.mark.parametrize("B,K,V", [(1, 3, 32000), (3, 4, 5003), (64, 4, 20011), (200, 2, 4099)])
+def test_greedy_only_calls(sv, oracle_mod, B, K, V):
+    """No draft logits and no ragged lengths: the streaming pass takes only the
+    argmax of target rows, with its own grid and chunking (up to 31 chunks a
+    row here, merged through LDS); greedy sequences match the oracle, and a
+    sampling sequence fails with SV_ERR_NO_DRAFT and emits -1."""
+    rng = np.random.default_rng(B * 7 + K)
+    tgt, drf, tok = _random_case(rng, B, K, V)
+    am = tgt[:, :K].argmax(axis=2)
+    tok = np.where(rng.random((B, K)) < 0.7, am, tok).astype(np.int32)  # deep greedy runs
+    temps = np.where(rng.random(B) < 0.25, 0.9, 0.0).astype(np.float32)
+    temps[0] = 0.0
+    for dtype in ("fp32", "bf16"):
+        _say(f"greedy-only B={B} K={K} V={V} dtype={dtype}")
+        inp = _inputs_from_numpy(tgt, drf, tok, temps, 1.0, dtype)
+        rep = run_both(sv, oracle_mod, inp, seed=1, ptol=_ptol(dtype), draft_none=True)
+        rep.check()
+        g = run_gpu(sv, inp, seed=1, draft_none=True)
+        samp = temps > 0
+        if samp.any():
+            assert g["error_word"] & sv.SV_ERR_NO_DRAFT
+            assert np.all(g["out_tokens"][samp] == -1)
+        assert np.all(g["out_tokens"][~samp][:, 0] >= 0)
+
+
 def test_identical_rows_accept_all_and_masked_vocab(sv, oracle_mod):
     rng = np.random.default_rng(3)
     B, K, V = 16, 5, 50000
