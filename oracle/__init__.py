@@ -76,13 +76,13 @@ def _load():
     lib.oracle_spec_verify.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f64,
                                        P, P, P, P, P, P, P, P, P, i32]
     lib.oracle_spec_verify_ragged.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, f64,
-                                              P, P, P, P, P, P, P, P, P, P, i32]
+                                              P, P, P, P, P, P, P, P, P, P, P, i32]
     lib.oracle_spec_verify_ragged.restype = i32
     lib.oracle_spec_verify_outcomes.argtypes = [P, P, i32, i32, i32, i32, P, f64, i32, P, P, P, P, P,
                                                 P, i32]
     lib.oracle_spec_verify_outcomes.restype = i32
     lib.oracle_spec_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P, P, P, P,
-                                            i32]
+                                            P, P, i32]
     lib.oracle_spec_verify_tree.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
@@ -168,7 +168,8 @@ def max_threads() -> int:
 
 def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray, seed: int,
                 temperature, beta: float = 1.0, nthreads: int = 0,
-                seq_ids: np.ndarray | None = None, draft_len: np.ndarray | None = None) -> dict:
+                seq_ids: np.ndarray | None = None, draft_len: np.ndarray | None = None,
+                force: np.ndarray | None = None) -> dict:
     """Run the oracle on a whole batch.
 
     target: [B, K+1, V] float32 or uint16 (bf16 bits); draft: [B, K, V] same
@@ -180,7 +181,9 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
     by (default 0..B-1), so a sample of a larger batch can be verified alone.
     draft_len [B] (default K for every sequence) gives ragged draft lengths
     K_b <= K; draft_conf [B, K] is the draft confidence max_v p_d (NaN past
-    K_b, for greedy and for failed sequences).
+    K_b, for greedy and for failed sequences).  force [B, K] (bool) reverses
+    the outcome of those accept tests (parity checks replay a near-tie the
+    other implementation decided the other way).
     """
     lib = _load()
     t_raw, dt = _as_raw(target)
@@ -214,12 +217,14 @@ def spec_verify(target: np.ndarray, draft: np.ndarray | None, tokens: np.ndarray
     if draft_len is not None:
         draft_len = np.ascontiguousarray(np.asarray(draft_len, dtype=np.int32))
         assert draft_len.shape == (B,)
+    if force is not None:
+        force = np.ascontiguousarray(np.asarray(force, dtype=bool).reshape(B, K).astype(np.uint8))
     err = lib.oracle_spec_verify_ragged(
         _ptr(t_raw), _ptr(d_raw), _ptr(tok), _ptr(draft_len), B, K, V, dt, int(seed) & (2**64 - 1),
         _ptr(temp), float(beta), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]),
         _ptr(res["p_target"]), _ptr(res["p_draft"]), _ptr(res["residual_mass"]),
         _ptr(res["margin_accept"]), _ptr(res["margin_bonus"]), _ptr(res["seq_error"]),
-        _ptr(res["draft_conf"]), _ptr(seq_ids), int(nthreads))
+        _ptr(res["draft_conf"]), _ptr(seq_ids), _ptr(force), int(nthreads))
     res["error"] = int(err)
     return res
 
@@ -263,11 +268,13 @@ def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: fl
 
 def spec_verify_tree(target: np.ndarray, draft: np.ndarray | None, parent: np.ndarray,
                      tokens: np.ndarray, seed: int, temperature, seq_ids=None,
-                     nthreads: int = 0) -> dict:
+                     nthreads: int = 0, force: np.ndarray | None = None) -> dict:
     """Tree verification of every sequence (see the C source): target
     [B, N+1, V], draft [B, N, V] (row c: the law the children of context c
     were drawn from), parent and tokens [B, N] int32.  Returns accepted_len
-    [B], out_tokens [B, N+1], path [B, N], margin [B], seq_error [B], error."""
+    [B], out_tokens [B, N+1], path [B, N], node_margin [B, N] (|u - ratio| of
+    each node tested, NaN otherwise), bonus_margin [B], seq_error [B], error.
+    force [B, N] (bool) reverses the outcome of those nodes' tests."""
     lib = _load()
     t_raw, dt = _as_raw(target)
     B, N1, V = t_raw.shape
@@ -283,14 +290,18 @@ def spec_verify_tree(target: np.ndarray, draft: np.ndarray | None, parent: np.nd
         temp = np.full(B, temp, dtype=np.float32)
     temp = np.ascontiguousarray(temp)
     ids = None if seq_ids is None else np.ascontiguousarray(seq_ids, dtype=np.int32)
+    if force is not None:
+        force = np.ascontiguousarray(np.asarray(force, dtype=bool).reshape(B, N).astype(np.uint8))
     res = {"accepted_len": np.zeros(B, dtype=np.int32),
            "out_tokens": np.zeros((B, N + 1), dtype=np.int32),
            "path": np.zeros((B, N), dtype=np.int32),
-           "margin": np.zeros(B, dtype=np.float64),
+           "node_margin": np.zeros((B, N), dtype=np.float64),
+           "bonus_margin": np.zeros(B, dtype=np.float64),
            "seq_error": np.zeros(B, dtype=np.int32)}
     err = lib.oracle_spec_verify_tree(
         _ptr(t_raw), _ptr(d_raw), _ptr(parent), _ptr(tokens), B, N, V, dt, int(seed) & (2**64 - 1),
         _ptr(temp), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["path"]),
-        _ptr(res["margin"]), _ptr(res["seq_error"]), _ptr(ids), int(nthreads))
+        _ptr(res["node_margin"]), _ptr(res["bonus_margin"]), _ptr(res["seq_error"]), _ptr(ids),
+        _ptr(force), int(nthreads))
     res["error"] = int(err)
     return res

@@ -295,6 +295,7 @@ typedef struct {
     const int32_t *seq_ids;   /* [B] global sequence index used by the uniforms, or NULL */
     const int32_t *draft_len; /* [B] drafts of each sequence (K_b <= K), or NULL for K */
     double *draft_conf;       /* [B, K]   or NULL */
+    const uint8_t *force;     /* [B, K] nonzero: that accept test takes the other outcome, or NULL */
 } or_call;
 
 static const void *or_row_ptr(const void *base, int dtype, size_t row, int32_t V)
@@ -417,7 +418,12 @@ static int or_verify_sequence(const or_call *c, int32_t b)
         }
         double u = oracle_uniform(c->seed, gb, (uint32_t)i, OR_ACCEPT);
         if (c->margin_accept) c->margin_accept[(size_t)b * Kr + i] = fabs(u - ratio);
-        if (u <= ratio) {
+        int accept = u <= ratio;
+        /* parity checks only: a decision another finite-precision path took
+         * the other way (its margin being within rounding) is replayed so
+         * that the rest of the sequence can still be compared */
+        if (c->force && c->force[(size_t)b * Kr + i]) accept = !accept;
+        if (accept) {
             out[i] = x[i];
             continue;
         }
@@ -490,18 +496,22 @@ static int or_verify_sequence(const or_call *c, int32_t b)
 
 /* Verify every sequence of a batch.  Returns the OR of the error bits.
  * nthreads <= 0 uses the OpenMP default; sequences are independent, so the
- * result does not depend on the thread count.                              */
+ * result does not depend on the thread count.  force [B, K] (or NULL) names
+ * accept tests whose outcome is reversed: a parity check replays a decision
+ * that sat within rounding of its threshold the way the other implementation
+ * took it, and compares the rest of the sequence.                           */
 int32_t oracle_spec_verify_ragged(const void *target, const void *draft, const int32_t *tokens,
                                   const int32_t *draft_len, int32_t B, int32_t K, int32_t V,
                                   int32_t dtype, uint64_t seed, const float *temperature,
                                   double beta, int32_t *accepted_len, int32_t *out_tokens,
                                   double *p_target, double *p_draft, double *residual_mass,
                                   double *margin_accept, double *margin_bonus, int32_t *seq_error,
-                                  double *draft_conf, const int32_t *seq_ids, int32_t nthreads)
+                                  double *draft_conf, const int32_t *seq_ids, const uint8_t *force,
+                                  int32_t nthreads)
 {
     or_call c = {target, draft, tokens, B, K, V, dtype, seed, temperature, beta,
                  accepted_len, out_tokens, p_target, p_draft, residual_mass,
-                 margin_accept, margin_bonus, seq_error, seq_ids, draft_len, draft_conf};
+                 margin_accept, margin_bonus, seq_error, seq_ids, draft_len, draft_conf, force};
     int32_t all_err = 0;
 #ifdef _OPENMP
     if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -668,9 +678,12 @@ int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32
  * A chain (parent[i] = i - 1) is the verify step with K = N, uniforms
  * included.  Outputs: accepted_len[b] = d, out_tokens[b, 0..d-1] the accepted
  * tokens and out_tokens[b, d] the bonus (-1 after), path[b, 0..d-1] the
- * accepted nodes (-1 after), margin[b] the smallest |u - ratio| or |u - C/Z|
- * over the decisions taken (for parity checks).  Only the rows the walk
- * visits are checked for finite maxima.                                      */
+ * accepted nodes (-1 after); for parity checks node_margin[b, j] = |u - ratio|
+ * of node j's accept test (NaN for nodes not tested) and bonus_margin[b] the
+ * distance of u from the ends of the bonus token's CDF interval.  force[b, j]
+ * (or NULL) reverses the outcome of node j's test, so that a near-tie another
+ * implementation decided the other way can be replayed.  Only the rows the
+ * walk visits are checked for finite maxima.                                 */
 static double or_nested(double r, double q, const double *Z, int32_t nZ)
 {
     for (int32_t i = 0; i < nZ; ++i) {
@@ -683,12 +696,13 @@ static double or_nested(double r, double q, const double *Z, int32_t nZ)
 static int or_tree_sequence(const void *target, const void *draft, const int32_t *parent,
                             const int32_t *tokens, int32_t N, int32_t V, int dtype, uint64_t seed,
                             uint32_t gb, double T, int32_t *acc, int32_t *out, int32_t *path,
-                            double *margin)
+                            double *node_margin, double *bonus_margin, const uint8_t *force)
 {
     *acc = 0;
     for (int32_t j = 0; j <= N; ++j) out[j] = -1;
     for (int32_t j = 0; j < N; ++j) path[j] = -1;
-    *margin = NAN;
+    for (int32_t j = 0; j < N; ++j) node_margin[j] = NAN;
+    *bonus_margin = NAN;
     for (int32_t i = 0; i < N; ++i)
         if (parent[i] < -1 || parent[i] >= i) return OR_ERR_TREE;
     if (!(T >= 0.0) || isinf(T)) return OR_ERR_TEMPERATURE;
@@ -723,7 +737,6 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
     }
     if (N > 0 && draft == NULL) return OR_ERR_NO_DRAFT;
     double *Z = (double *)malloc(sizeof(double) * (size_t)(N + 1));
-    double mg = INFINITY;
     or_row rt, rd;
     int32_t nZ = 0;
     for (;;) {
@@ -735,8 +748,8 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
             free(Z);
             for (int32_t j = 0; j <= N; ++j) out[j] = -1;
             for (int32_t j = 0; j < N; ++j) path[j] = -1;
+            for (int32_t j = 0; j < N; ++j) node_margin[j] = NAN;
             *acc = 0;
-            *margin = NAN;
             return err | e;
         }
         nZ = 0;
@@ -756,9 +769,10 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
                 ratio = (lq == -INFINITY) ? INFINITY : rx / qx;
             }
             const double u = oracle_uniform(seed, gb, (uint32_t)j, OR_ACCEPT);
-            const double m = fabs(u - ratio);
-            if (m < mg) mg = m;
-            if (u <= ratio) {
+            node_margin[j] = fabs(u - ratio);
+            int accept = u <= ratio;
+            if (force && force[j]) accept = !accept;
+            if (accept) {
                 next = j;
                 break;
             }
@@ -807,13 +821,11 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
             C = S;
         }
         const double m1 = fabs(uB - Cprev / S), m2 = fabs(uB - C / S);
-        if (m1 < mg) mg = m1;
-        if (m2 < mg) mg = m2;
         free(w);
         free(Z);
         out[d] = bonus;
         *acc = d;
-        *margin = mg;
+        *bonus_margin = m1 < m2 ? m1 : m2;
         return err;
     }
 }
@@ -821,8 +833,9 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
 int32_t oracle_spec_verify_tree(const void *target, const void *draft, const int32_t *parent,
                                 const int32_t *tokens, int32_t B, int32_t N, int32_t V, int32_t dtype,
                                 uint64_t seed, const float *temperature, int32_t *accepted_len,
-                                int32_t *out_tokens, int32_t *path, double *margin, int32_t *seq_error,
-                                const int32_t *seq_ids, int32_t nthreads)
+                                int32_t *out_tokens, int32_t *path, double *node_margin,
+                                double *bonus_margin, int32_t *seq_error, const int32_t *seq_ids,
+                                const uint8_t *force, int32_t nthreads)
 {
     int32_t all_err = 0;
 #ifdef _OPENMP
@@ -836,7 +849,8 @@ int32_t oracle_spec_verify_tree(const void *target, const void *draft, const int
                                  parent + (size_t)b * N, tokens + (size_t)b * N, N, V, dtype, seed,
                                  seq_ids ? (uint32_t)seq_ids[b] : (uint32_t)b,
                                  (double)temperature[b], accepted_len + b, out_tokens + (size_t)b * (N + 1),
-                                 path + (size_t)b * N, margin + b);
+                                 path + (size_t)b * N, node_margin + (size_t)b * N, bonus_margin + b,
+                                 force ? force + (size_t)b * N : NULL);
         if (seq_error) seq_error[b] = e;
         all_err |= e;
     }
@@ -854,7 +868,7 @@ int32_t oracle_spec_verify(const void *target, const void *draft, const int32_t 
     return oracle_spec_verify_ragged(target, draft, tokens, NULL, B, K, V, dtype, seed, temperature,
                                      beta, accepted_len, out_tokens, p_target, p_draft,
                                      residual_mass, margin_accept, margin_bonus, seq_error, NULL,
-                                     seq_ids, nthreads);
+                                     seq_ids, NULL, nthreads);
 }
 
 /* Full draft log-law ln p_d'(v) of one row (for invariant checks). */

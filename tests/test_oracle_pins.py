@@ -512,3 +512,141 @@ def test_draft_confidence_is_the_softmax_maximum(oracle_mod, dtype):
                     continue
                 want = softmax(dz[b, i], float(np.float32(temps[b]))).max()
                 assert abs(conf[b, i] - want) <= 1e-12 * want, (b, i, conf[b, i], want)
+
+
+# --------------------------------------------------------------------------
+# Replayed decisions: the parity rule lets two finite-precision paths differ
+# at a decision within rounding of its threshold, and then compares the rest
+# of the sequence with the oracle replaying that decision the other way.  The
+# replay is pinned against ordinary runs on inputs that force the same
+# outcome through the method itself: an out-of-range draft token is rejected
+# (ratio 0), and a draft token the draft law gives no mass is accepted (ratio
+# +inf).  Neither substitution changes any row, so the rest of the sequence
+# must come out the same.
+
+def _replay_batch(rng, B, K, V, dtype):
+    tgt = (rng.normal(size=(B, K + 1, V)) * 2).astype(np.float32)
+    drf = (tgt[:, :K] + 0.7 * rng.normal(size=(B, K, V))).astype(np.float32)
+    drf[:, :, V - 1] = -np.inf  # token V-1: no draft mass, always accepted when drafted
+    tok = rng.integers(0, V - 1, size=(B, K)).astype(np.int32)
+    am = drf.argmax(axis=2)
+    tok = np.where(rng.random((B, K)) < 0.6, am, tok).astype(np.int32)
+    if dtype == "bf16":
+        return to_bf16_bits(tgt), to_bf16_bits(drf), tok
+    return tgt, drf, tok
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("beta", [1.0, 0.5])
+def test_forced_decisions_equal_token_substitutions(oracle_mod, dtype, beta):
+    """Pin (K, accept rule): replaying an accepted position m as a rejection
+    gives what the oracle gives with x_m out of range; replaying the rejected
+    position n as an acceptance gives what it gives with x_n replaced by a
+    token of zero draft mass (up to that token itself)."""
+    rng = np.random.default_rng(66 if dtype == "fp32" else 67)
+    B, K, V = 160, 4, 61
+    tgt, drf, tok = _replay_batch(rng, B, K, V, dtype)
+    temps = rng.uniform(0.5, 1.5, size=B).astype(np.float32)
+    base = oracle_mod.spec_verify(tgt, drf, tok, 21, temps, beta)
+    assert base["error"] == 0
+    n = base["accepted_len"]
+    assert (n > 0).sum() > 40 and (n < K).sum() > 40
+    checked_rej = checked_acc = 0
+    for b in range(B):
+        ids = np.array([b])
+        sl = slice(b, b + 1)
+        if n[b] > 0:  # replay an accepted position as a rejection
+            m = int(rng.integers(0, n[b]))
+            force = np.zeros((1, K), bool)
+            force[0, m] = True
+            got = oracle_mod.spec_verify(tgt[sl], drf[sl], tok[sl], 21, temps[sl], beta, seq_ids=ids,
+                                         force=force)
+            t2 = tok[sl].copy()
+            t2[0, m] = -1
+            want = oracle_mod.spec_verify(tgt[sl], drf[sl], t2, 21, temps[sl], beta, seq_ids=ids)
+            assert want["seq_error"][0] == oracle_mod.ERR_TOKEN and got["seq_error"][0] == 0
+            assert got["accepted_len"][0] == m == want["accepted_len"][0]
+            assert np.array_equal(got["out_tokens"], want["out_tokens"])
+            for key in ("residual_mass", "margin_bonus"):
+                assert np.array_equal(got[key], want[key]), key
+            assert np.array_equal(got["p_target"][0, :m], want["p_target"][0, :m])
+            checked_rej += 1
+        if n[b] < K:  # replay the rejection at n as an acceptance
+            m = int(n[b])
+            force = np.zeros((1, K), bool)
+            force[0, m] = True
+            got = oracle_mod.spec_verify(tgt[sl], drf[sl], tok[sl], 21, temps[sl], beta, seq_ids=ids,
+                                         force=force)
+            t2 = tok[sl].copy()
+            t2[0, m] = V - 1
+            want = oracle_mod.spec_verify(tgt[sl], drf[sl], t2, 21, temps[sl], beta, seq_ids=ids)
+            assert got["accepted_len"][0] == want["accepted_len"][0] > m
+            g_out, w_out = got["out_tokens"][0].copy(), want["out_tokens"][0].copy()
+            assert g_out[m] == tok[b, m] and w_out[m] == V - 1
+            g_out[m] = w_out[m] = 0
+            assert np.array_equal(g_out, w_out)
+            for key in ("residual_mass", "margin_bonus"):
+                assert np.array_equal(got[key], want[key]), key
+            for key in ("p_target", "p_draft", "margin_accept"):
+                assert np.array_equal(got[key][0, m + 1:], want[key][0, m + 1:], equal_nan=True), key
+            checked_acc += 1
+    assert checked_rej > 40 and checked_acc > 40
+
+
+# --------------------------------------------------------------------------
+# Zero residual mass after a rejection (reading of a case the pages leave
+# open: the residual max(p_t - q', 0) can only vanish through rounding, and
+# the bonus is then drawn from p_t of that position).  Reached on purpose by
+# underflow: every token but one has logit -800 in the target row and -790 in
+# the draft row, so both laws put all their mass (1 in double precision) on
+# the one finite-mass token d, a drafted token x != d has ratio e^-10 (bf16:
+# e^-8) and is rejected for almost every u, and the clamped residual is 0 at
+# every token.  p_t of that position is then the point mass at d: the bonus
+# must be d, and the reported mass C(V-1) of the bonus draw is 1.
+
+def _underflow_case(rng, B, K, V, dtype):
+    tgt = np.full((B, K + 1, V), -800.0, dtype=np.float32)
+    drf = np.full((B, K, V), -790.0, dtype=np.float32)
+    dom = rng.integers(0, V, size=(B, K + 1))
+    tok = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        for i in range(K + 1):
+            tgt[b, i, dom[b, i]] = 0.0
+            if i < K:
+                drf[b, i, dom[b, i]] = 0.0
+                tok[b, i] = (dom[b, i] + 1 + int(rng.integers(0, V - 1))) % V
+    if dtype == "bf16":
+        return to_bf16_bits(tgt), to_bf16_bits(drf), tok, dom
+    return tgt, drf, tok, dom
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("V,K", [(2, 1), (2, 3), (5000, 2)])
+def test_zero_residual_mass_draws_from_target(oracle_mod, dtype, V, K):
+    rng = np.random.default_rng(V + K)
+    B = 48
+    tgt, drf, tok, dom = _underflow_case(rng, B, K, V, dtype)
+    tz, dz = exact_values(tgt), exact_values(drf)
+    u = oracle_mod.uniforms(3, B, K + 1)[:, :, 0]
+    res = oracle_mod.spec_verify(tgt, drf, tok, 3, np.float32(1.0), 1.0)
+    assert res["error"] == 0
+    for b in range(B):
+        # the accept scan by the rule itself: ratio = p_t(x) / q(x) in log form
+        n = K
+        for i in range(K):
+            x = tok[b, i]
+            lt = tz[b, i, x] - scipy.special.logsumexp(tz[b, i])
+            ld = dz[b, i, x] - scipy.special.logsumexp(dz[b, i])
+            if not u[b, i] <= np.exp(lt - ld):
+                n = i
+                break
+        assert res["accepted_len"][b] == n
+        assert n < K  # ratio e^-10 (bf16: e^-8): every sequence rejects here
+        # the case is reached: the clamped residual has no mass in double ...
+        r = np.maximum(softmax(tz[b, n], 1.0) - softmax(dz[b, n], 1.0), 0.0)
+        assert r.sum() == 0.0
+        # ... and p_t of that position is the point mass at the finite token
+        assert softmax(tz[b, n], 1.0)[dom[b, n]] == 1.0
+        assert res["out_tokens"][b, n] == dom[b, n]
+        assert np.all(res["out_tokens"][b, n + 1:] == -1)
+        assert res["residual_mass"][b] == 1.0

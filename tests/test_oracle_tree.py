@@ -180,3 +180,59 @@ def test_tree_error_paths(oracle_mod):
     assert e[4] == oracle_mod.ERR_TEMPERATURE
     r = oracle_mod.spec_verify_tree(tgt, None, parent, tok, 1, np.float32(1.0))
     assert np.all(r["seq_error"][[0, 2, 3]] == oracle_mod.ERR_NO_DRAFT)
+
+
+def test_forced_node_decisions_equal_token_substitutions(oracle_mod):
+    """Pin (replayed near-ties, as for the chain): replaying an accepted node
+    as a rejection gives what the walk gives with that node's token out of
+    range (ratio 0: rejected, and the law still takes its residual); replaying
+    a rejected node as an acceptance gives what it gives with that node's
+    token replaced by one of zero draft mass (ratio +inf), up to that token.
+    Neither substitution changes a row, so the rest of the walk must agree;
+    forcing a chain tree equals forcing the chain verify step."""
+    rng = np.random.default_rng(71)
+    B, V = 120, 41
+    parent = np.array([-1, -1, -1, 0, 0, 1, 3, 3, 5], dtype=np.int32)
+    N = parent.size
+    tgt = (rng.normal(size=(B, N + 1, V)) * 1.5).astype(np.float32)
+    drf = (tgt[:, :N] + 0.8 * rng.normal(size=(B, N, V))).astype(np.float32)
+    drf[:, :, V - 1] = -np.inf  # token V-1 has no draft mass in any context
+    tok = rng.integers(0, V - 1, size=(B, N)).astype(np.int32)
+    temps = rng.uniform(0.6, 1.4, size=B).astype(np.float32)
+    par = np.tile(parent, (B, 1))
+    base = oracle_mod.spec_verify_tree(tgt, drf, par, tok, 5, temps)
+    assert base["error"] == 0
+    n_rej = n_acc = 0
+    for b in range(B):
+        sl, ids = slice(b, b + 1), np.array([b])
+        tested = np.flatnonzero(~np.isnan(base["node_margin"][b]))
+        on_path = set(int(j) for j in base["path"][b] if j >= 0)
+        for j in tested:
+            force = np.zeros((1, N), bool)
+            force[0, j] = True
+            got = oracle_mod.spec_verify_tree(tgt[sl], drf[sl], par[sl], tok[sl], 5, temps[sl],
+                                              seq_ids=ids, force=force)
+            t2 = tok[sl].copy()
+            t2[0, j] = -1 if j in on_path else V - 1
+            want = oracle_mod.spec_verify_tree(tgt[sl], drf[sl], par[sl], t2, 5, temps[sl], seq_ids=ids)
+            assert np.array_equal(got["path"], want["path"])
+            assert got["accepted_len"][0] == want["accepted_len"][0]
+            go, wo = got["out_tokens"][0].copy(), want["out_tokens"][0].copy()
+            if j not in on_path:  # the replayed acceptance emits node j's own token
+                d = list(got["path"][0]).index(j)
+                assert go[d] == tok[b, j] and wo[d] == V - 1
+                go[d] = wo[d] = 0
+                n_acc += 1
+            else:
+                n_rej += 1
+            assert np.array_equal(go, wo)
+            assert np.array_equal(got["bonus_margin"], want["bonus_margin"])
+    assert n_rej > 50 and n_acc > 50
+    # a chain: forcing the tree equals forcing the chain verify step
+    chain = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    force = rng.random((B, N)) < 0.2
+    dch = np.ascontiguousarray(drf[:, :N])
+    a = oracle_mod.spec_verify(tgt, dch, tok, 8, temps, 1.0, force=force)
+    t = oracle_mod.spec_verify_tree(tgt, dch, chain, tok, 8, temps, force=force)
+    assert np.array_equal(a["accepted_len"], t["accepted_len"])
+    assert np.array_equal(a["out_tokens"], t["out_tokens"])
