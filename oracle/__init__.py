@@ -82,7 +82,7 @@ def _load():
                                                 P, i32]
     lib.oracle_spec_verify_outcomes.restype = i32
     lib.oracle_spec_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P, P, P, P,
-                                            P, P, i32]
+                                            P, P, P, P, i32]
     lib.oracle_spec_verify_tree.restype = i32
     lib.oracle_uniforms.argtypes = [u64, i32, i32, P]
     lib.oracle_uniforms.restype = None
@@ -268,13 +268,16 @@ def outcomes(target: np.ndarray, draft: np.ndarray | None, temperature, beta: fl
 
 def spec_verify_tree(target: np.ndarray, draft: np.ndarray | None, parent: np.ndarray,
                      tokens: np.ndarray, seed: int, temperature, seq_ids=None,
-                     nthreads: int = 0, force: np.ndarray | None = None) -> dict:
+                     nthreads: int = 0, force: np.ndarray | None = None,
+                     probe: np.ndarray | None = None) -> dict:
     """Tree verification of every sequence (see the C source): target
     [B, N+1, V], draft [B, N, V] (row c: the law the children of context c
     were drawn from), parent and tokens [B, N] int32.  Returns accepted_len
     [B], out_tokens [B, N+1], path [B, N], node_margin [B, N] (|u - ratio| of
     each node tested, NaN otherwise), bonus_margin [B], seq_error [B], error.
-    force [B, N] (bool) reverses the outcome of those nodes' tests."""
+    force [B, N] (bool) reverses the outcome of those nodes' tests; probe [B]
+    names a token whose CDF interval under the final law is returned as
+    probe_cdf [B, 2]."""
     lib = _load()
     t_raw, dt = _as_raw(target)
     B, N1, V = t_raw.shape
@@ -298,10 +301,13 @@ def spec_verify_tree(target: np.ndarray, draft: np.ndarray | None, parent: np.nd
            "node_margin": np.zeros((B, N), dtype=np.float64),
            "bonus_margin": np.zeros(B, dtype=np.float64),
            "seq_error": np.zeros(B, dtype=np.int32)}
+    if probe is not None:
+        probe = np.ascontiguousarray(np.asarray(probe, dtype=np.int32).reshape(B))
+        res["probe_cdf"] = np.full((B, 2), np.nan)
     err = lib.oracle_spec_verify_tree(
         _ptr(t_raw), _ptr(d_raw), _ptr(parent), _ptr(tokens), B, N, V, dt, int(seed) & (2**64 - 1),
         _ptr(temp), _ptr(res["accepted_len"]), _ptr(res["out_tokens"]), _ptr(res["path"]),
         _ptr(res["node_margin"]), _ptr(res["bonus_margin"]), _ptr(res["seq_error"]), _ptr(ids),
-        _ptr(force), int(nthreads))
+        _ptr(force), _ptr(probe), _ptr(res.get("probe_cdf")), int(nthreads))
     res["error"] = int(err)
     return res

@@ -675,6 +675,17 @@ int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32
  *    number of accepted nodes.
  *  - Greedy (T == 0): the first child whose token is the target argmax is
  *    accepted; the bonus is the final context's argmax.
+ * The law after L rejections that left mass is computed in closed form:
+ * with z_i the mass of the i-th residual, r_{i+1} = max(r_i - q, 0) / z_i
+ * unrolls to r_L = max(p - q A, 0) / P, A = sum_{k<L} prod_{i<k} z_i,
+ * P = prod_{i<L} z_i (A = 0, P = 1 for p itself; once p - q A_i <= 0 at a
+ * token it stays so, as A only grows), and a rejection's residual is
+ * max(p - q (A + P), 0) / P.  Each element is formed as
+ * p(v) max(-expm1(s(v)), 0), s(v) = ln(q(v) A / p(v)) = (z_d(v) - z_t(v)) / T
+ * + ln(S_t / S_d) + ln A with S the rows' sums relative to their maxima, so
+ * that repeated rejections, whose residual masses multiply, keep the law's
+ * shape: the iterated subtraction r - q leaves each element a rounding error
+ * of ~1e-16 of p, which is the whole of r once P falls that low.
  * A chain (parent[i] = i - 1) is the verify step with K = N, uniforms
  * included.  Outputs: accepted_len[b] = d, out_tokens[b, 0..d-1] the accepted
  * tokens and out_tokens[b, d] the bonus (-1 after), path[b, 0..d-1] the
@@ -682,21 +693,42 @@ int32_t oracle_spec_verify_outcomes(const void *target, const void *draft, int32
  * of node j's accept test (NaN for nodes not tested) and bonus_margin[b] the
  * distance of u from the ends of the bonus token's CDF interval.  force[b, j]
  * (or NULL) reverses the outcome of node j's test, so that a near-tie another
- * implementation decided the other way can be replayed.  Only the rows the
- * walk visits are checked for finite maxima.                                 */
-static double or_nested(double r, double q, const double *Z, int32_t nZ)
+ * implementation decided the other way can be replayed.  probe[b] (or NULL):
+ * a token whose CDF interval [C(t-1), C(t)] / C(V-1) under the final law is
+ * written to probe_cdf[b, 0..1] (parity checks of a bonus another
+ * implementation drew).  Only the rows the walk visits are checked for
+ * finite maxima.                                                             */
+/* Max and sum of exp((z - max) / T) of a row. */
+static double or_row_sum(const void *row, int dtype, int32_t V, double T, double *m_out)
 {
-    for (int32_t i = 0; i < nZ; ++i) {
-        double d = r - q;
-        r = (d > 0.0 ? d : 0.0) / Z[i];
+    double m = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+        double a = or_logit(row, dtype, (size_t)v) / T;
+        if (a > m) m = a;
     }
-    return r;
+    double s = 0.0;
+    for (int32_t v = 0; v < V; ++v) s += exp(or_logit(row, dtype, (size_t)v) / T - m);
+    *m_out = m;
+    return s;
+}
+
+/* Element v of max(p - q A, 0) (A > 0) as p(v) max(-expm1(s), 0), with
+ * lnR = ln(S_t / S_d) + ln A. */
+static double or_tree_resid(const or_row *rt, const void *dz, double lnR, int32_t v)
+{
+    const double pv = exp(or_logprob(rt, v));
+    if (pv == 0.0) return 0.0;
+    const double zt = or_logit(rt->z, rt->dtype, (size_t)v), zd = or_logit(dz, rt->dtype, (size_t)v);
+    const double sv = (zd - zt) / rt->T + lnR; /* -inf where the draft gives v no mass */
+    const double f = -expm1(sv);
+    return f > 0.0 ? pv * f : 0.0;
 }
 
 static int or_tree_sequence(const void *target, const void *draft, const int32_t *parent,
                             const int32_t *tokens, int32_t N, int32_t V, int dtype, uint64_t seed,
                             uint32_t gb, double T, int32_t *acc, int32_t *out, int32_t *path,
-                            double *node_margin, double *bonus_margin, const uint8_t *force)
+                            double *node_margin, double *bonus_margin, const uint8_t *force,
+                            int32_t probe, double *probe_cdf)
 {
     *acc = 0;
     for (int32_t j = 0; j <= N; ++j) out[j] = -1;
@@ -736,37 +768,42 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
         }
     }
     if (N > 0 && draft == NULL) return OR_ERR_NO_DRAFT;
-    double *Z = (double *)malloc(sizeof(double) * (size_t)(N + 1));
     or_row rt, rd;
-    int32_t nZ = 0;
     for (;;) {
-        int e = or_prepare(&rt, or_row_ptr(target, dtype, (size_t)(cur + 1), V), dtype, V, T, 0, 1.0);
+        const void *trow = or_row_ptr(target, dtype, (size_t)(cur + 1), V);
+        const void *drow = draft ? or_row_ptr(draft, dtype, (size_t)(cur + 1), V) : NULL;
+        int e = or_prepare(&rt, trow, dtype, V, T, 0, 1.0);
         int have_child = 0;
         for (int32_t j = cur + 1; j < N; ++j) have_child |= parent[j] == cur;
-        if (!e && have_child) e = or_prepare(&rd, or_row_ptr(draft, dtype, (size_t)(cur + 1), V), dtype, V, T, 0, 1.0);
+        if (!e && have_child) e = or_prepare(&rd, drow, dtype, V, T, 0, 1.0);
         if (e) {
-            free(Z);
             for (int32_t j = 0; j <= N; ++j) out[j] = -1;
             for (int32_t j = 0; j < N; ++j) path[j] = -1;
             for (int32_t j = 0; j < N; ++j) node_margin[j] = NAN;
             *acc = 0;
             return err | e;
         }
-        nZ = 0;
+        /* ln(S_t / S_d) from the rows' sums relative to their maxima */
+        double lnST = 0.0;
+        if (have_child) {
+            double mt, md;
+            const double st = or_row_sum(trow, dtype, V, T, &mt), sd = or_row_sum(drow, dtype, V, T, &md);
+            lnST = (mt - md) + log(st / sd);
+        }
+        double A = 0.0, P = 1.0; /* the current law r = max(p - q A, 0) / P */
         int32_t next = -1;
         for (int32_t j = cur + 1; j < N && next < 0; ++j) {
             if (parent[j] != cur) continue;
             const int32_t x = tokens[j];
             double ratio;
-            double qx = 0.0;
             if (x < 0 || x >= V) {
                 err |= OR_ERR_TOKEN;
                 ratio = 0.0;
             } else {
                 const double lq = or_logprob(&rd, x);
-                qx = exp(lq);
-                const double rx = or_nested(exp(or_logprob(&rt, x)), qx, Z, nZ);
-                ratio = (lq == -INFINITY) ? INFINITY : rx / qx;
+                /* r(x) / q(x) = max(p(x) / q(x) - A, 0) / P */
+                const double pq = exp(or_logprob(&rt, x) - lq);
+                ratio = (lq == -INFINITY) ? INFINITY : (A == 0.0 ? pq : fmax(pq - A, 0.0) / P);
             }
             const double u = oracle_uniform(seed, gb, (uint32_t)j, OR_ACCEPT);
             node_margin[j] = fabs(u - ratio);
@@ -776,14 +813,14 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
                 next = j;
                 break;
             }
-            /* the law after this rejection */
-            double z = 0.0;
-            for (int32_t v = 0; v < V; ++v) {
-                const double qv = exp(or_logprob(&rd, v));
-                const double dv = or_nested(exp(or_logprob(&rt, v)), qv, Z, nZ) - qv;
-                z += dv > 0.0 ? dv : 0.0;
+            /* the law after this rejection: max(r - q, 0) = max(p - q (A + P), 0) / P */
+            const double lnR = lnST + log(A + P);
+            double sw = 0.0;
+            for (int32_t v = 0; v < V; ++v) sw += or_tree_resid(&rt, drow, lnR, v);
+            if (sw > 0.0) { /* else the law stays as it is */
+                A = A + P;
+                P = sw;
             }
-            if (z > 0.0) Z[nZ++] = z;
         }
         if (next >= 0) {
             out[d] = tokens[next];
@@ -794,10 +831,10 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
         }
         /* bonus from the current law */
         double *w = (double *)malloc(sizeof(double) * (size_t)V);
+        const double lnR = A > 0.0 ? lnST + log(A) : 0.0;
         double S = 0.0;
         for (int32_t v = 0; v < V; ++v) {
-            const double pv = exp(or_logprob(&rt, v));
-            w[v] = nZ ? or_nested(pv, exp(or_logprob(&rd, v)), Z, nZ) : pv;
+            w[v] = A > 0.0 ? or_tree_resid(&rt, drow, lnR, v) : exp(or_logprob(&rt, v));
             S += w[v];
         }
         const double uB = oracle_uniform(seed, gb, (uint32_t)d, OR_BONUS);
@@ -821,8 +858,16 @@ static int or_tree_sequence(const void *target, const void *draft, const int32_t
             C = S;
         }
         const double m1 = fabs(uB - Cprev / S), m2 = fabs(uB - C / S);
+        if (probe_cdf) {
+            probe_cdf[0] = probe_cdf[1] = NAN;
+            if (probe >= 0 && probe < V) {
+                double cp = 0.0;
+                for (int32_t v = 0; v < probe; ++v) cp += w[v];
+                probe_cdf[0] = cp / S;
+                probe_cdf[1] = (cp + w[probe]) / S;
+            }
+        }
         free(w);
-        free(Z);
         out[d] = bonus;
         *acc = d;
         *bonus_margin = m1 < m2 ? m1 : m2;
@@ -835,7 +880,8 @@ int32_t oracle_spec_verify_tree(const void *target, const void *draft, const int
                                 uint64_t seed, const float *temperature, int32_t *accepted_len,
                                 int32_t *out_tokens, int32_t *path, double *node_margin,
                                 double *bonus_margin, int32_t *seq_error, const int32_t *seq_ids,
-                                const uint8_t *force, int32_t nthreads)
+                                const uint8_t *force, const int32_t *probe, double *probe_cdf,
+                                int32_t nthreads)
 {
     int32_t all_err = 0;
 #ifdef _OPENMP
@@ -850,7 +896,8 @@ int32_t oracle_spec_verify_tree(const void *target, const void *draft, const int
                                  seq_ids ? (uint32_t)seq_ids[b] : (uint32_t)b,
                                  (double)temperature[b], accepted_len + b, out_tokens + (size_t)b * (N + 1),
                                  path + (size_t)b * N, node_margin + (size_t)b * N, bonus_margin + b,
-                                 force ? force + (size_t)b * N : NULL);
+                                 force ? force + (size_t)b * N : NULL, probe ? probe[b] : -1,
+                                 probe_cdf ? probe_cdf + (size_t)b * 2 : NULL);
         if (seq_error) seq_error[b] = e;
         all_err |= e;
     }

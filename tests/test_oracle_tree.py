@@ -236,3 +236,61 @@ def test_forced_node_decisions_equal_token_substitutions(oracle_mod):
     t = oracle_mod.spec_verify_tree(tgt, dch, chain, tok, 8, temps, force=force)
     assert np.array_equal(a["accepted_len"], t["accepted_len"])
     assert np.array_equal(a["out_tokens"], t["out_tokens"])
+
+
+def test_repeated_rejections_match_high_precision(oracle_mod):
+    """Pin (the recursion itself, evaluated exactly): siblings that all carry
+    the token x of a draft law equal to the target law except at x, which the
+    draft favours.  Each rejection of x leaves the residual max(r - q, 0)
+    proportional to p off x, its mass multiplying into a factor ~1e-14 of p
+    after four rejections: a case where subtracting r - q in double leaves
+    nothing but rounding.  The recursion r <- max(r - q, 0) / sum max(r - q, 0)
+    is carried out in 60-digit decimal arithmetic from the same logits, and the
+    oracle's bonus token and its CDF interval must agree with it."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    rng = np.random.default_rng(92)
+    B, V, N = 64, 5003, 4
+    parent = np.tile(np.array([-1] * N, dtype=np.int32), (B, 1))
+    tgt = rng.normal(size=(B, N + 1, V)).astype(np.float32)
+    drf = tgt[:, :N].copy()
+    x = rng.integers(0, V, size=B)
+    drf[np.arange(B), 0, x] += np.float32(np.log1p(2e-3 * V / 1.65))  # ~1e-3 of draft mass moved to x
+    tok = np.repeat(x[:, None], N, axis=1).astype(np.int32)
+    res = oracle_mod.spec_verify_tree(tgt, drf, parent, tok, 11, np.ones(B, np.float32))
+    assert res["error"] == 0
+    checked = 0
+    for b in range(B):
+        if res["accepted_len"][b] != 0:
+            continue  # the first sibling was accepted (ratio ~0.14)
+        zt = [Decimal(float(v)) for v in tgt[b, 0]]
+        zd = [Decimal(float(v)) for v in drf[b, 0]]
+        et = [v.exp() for v in zt]
+        ed = [v.exp() for v in zd]
+        st, sd = sum(et), sum(ed)
+        p = [v / st for v in et]
+        q = [v / sd for v in ed]
+        r = p
+        for j in range(N):  # every sibling carries x: all rejected (ratio 0 after the first)
+            dlt = [max(ri - qi, Decimal(0)) for ri, qi in zip(r, q)]
+            z = sum(dlt)
+            if z > 0:
+                r = [v / z for v in dlt]
+        Z = sum(r)
+        u = Decimal(oracle_mod.uniform(11, b, 0, 1))
+        c = Decimal(0)
+        want = None
+        for v in range(V):
+            lo = c / Z
+            c += r[v]
+            if c >= u * Z:
+                want, want_lo, want_hi = v, lo, c / Z
+                break
+        got = oracle_mod.spec_verify_tree(tgt[b:b + 1], drf[b:b + 1], parent[b:b + 1], tok[b:b + 1], 11,
+                                          np.ones(1, np.float32), seq_ids=np.array([b]),
+                                          probe=np.array([want]))
+        assert res["out_tokens"][b, 0] == want, (b, res["out_tokens"][b, 0], want)
+        assert abs(got["probe_cdf"][0, 0] - float(want_lo)) < 1e-12
+        assert abs(got["probe_cdf"][0, 1] - float(want_hi)) < 1e-12
+        checked += 1
+    assert checked > 40
