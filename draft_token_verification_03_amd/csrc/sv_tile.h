@@ -129,24 +129,24 @@ __device__ __forceinline__ void run_sum_tile(const uint4 (&r)[U], const ExpScale
     }
 }
 
-// Beta-weighted draft row: as run_sum_tile, and the workgroup keeps the
-// chunk's top-4 so far, by (value desc, index asc), in four LDS slots of
-// 64-bit keys that every wave reads and updates.  A key orders like its
-// (value, index) pair, so the slots take new entries with atomic maxima: an
-// insert walks down the slots, and at each one the larger key stays and the
-// smaller moves on, which keeps the slots plus the keys that fall off the end
-// equal to everything inserted, and the slots the four best, under any
-// interleaving of the waves.  The lanes' sums cover every element that
-// never enters the slots or falls out of them.  The 4th slot is a floor no
-// later element reaches in most tiles (one shared list sees four waves'
-// elements, so after t tiles a wave's next tile holds a new entry with
-// probability ~1/t), so most tiles take the plain sum.  A tile with a few
-// candidates has each inserted by its own lane; the first tile, or one with
-// many candidates (rising rows), reduces per-lane lists to the wave's top-4
-// first and inserts those four.
+// Beta-weighted draft row: as run_sum_tile, and each wave keeps the top-4
+// of the elements it has seen, by (value desc, index asc), in a list that
+// every lane holds alike, out of its sums; at the end of the chunk the four
+// waves' lists give the chunk's top-4 and their other entries join the sum
+// (run_finish_top).  The 4th entry is a floor that most later tiles do not
+// reach (after t tiles, a wave's next tile holds a new entry with probability
+// ~4/t), so most tiles take the plain sum.  Elements that beat the floor
+// when their tile arrives are inserted one at a time -- lanes in order, each
+// lane's in token order -- or, when a tile holds many (the first tile,
+// rising rows), through per-lane lists and the wave's top-4 of them.  An
+// entry pushed out of the list, or a candidate that no longer makes it, has
+// its mass added by a lane that the wave's own data fixes.  Every element
+// thus reaches the sum, or the chunk's top-4, along a path and in an order
+// that do not depend on how the waves are timed against each other: a call
+// gives the same bits every time.
 
 // Key of (v, i), i in [0, INT_MAX): larger keys are better entries; -0 counts
-// as +0, as in `better`.  Key 0 is an empty slot.
+// as +0, as in `better`.  Key 0 is an empty slot.  (Used by the outcome pass.)
 __device__ __forceinline__ uint64_t top_key(float v, int i)
 {
     uint32_t b = __float_as_uint(v + 0.0f);
@@ -167,27 +167,6 @@ __device__ __forceinline__ int key_index(uint64_t k)
     return k == 0 ? INT_MAX : 0x7fffffff - (int)(uint32_t)k;
 }
 
-// Insert key k into the slots; returns the key that falls out (k itself if it
-// does not enter, 0 if it took an empty slot).
-__device__ __forceinline__ uint64_t slots_insert(uint64_t *slots, uint64_t k)
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint64_t old = atomicMax((unsigned long long *)&slots[j], (unsigned long long)k);
-        k = old < k ? old : k;
-    }
-    return k;
-}
-
-// The 4th slot as (value, index); a stale read is a lower bound of the
-// current one, as slots only rise.
-__device__ __forceinline__ void slots_floor(const uint64_t *slots, float &fv, int &fi)
-{
-    const uint64_t k = __hip_atomic_load(&slots[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    fv = key_value(k);
-    fi = key_index(k);
-}
-
 __device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &out_v, int &out_i)
 {
     if (!better(v, i, t.v[3], t.i[3])) return false;
@@ -199,21 +178,34 @@ __device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &o
 
 constexpr int kSerialCandidates = 16;
 
+// Element `bit` = u * VEC + k of a tile, u and k known only at run time
+// (selects, no indexed register array).
+template <int DT, int U>
+__device__ __forceinline__ float tile_elt(const uint4 (&r)[U], int bit)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    const int u = bit / VEC;
+    uint4 w = r[0];
+#pragma unroll
+    for (int j = 1; j < U; ++j)
+        if (u == j) w = r[j];
+    return elt_of<DT>(w, bit % VEC);
+}
+
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
-                                                 const ExpScale &e, RowRun &run, uint64_t *slots)
+                                                 const ExpScale &e, RowRun &run, Top4 &wt)
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int lane = threadIdx.x & 63;
-    float fv;
-    int fi;
-    slots_floor(slots, fv, fi);
+    const float fv = wt.v[3];
+    const int fi = wt.i[3];
     const float mx = tile_lane_max<DT, U>(r);
     run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
     // the lane's first token of the tile is its lowest
     const bool maybe = mx > fv || (mx == fv && elem_index(q0, 0, 0, VEC) < fi);
-    if (__ballot(maybe) == 0ull) {  // no element can enter the slots
+    if (__ballot(maybe) == 0ull) {  // no element can enter the list
         if (!have_m) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -250,26 +242,33 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
             for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
         run.s += (double)ev[0];
     }
-    // keys that fall out of the slots, by the lane that inserted them; each
-    // is at most the element inserted, so at most the wave's maximum
-    double lost = 0.0;
+    double lost = 0.0;  // masses leaving the list that this lane adds
     if (wave_sum_int(ncand) <= kSerialCandidates) {
-        if (cmask != 0u) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float x[VEC];
-                Elt<DT>::unpack(r[u], x);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    if (!((cmask >> (u * VEC + k)) & 1u)) continue;
-                    const uint64_t out = slots_insert(slots, top_key(x[k], elem_index(q0, u, k, VEC)));
-                    if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
-                }
+        // one candidate at a time: lanes in order, each lane's in token order
+        uint32_t rem = cmask;
+        double ulost = 0.0;  // alike in every lane; lane 0 adds it
+        for (;;) {
+            const uint64_t lanes = __ballot(rem != 0u);
+            if (lanes == 0ull) break;
+            const int L = __ffsll((unsigned long long)lanes) - 1;
+            const int bit = rem != 0u ? __ffs(rem) - 1 : 0;
+            const float xv = tile_elt<DT, U>(r, bit);
+            const int xi = elem_index(q0, bit / VEC, bit % VEC, VEC);
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), L));
+            const int i = __builtin_amdgcn_readlane(xi, L);
+            if (lane == L) rem &= rem - 1u;
+            float ov;
+            int oi;
+            if (top_insert_out(wt, v, i, ov, oi)) {
+                if (oi != INT_MAX && have_m) ulost += (double)exp_scaled(ov, run.o, e);
+            } else if (have_m) {
+                ulost += (double)exp_scaled(v, run.o, e);
             }
         }
+        if (lane == 0) lost += ulost;
     } else {
-        // per-lane lists of the candidates, the wave's top-4 of them, and
-        // lanes 0..3 insert its entries
+        // many: each lane's candidates into its own list in token order, the
+        // wave's top-4 of those lists merged with the wave list
         Top4 t;
         top_clear(t);
 #pragma unroll
@@ -279,23 +278,28 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 if (!((cmask >> (u * VEC + k)) & 1u)) continue;
-                float ov = x[k];
-                int oi = elem_index(q0, u, k, VEC);
-                top_insert_out(t, x[k], oi, ov, oi);
-                if (oi != INT_MAX && have_m) lost += (double)exp_scaled(ov, run.o, e);
+                float ov;
+                int oi;
+                if (top_insert_out(t, x[k], elem_index(q0, u, k, VEC), ov, oi)) {
+                    if (oi != INT_MAX && have_m) lost += (double)exp_scaled(ov, run.o, e);
+                } else if (have_m) {
+                    lost += (double)exp_scaled(x[k], run.o, e);
+                }
             }
         }
         const Top4 nw = wave_top4(t);
+        Top4 m = wt;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (t.i[k] != INT_MAX && !top_has(nw, t.i[k]) && have_m)
-                lost += (double)exp_scaled(t.v[k], run.o, e);
-        const float v = lane == 0 ? nw.v[0] : lane == 1 ? nw.v[1] : lane == 2 ? nw.v[2] : nw.v[3];
-        const int i = lane == 0 ? nw.i[0] : lane == 1 ? nw.i[1] : lane == 2 ? nw.i[2] : nw.i[3];
-        if (lane < 4 && i != INT_MAX) {
-            const uint64_t out = slots_insert(slots, top_key(v, i));
-            if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
+        for (int k = 0; k < 4; ++k) top_insert(m, nw.v[k], nw.i[k]);
+        if (have_m) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (t.i[k] != INT_MAX && !top_has(m, t.i[k])) lost += (double)exp_scaled(t.v[k], run.o, e);
+                if (lane == 0 && wt.i[k] != INT_MAX && !top_has(m, wt.i[k]))
+                    lost += (double)exp_scaled(wt.v[k], run.o, e);
+            }
         }
+        wt = m;
     }
     run.s += lost;
 }
@@ -336,20 +340,32 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
     S = block_sum(sc, lds_d);
 }
 
-// Weighted draft row chunk: block max M, the chunk's top-4 (the slots, once
-// every wave has finished) and the mass outside it.
-__device__ __forceinline__ void run_finish_top(const RowRun &run, const uint64_t *slots, const ExpScale &e,
-                                               float *lds_f, double *lds_d, float &M, double &S_excl,
-                                               Top4 &ct)
+// Weighted draft row chunk: block max M, the chunk's top-4 from the waves'
+// lists (merged in wave order), and the mass outside it: the lanes' sums and
+// the wave-list entries the chunk's top-4 does not keep.  lds_f / lds_i hold
+// 4 + 4 * kWaves entries.
+__device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &wt, const ExpScale &e,
+                                               float *lds_f, int *lds_i, double *lds_d, float &M,
+                                               double &S_excl, Top4 &ct)
 {
-    M = block_max(run.m, lds_f);  // its barrier also orders every insert before the reads
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint64_t key = slots[k];
-        ct.v[k] = key_value(key);
-        ct.i[k] = key_index(key);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    M = block_max(run.m, lds_f);  // uses entries 0..kWaves-1, ends with a barrier
+    if (lane < 4) {
+        lds_f[4 + wave * 4 + lane] = lane == 0 ? wt.v[0] : lane == 1 ? wt.v[1] : lane == 2 ? wt.v[2] : wt.v[3];
+        lds_i[4 + wave * 4 + lane] = lane == 0 ? wt.i[0] : lane == 1 ? wt.i[1] : lane == 2 ? wt.i[2] : wt.i[3];
     }
-    const double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - (double)row_offset(M, e));
+    __syncthreads();
+    top_clear(ct);
+#pragma unroll
+    for (int j = 0; j < 4 * kWaves; ++j) top_insert(ct, lds_f[4 + j], lds_i[4 + j]);
+    const double oM = (double)row_offset(M, e);
+    double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - oM);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (wt.i[k] != INT_MAX && wt.v[k] != -INFINITY && !top_has(ct, wt.i[k]))
+                sc += exp_scaled64(wt.v[k], oM, e.c64);
+    }
     S_excl = block_sum(sc, lds_d);
 }
 

@@ -42,19 +42,25 @@ constexpr int kTreeLoads = 1;
 using TreeTile = PairTileU<kTreeLoads>;
 static_assert(kTreeBlock * kTreeLoads == kTreeStepVecs, "tile step of the tree walk");
 
-// How the mass w(v) of a law is formed per element (fp32), the same way in
-// every pass that sums it and in the bonus search that re-reads one step:
-//   kLawTarget  w = exp2(z_t c - o_t)                (p * S_t)
-//   kLawNested  w = r_L(v), r_0 = p, r_{i+1} = max(r_i - q, 0) / Z_i
-//   kLawNext    w = max(r_L(v) - q(v), 0)            (the mass after a rejection)
-constexpr int kLawTarget = 0, kLawNested = 1, kLawNext = 2;
+// The law at a context after L rejections that left mass.  With p, q the
+// context's target and draft laws and z_i the mass of the i-th residual,
+// r_{i+1} = max(r_i - q, 0) / z_i unrolls to
+//   r_L = max(p - q A, 0) / P,   A = sum_{k<L} prod_{i<k} z_i,  P = prod_{i<L} z_i
+// (A = 0, P = 1 for the target law itself; once p - q A_i <= 0 at a token it
+// stays so, since A only grows), and a rejection's residual is
+// max(r_L - q, 0) = max(p - q (A + P), 0) / P.  So every law is formed per
+// element as one residual of the target and draft rows, like the verify
+// step's, with relative accuracy where p and q A nearly cancel:
+//   w(v) = exp2(z_t c - o_t) * max(1 - 2^{(z_d - z_t) c + kappa}, 0),
+//   kappa = o_t - o_d + log2(S_t / S_d) + log2(A)     (= S_t P r_L(v)),
+// the fp32 kappa split into hi + lo parts so that one fma rounds it once.
+// A pass of kLawTarget forms w = exp2(z_t c - o_t) = S_t p(v) (A = 0).
+constexpr int kLawTarget = 0, kLawResidual = 1;
 
 struct Law {
     ExpScale e;
-    float ot, od;          // row offsets fp32(m c)
-    float inv_st, inv_sd;  // 1 / S_t, 1 / S_d
-    int levels;            // L
-    const float *inv_z;    // [L] in LDS
+    float ot;              // target row offset fp32(m_t c)
+    float k_hi, k_lo;      // kappa
 };
 
 template <int MODE>
@@ -62,10 +68,14 @@ __device__ __forceinline__ float law_mass(float zt, float zd, const Law &w)
 {
     const float pt = exp_scaled(zt, w.ot, w.e);
     if (MODE == kLawTarget) return pt;
-    const float q = exp_scaled(zd, w.od, w.e) * w.inv_sd;
-    float r = pt * w.inv_st;
-    for (int i = 0; i < w.levels; ++i) r = fmaxf(r - q, 0.f) * w.inv_z[i];
-    return MODE == kLawNested ? r : fmaxf(r - q, 0.f);
+    const float d = __builtin_fmaf(zd - zt, w.e.c, w.k_hi) + w.k_lo;
+    return pt * fmaxf(one_minus_exp2(d), 0.f);  // q A >= p (or a NaN of masked tokens): no mass
+}
+
+__device__ __forceinline__ void law_kappa(Law &w, double kappa)
+{
+    w.k_hi = (float)kappa;
+    w.k_lo = (float)(kappa - (double)w.k_hi);
 }
 
 // Sum of w over the vector pair (fp32, pairwise).
@@ -264,8 +274,6 @@ __device__ __forceinline__ int law_draw(const char *trow, const char *drow, int 
 struct TreeShared {
     int32_t par[kMaxK], tok[kMaxK];
     int32_t path[kMaxK], out[kMaxK + 1];
-    float inv_z[kMaxK];
-    double z[kMaxK];
     double ssum[kMaxTreeSteps];
     int32_t next, err;
 };
@@ -367,29 +375,29 @@ __global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
         Law w;
         w.e = e;
         w.ot = row_offset(Mt, e);
-        w.od = drow ? row_offset(Md, e) : 0.f;
-        w.inv_st = (float)(1.0 / St);
-        w.inv_sd = (float)(1.0 / Sd);
-        w.levels = 0;
-        w.inv_z = sh.inv_z;
-        int levels = 0;         // laws after rejections with a positive mass
-        int ssum_mode = -1;     // how ssum[] was last filled (-1: not for this law)
+        const float od = drow ? row_offset(Md, e) : 0.f;
+        // kappa without its log2(A) term: log2(q(v) / p(v)) = (z_d - z_t) c + k0
+        const double k0 = drow ? ((double)w.ot - (double)od) + log2(St / Sd) : 0.0;
+        double A = 0.0, P = 1.0;  // the current law r = max(p - q A, 0) / P (identical in every thread)
+        bool ssum_ready = false;  // ssum[] holds the current law's step masses (total ssum_total)
         double ssum_total = 0.0;
         int next = -1;
         for (int j = ctx; j < N && next < 0; ++j) {
             if (sh.par[j] != cur) continue;
             if (tid == 0) {
+                // accept iff u <= r(x) / q(x) = max(p(x)/q(x) - A, 0) / P, in fp64 from the logits
                 const int x = sh.tok[j];
                 double ratio = 0.0;
                 if (x < 0 || x >= V) {
                     sh.err |= SV_ERR_TOKEN;
                 } else {
-                    const double px = exp_scaled64(Elt<DT>::scalar(trow, x), (double)w.ot, e.c64) / St;
-                    const double lq = Elt<DT>::scalar(drow, x) * e.c64 - (double)w.od;
-                    const double qx = exp2(lq) / Sd;
-                    double r = px;
-                    for (int i = 0; i < levels; ++i) r = fmax(r - qx, 0.0) / sh.z[i];
-                    ratio = lq == -INFINITY ? INFINITY : r / qx;
+                    const float zt = Elt<DT>::scalar(trow, x), zd = Elt<DT>::scalar(drow, x);
+                    if (zd == -INFINITY) {
+                        ratio = INFINITY;  // no draft mass: cannot be rejected
+                    } else {
+                        const double pq = exp2(((double)zt - (double)zd) * e.c64 - k0);
+                        ratio = A == 0.0 ? pq : fmax(pq - A, 0.0) / P;
+                    }
                 }
                 const float u = philox_uniform(t.seed, (uint32_t)(t.b0 + b), (uint32_t)j, kPurposeAccept);
                 sh.next = (double)u <= ratio ? 1 : 0;
@@ -401,20 +409,18 @@ __global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
                 next = j;
                 break;
             }
-            // rejected: the mass of the next law, kept per step for the bonus
-            w.levels = levels;
-            const double z = law_pass<DT, kLawNext>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
-            if (z > 0.0) {
-                if (tid == 0) {
-                    sh.z[levels] = z;
-                    sh.inv_z[levels] = (float)(1.0 / z);
-                }
-                __syncthreads();
-                ssum_mode = kLawNext;
-                ssum_total = z;
-                ++levels;
+            // rejected: the residual max(r - q, 0) = max(p - q (A + P), 0) / P, kept per
+            // step for the bonus; its pass sums S_t P z, z the residual's mass
+            const double A2 = A + P;
+            law_kappa(w, k0 + log2(A2));
+            const double sw = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            if (sw > 0.0) {
+                A = A2;
+                P = sw / St;  // P z
+                ssum_ready = true;
+                ssum_total = sw;
             } else {
-                ssum_mode = -1;  // the law stays; its masses are formed again below
+                ssum_ready = false;  // no mass: the law stays as it was
             }
         }
         if (next >= 0) {
@@ -428,18 +434,14 @@ __global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
         }
         // no child left: the bonus from the current law
         const float uB = philox_uniform(t.seed, (uint32_t)(t.b0 + b), (uint32_t)d, kPurposeBonus);
-        if (levels == 0) {
-            w.levels = 0;
+        if (A == 0.0) {
             const double tot = law_pass<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, lds_d);
             bonus = law_draw<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
-        } else if (ssum_mode == kLawNext) {
-            w.levels = levels - 1;  // the pass that formed ssum[] ran before the last level
-            bonus = law_draw<DT, kLawNext>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * ssum_total, lds_d,
-                                           lds_i);
         } else {
-            w.levels = levels;
-            const double tot = law_pass<DT, kLawNested>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
-            bonus = law_draw<DT, kLawNested>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
+            law_kappa(w, k0 + log2(A));
+            double tot = ssum_total;
+            if (!ssum_ready) tot = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            bonus = law_draw<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
         }
         break;
     }

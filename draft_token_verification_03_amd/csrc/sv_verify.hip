@@ -219,13 +219,12 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
         RowRun run;
         run_clear(run);
         if (track_top) {
-            __shared__ uint64_t slots[4];  // the chunk's top-4 keys, empty at first
-            if (threadIdx.x < 4) slots[threadIdx.x] = 0;
-            __syncthreads();
+            Top4 wt;  // this wave's top-4 so far
+            top_clear(wt);
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
-                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, slots);
+                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, wt);
             });
-            run_finish_top(run, slots, e, lds_f, lds_d, part.m, part.s, ct);
+            run_finish_top(run, wt, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
             if (threadIdx.x < 4) {
                 // lane k: the mass of entry k, relative to the chunk's offset;
                 // one chunk a row: the row's normaliser D (lane 0 adds the quad)
