@@ -178,28 +178,83 @@ __device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &o
 
 constexpr int kSerialCandidates = 16;
 
-// Element `bit` = u * VEC + k of a tile, u and k known only at run time
-// (selects, no indexed register array).
-template <int DT, int U>
-__device__ __forceinline__ float tile_elt(const uint4 (&r)[U], int bit)
+// A wave's top-4 list, alike in every lane: four keys (top_key order: value,
+// then lower index; 0 = empty, below every element's key), k0 the best, as
+// scalars of one type so that the list stays in registers.
+struct WaveTop {
+    uint64_t k0, k1, k2, k3;
+};
+
+__device__ __forceinline__ void wtop_clear(WaveTop &w) { w.k0 = w.k1 = w.k2 = w.k3 = 0; }
+
+// Insert key k; returns the key that leaves the list (k itself when it does
+// not enter; 0 for an empty slot).  Branch-free: the list is sorted, so
+// beating slot j implies beating every later one, and each slot keeps its
+// key, takes k or takes the key above it.
+__device__ __forceinline__ uint64_t wtop_insert(WaveTop &w, uint64_t k)
 {
-    constexpr int VEC = Elt<DT>::kVec;
-    const int u = bit / VEC;
-    uint4 w = r[0];
-#pragma unroll
-    for (int j = 1; j < U; ++j)
-        if (u == j) w = r[j];
-    return elt_of<DT>(w, bit % VEC);
+    const bool b3 = k > w.k3, b2 = k > w.k2, b1 = k > w.k1, b0 = k > w.k0;
+    const uint64_t out = b3 ? w.k3 : k;
+    const uint64_t n3 = !b3 ? w.k3 : !b2 ? k : w.k2;
+    const uint64_t n2 = !b2 ? w.k2 : !b1 ? k : w.k1;
+    const uint64_t n1 = !b1 ? w.k1 : !b0 ? k : w.k0;
+    const uint64_t n0 = !b0 ? w.k0 : k;
+    w.k0 = n0;
+    w.k1 = n1;
+    w.k2 = n2;
+    w.k3 = n3;
+    return out;
 }
 
+__device__ __forceinline__ bool wtop_has(const WaveTop &w, uint64_t k)
+{
+    return k != 0 && (w.k0 == k || w.k1 == k || w.k2 == k || w.k3 == k);
+}
+
+// One round of the wave merge: the best head of the lanes' lists (every
+// lane gets it), popped from the list that holds it.
+__device__ __forceinline__ uint64_t wtop_pop_best(WaveTop &t)
+{
+    // keys order as (value desc, index asc) pairs do: the wave argmax of the
+    // decoded heads (DPP butterflies) finds the best key
+    float v = key_value(t.k0);
+    int i = key_index(t.k0);
+    wave_argmax(v, i);
+    const uint64_t best = i == INT_MAX ? 0 : top_key(v, i);
+    if (best != 0 && t.k0 == best) {
+        t.k0 = t.k1;
+        t.k1 = t.k2;
+        t.k2 = t.k3;
+        t.k3 = 0;
+    }
+    return best;
+}
+
+// The wave's top-4 of the lanes' lists (every lane gets it).
+__device__ __forceinline__ WaveTop wtop_wave_merge(WaveTop t)
+{
+    WaveTop out;
+    out.k0 = wtop_pop_best(t);
+    out.k1 = wtop_pop_best(t);
+    out.k2 = wtop_pop_best(t);
+    out.k3 = wtop_pop_best(t);
+    return out;
+}
+
+// The floor a tile's elements must beat: the wave's 4th key, or the block's
+// floor from the last exchange of the waves' lists when that is higher (an
+// element below the block's 4th best of what all waves had seen then cannot
+// be in the chunk's top-4).
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
-                                                 const ExpScale &e, RowRun &run, Top4 &wt)
+                                                 const ExpScale &e, RowRun &run, WaveTop &wt,
+                                                 uint64_t block_floor)
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int lane = threadIdx.x & 63;
-    const float fv = wt.v[3];
-    const int fi = wt.i[3];
+    const uint64_t floor_key = wt.k3 > block_floor ? wt.k3 : block_floor;
+    const float fv = key_value(floor_key);
+    const int fi = key_index(floor_key);
     const float mx = tile_lane_max<DT, U>(r);
     run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
@@ -244,33 +299,35 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
     }
     double lost = 0.0;  // masses leaving the list that this lane adds
     if (wave_sum_int(ncand) <= kSerialCandidates) {
-        // one candidate at a time: lanes in order, each lane's in token order
-        uint32_t rem = cmask;
-        double ulost = 0.0;  // alike in every lane; lane 0 adds it
-        for (;;) {
-            const uint64_t lanes = __ballot(rem != 0u);
-            if (lanes == 0ull) break;
-            const int L = __ffsll((unsigned long long)lanes) - 1;
-            const int bit = rem != 0u ? __ffs(rem) - 1 : 0;
-            const float xv = tile_elt<DT, U>(r, bit);
-            const int xi = elem_index(q0, bit / VEC, bit % VEC, VEC);
-            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), L));
-            const int i = __builtin_amdgcn_readlane(xi, L);
-            if (lane == L) rem &= rem - 1u;
-            float ov;
-            int oi;
-            if (top_insert_out(wt, v, i, ov, oi)) {
-                if (oi != INT_MAX && have_m) ulost += (double)exp_scaled(ov, run.o, e);
-            } else if (have_m) {
-                ulost += (double)exp_scaled(v, run.o, e);
+        // one candidate at a time, in a fixed order: element position of the
+        // tile, then lane (the lists and every mass that leaves them are
+        // alike in every lane; lane 0 adds those masses)
+        double ulost = 0.0;
+        const int wbase = (int)threadIdx.x & ~63;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (__ballot((cmask >> (u * VEC)) & ((1u << VEC) - 1u)) == 0ull) continue;
+            float x[VEC];
+            Elt<DT>::unpack(r[u], x);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                uint64_t m = __ballot((cmask >> (u * VEC + k)) & 1u);
+                while (m != 0ull) {
+                    const int L = __ffsll((unsigned long long)m) - 1;
+                    m &= m - 1ull;
+                    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), L));
+                    const int i = (q0 + u * kBlock + wbase + L) * VEC + k;
+                    const uint64_t out = wtop_insert(wt, top_key(v, i));
+                    if (out != 0 && have_m) ulost += (double)exp_scaled(key_value(out), run.o, e);
+                }
             }
         }
         if (lane == 0) lost += ulost;
     } else {
         // many: each lane's candidates into its own list in token order, the
         // wave's top-4 of those lists merged with the wave list
-        Top4 t;
-        top_clear(t);
+        WaveTop t;
+        wtop_clear(t);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float x[VEC];
@@ -278,25 +335,26 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 if (!((cmask >> (u * VEC + k)) & 1u)) continue;
-                float ov;
-                int oi;
-                if (top_insert_out(t, x[k], elem_index(q0, u, k, VEC), ov, oi)) {
-                    if (oi != INT_MAX && have_m) lost += (double)exp_scaled(ov, run.o, e);
-                } else if (have_m) {
-                    lost += (double)exp_scaled(x[k], run.o, e);
-                }
+                const uint64_t out = wtop_insert(t, top_key(x[k], elem_index(q0, u, k, VEC)));
+                if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
             }
         }
-        const Top4 nw = wave_top4(t);
-        Top4 m = wt;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) top_insert(m, nw.v[k], nw.i[k]);
+        const WaveTop nw = wtop_wave_merge(t);
+        WaveTop m = wt;
+        wtop_insert(m, nw.k0);
+        wtop_insert(m, nw.k1);
+        wtop_insert(m, nw.k2);
+        wtop_insert(m, nw.k3);
         if (have_m) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (t.i[k] != INT_MAX && !top_has(m, t.i[k])) lost += (double)exp_scaled(t.v[k], run.o, e);
-                if (lane == 0 && wt.i[k] != INT_MAX && !top_has(m, wt.i[k]))
-                    lost += (double)exp_scaled(wt.v[k], run.o, e);
+            if (t.k0 != 0 && !wtop_has(m, t.k0)) lost += (double)exp_scaled(key_value(t.k0), run.o, e);
+            if (t.k1 != 0 && !wtop_has(m, t.k1)) lost += (double)exp_scaled(key_value(t.k1), run.o, e);
+            if (t.k2 != 0 && !wtop_has(m, t.k2)) lost += (double)exp_scaled(key_value(t.k2), run.o, e);
+            if (t.k3 != 0 && !wtop_has(m, t.k3)) lost += (double)exp_scaled(key_value(t.k3), run.o, e);
+            if (lane == 0) {
+                if (wt.k0 != 0 && !wtop_has(m, wt.k0)) lost += (double)exp_scaled(key_value(wt.k0), run.o, e);
+                if (wt.k1 != 0 && !wtop_has(m, wt.k1)) lost += (double)exp_scaled(key_value(wt.k1), run.o, e);
+                if (wt.k2 != 0 && !wtop_has(m, wt.k2)) lost += (double)exp_scaled(key_value(wt.k2), run.o, e);
+                if (wt.k3 != 0 && !wtop_has(m, wt.k3)) lost += (double)exp_scaled(key_value(wt.k3), run.o, e);
             }
         }
         wt = m;
@@ -340,31 +398,67 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
     S = block_sum(sc, lds_d);
 }
 
+// Exchange of the waves' lists after a fixed number of tiles (the same in
+// every wave, so the result is too): the 4th best of the four lists' keys.
+// lds_keys holds 4 * kWaves 8-byte words.
+__device__ __forceinline__ uint64_t block_floor_of(const WaveTop &wt, double *lds_keys)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t *keys = reinterpret_cast<uint64_t *>(lds_keys) + wave * 4;
+    // a fixed field per lane (a select between fields by lane would become an
+    // indexed access that keeps the list out of registers)
+    if (lane == 0) keys[0] = wt.k0;
+    if (lane == 1) keys[1] = wt.k1;
+    if (lane == 2) keys[2] = wt.k2;
+    if (lane == 3) keys[3] = wt.k3;
+    __syncthreads();
+    WaveTop c;
+    wtop_clear(c);
+    const uint64_t *all = reinterpret_cast<const uint64_t *>(lds_keys);
+#pragma unroll
+    for (int j = 0; j < 4 * kWaves; ++j) wtop_insert(c, all[j]);
+    __syncthreads();  // lds_keys free again
+    return c.k3;
+}
+
 // Weighted draft row chunk: block max M, the chunk's top-4 from the waves'
 // lists (merged in wave order), and the mass outside it: the lanes' sums and
-// the wave-list entries the chunk's top-4 does not keep.  lds_f / lds_i hold
-// 4 + 4 * kWaves entries.
-__device__ __forceinline__ void run_finish_top(const RowRun &run, const Top4 &wt, const ExpScale &e,
-                                               float *lds_f, int *lds_i, double *lds_d, float &M,
+// the wave-list entries the chunk's top-4 does not keep.  lds_f holds kWaves
+// entries, lds_keys 4 * kWaves 8-byte words.
+__device__ __forceinline__ void run_finish_top(const RowRun &run, const WaveTop &wt, const ExpScale &e,
+                                               float *lds_f, double *lds_keys, double *lds_d, float &M,
                                                double &S_excl, Top4 &ct)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     M = block_max(run.m, lds_f);  // uses entries 0..kWaves-1, ends with a barrier
-    if (lane < 4) {
-        lds_f[4 + wave * 4 + lane] = lane == 0 ? wt.v[0] : lane == 1 ? wt.v[1] : lane == 2 ? wt.v[2] : wt.v[3];
-        lds_i[4 + wave * 4 + lane] = lane == 0 ? wt.i[0] : lane == 1 ? wt.i[1] : lane == 2 ? wt.i[2] : wt.i[3];
-    }
+    // each of lanes 0..3 stores one key of its wave's list (a fixed field
+    // per lane: a select between fields by lane would become an indexed
+    // access that keeps the list out of registers)
+    uint64_t *keys = reinterpret_cast<uint64_t *>(lds_keys) + wave * 4;
+    if (lane == 0) keys[0] = wt.k0;
+    if (lane == 1) keys[1] = wt.k1;
+    if (lane == 2) keys[2] = wt.k2;
+    if (lane == 3) keys[3] = wt.k3;
     __syncthreads();
-    top_clear(ct);
+    WaveTop c;
+    wtop_clear(c);
+    const uint64_t *all = reinterpret_cast<const uint64_t *>(lds_keys);
 #pragma unroll
-    for (int j = 0; j < 4 * kWaves; ++j) top_insert(ct, lds_f[4 + j], lds_i[4 + j]);
+    for (int j = 0; j < 4 * kWaves; ++j) wtop_insert(c, all[j]);
+    const uint64_t ck[4] = {c.k0, c.k1, c.k2, c.k3};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ct.v[j] = key_value(ck[j]);
+        ct.i[j] = key_index(ck[j]);
+    }
     const double oM = (double)row_offset(M, e);
     double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - oM);
     if (lane == 0) {
+        const uint64_t wk[4] = {wt.k0, wt.k1, wt.k2, wt.k3};
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (wt.i[k] != INT_MAX && wt.v[k] != -INFINITY && !top_has(ct, wt.i[k]))
-                sc += exp_scaled64(wt.v[k], oM, e.c64);
+        for (int j = 0; j < 4; ++j)
+            if (wk[j] != 0 && key_value(wk[j]) != -INFINITY && !wtop_has(c, wk[j]))
+                sc += exp_scaled64(key_value(wk[j]), oM, e.c64);
     }
     S_excl = block_sum(sc, lds_d);
 }

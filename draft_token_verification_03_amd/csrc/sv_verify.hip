@@ -219,12 +219,19 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
         RowRun run;
         run_clear(run);
         if (track_top) {
-            Top4 wt;  // this wave's top-4 so far
-            top_clear(wt);
+            __shared__ double lds_keys[kWaves * 4];  // the waves' lists, exchanged
+            WaveTop wt;  // this wave's top-4 so far, alike in every lane
+            wtop_clear(wt);
+            uint64_t block_floor = 0;
+            int tiles = 0;
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
-                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, wt);
+                run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, wt, block_floor);
+                ++tiles;
+                // the waves share their lists after 1, 2 and 4 tiles: the block's
+                // floor rises with four waves' data instead of one's
+                if (tiles == 1 || tiles == 2 || tiles == 4) block_floor = block_floor_of(wt, lds_keys);
             });
-            run_finish_top(run, wt, e, lds_f, lds_i, lds_d, part.m, part.s, ct);
+            run_finish_top(run, wt, e, lds_f, lds_keys, lds_d, part.m, part.s, ct);
             if (threadIdx.x < 4) {
                 // lane k: the mass of entry k, relative to the chunk's offset;
                 // one chunk a row: the row's normaliser D (lane 0 adds the quad)
