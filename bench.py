@@ -6,13 +6,19 @@ bonus draw) over one batch of synthetic logits already resident in HBM.  The
 input batch is replicated so that consecutive steps read different copies and
 the working set exceeds the 256 MB Infinity Cache: every step streams from HBM.
 
-Prints one JSON line:
+Prints one JSON line for the headline workload (default C5: B=512, K=5,
+V=128256, fp32, per-sequence T ~ U[0.5, 1.2], beta = 0.5):
   value          verified logits per second, B*(K+1)*V per step / step time
   roofline       the dominant kernel, the streaming pass: the logit bytes it
                  must read / its duration (HIP events recorded around its
                  launch in every timed step), against 8 TB/s
   step_roofline  algorithmic bytes of the whole step / step time
-  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+  step_us        median, p10 and p90 of single-step times (an event pair
+                 around each step of a further timed region)
+  per_config     the same figures for the other workloads of the target
+                 (C2, C3, C4), each timed the same way
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload, on
+                 all host cores and on one
 
 With --outcomes F a step is instead one spec_verify_outcomes call (the
 verification-outcome distribution with F ranked bonus tokens per position);
@@ -37,7 +43,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MALL_BYTES = 256 * 2**20       # Infinity Cache
-DEFAULT_WORKLOAD = "C2"
+DEFAULT_WORKLOAD = "C5"
+PER_CONFIG = ("C2", "C3", "C4")  # the other configurations the 70% target names
 
 
 def kernel_source_hash() -> str:
@@ -67,8 +74,9 @@ def load_traffic(tag: str) -> float | None:
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, w, seconds: float) -> dict:
-    """Time the oracle as it stands on host cores over a bounded sample."""
+def cpu_baseline(inp, w, seconds: float, seconds_one: float) -> dict:
+    """Time the oracle as it stands on host cores over a bounded sample, on
+    all of them and on one."""
     import numpy as np
     import torch
 
@@ -81,22 +89,29 @@ def cpu_baseline(inp, w, seconds: float) -> dict:
     h = to_numpy_inputs(sub)
     if w.greedy:
         h["draft"] = None
+
+    def run(threads: int, budget: float):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.spec_verify(h["target"], h["draft"], h["tokens"], 0, h["temperature"], h["beta"],
+                               nthreads=threads, seq_ids=ids)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget or calls >= 1000:
+                return calls, el
+
     threads = max(1, min(len(os.sched_getaffinity(0)), oracle.max_threads()))
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.spec_verify(h["target"], h["draft"], h["tokens"], 0, h["temperature"], h["beta"],
-                           nthreads=threads, seq_ids=ids)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or calls >= 1000:
-            break
-    logits = calls * nseq * (w.K + 1) * w.V
-    return {"value": logits / el, "unit": "logits/s", "cores": min(threads, nseq),
+    calls, el = run(threads, seconds)
+    calls1, el1 = run(1, seconds_one)
+    per_call = nseq * (w.K + 1) * w.V
+    return {"value": calls * per_call / el, "unit": "logits/s", "cores": min(threads, nseq),
             "kind": "oracle",
             "sample": f"{nseq} of {w.B} sequences of {w.tag()}, {calls} calls in {el:.1f} s, "
                       f"OpenMP over sequences, {threads} threads in the team, "
-                      f"{min(threads, nseq)} busy (one sequence each at a time)"}
+                      f"{min(threads, nseq)} busy (one sequence each at a time)",
+            "one_thread": {"value": calls1 * per_call / el1, "unit": "logits/s", "cores": 1,
+                           "sample": f"the same {nseq} sequences, {calls1} calls in {el1:.1f} s"}}
 
 
 def cpu_baseline_outcomes(inp, w, F: int, seconds: float) -> dict:
@@ -395,7 +410,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget on all host cores")
+    ap.add_argument("--cpu-seconds-one", type=float, default=6.0,
+                    help="oracle time budget on one host core")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time the headline workload only")
+    ap.add_argument("--beta", type=float, default=None,
+                    help="override the workload's beta (e.g. the C4 shape with beta-weighted bf16 rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ragged", action="store_true",
                     help="ragged draft lengths K_b ~ U{0..K} per sequence (spec_verify_ragged)")
@@ -438,6 +460,8 @@ def main() -> int:
 
     sv.load_library()
     w = WORKLOADS[args.workload]
+    if args.beta is not None:
+        w = w.sized(beta=args.beta)
     print(f"# workload {args.workload} {w.tag()}", file=sys.stderr, flush=True)
     if args.tree:
         if args.ragged:
@@ -459,6 +483,39 @@ def main() -> int:
             return 2
         print(json.dumps(bench_outcomes(args, sv, w, base, dev)), flush=True)
         return 0
+    rec = bench_verify(args, sv, w, args.workload, base, dev)
+    if (not args.no_per_config and not args.ragged and args.workload == DEFAULT_WORKLOAD
+            and args.beta is None):
+        # the other workloads the 70% target names, timed the same way
+        per = {}
+        for name in PER_CONFIG:
+            wn = WORKLOADS[name]
+            print(f"# workload {name} {wn.tag()}", file=sys.stderr, flush=True)
+            r = bench_verify(args, sv, wn, name, make_inputs(wn, seed=args.seed, device=dev), dev)
+            per[name] = {"workload": wn.tag(), "value": r["value"], "unit": r["unit"],
+                         "ms_per_step": r["ms_per_step"], "step_us": r["step_us"],
+                         "step_frac": r["step_roofline"]["frac"],
+                         "dominant_kernel": r["roofline"]["kernel"],
+                         "dominant_kernel_ms": r["roofline"]["kernel_ms"],
+                         "dominant_kernel_frac": r["roofline"]["frac"],
+                         "traffic": r["roofline"]["traffic"],
+                         "read_floor_frac": (r["roofline"]["read_floor"] or {}).get("frac"),
+                         "algorithmic_bytes_per_step": r["config"]["algorithmic_bytes_per_step"],
+                         "mean_accepted_len": r["config"]["mean_accepted_len"]}
+        rec["per_config"] = per
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(base, w, args.cpu_seconds, args.cpu_seconds_one)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_verify(args, sv, w, name: str, base: dict, dev) -> dict:
+    """One workload: value (region 1), the streaming pass's roofline (region
+    2), its read floor (region 3) and single-step percentiles (region 4)."""
+    import torch
+
+    from workload import ragged_lengths, ragged_rows
+
     alg_bytes = w.algorithmic_bytes()
     draft_len = None
     logits_per_step = w.B * (w.K + 1) * w.V
@@ -532,10 +589,25 @@ def main() -> int:
     torch.cuda.synchronize()
     floor_ms = None if args.ragged else sum(e0.elapsed_time(e1) for e0, e1 in pass_ev) / args.steps
 
+    # Timed region 4 (percentiles): the steps again, each between its own pair
+    # of events.
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    step_ev[0].record(stream)
+    for k in range(args.steps):
+        j = args.warmup + 2 * args.steps + k
+        calls[j % reps](args.seed + j)
+        step_ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    import numpy as np
+    per_step = np.array([step_ev[k].elapsed_time(step_ev[k + 1]) * 1e3 for k in range(args.steps)])
+    step_us = {"median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+               "p90": float(np.percentile(per_step, 90)), "steps": int(args.steps)}
+
     value = logits_per_step / (ms * 1e-3)
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     pass_achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
-    traffic = None if args.ragged else load_traffic(args.workload)
+    traffic = None if args.ragged else load_traffic(name)
     rec = {
         "metric": "verified logits/sec and achieved HBM GB/s (% of MI355X peak), B*(K+1)*V",
         "value": value,
@@ -577,11 +649,11 @@ def main() -> int:
         "step_roofline": {"achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
                           "scope": "algorithmic bytes of the whole step / step time",
                           "ms_per_step_with_pass_events": ms_with_events},
+        "step_us": step_us,
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(base, w, args.cpu_seconds)
-    print(json.dumps(rec), flush=True)
-    return 0
+    return rec
+
+
 
 
 if __name__ == "__main__":
