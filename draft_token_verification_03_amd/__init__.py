@@ -22,6 +22,7 @@ SV_OK = 0
 SV_EINVAL = -1
 SV_EWORKSPACE = -2
 SV_EHIP = -3
+SV_ESCRATCH = -4
 
 SV_ERR_TOKEN = 1
 SV_ERR_TEMPERATURE = 2
@@ -34,7 +35,8 @@ MAX_TREE_NODES = 128
 
 EXPORTED = ("spec_verify", "spec_verify_ragged", "spec_verify_workspace_size", "spec_verify_row_stats",
             "spec_verify_uniforms", "spec_verify_stream_probe", "spec_verify_outcomes",
-            "spec_verify_outcomes_workspace_size", "spec_verify_tree", "spec_verify_status_str")
+            "spec_verify_outcomes_workspace_size", "spec_verify_tree", "spec_verify_status_str",
+            "spec_verify_noalloc", "spec_verify_noalloc_max_scratch")
 MAX_OUTCOME_F = 32
 
 
@@ -84,6 +86,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_outcomes.restype = i32
     lib.spec_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, u64, P, P, P, P, P, P, P, P]
     lib.spec_verify_tree.restype = i32
+    lib.spec_verify_noalloc.argtypes = [P, P, P, i32, i32, i32, i32, u64, P, f32, P, P,
+                                        ctypes.POINTER(_Aux), P]
+    lib.spec_verify_noalloc.restype = i32
+    lib.spec_verify_noalloc_max_scratch.argtypes = []
+    lib.spec_verify_noalloc_max_scratch.restype = sz
     lib.spec_verify_status_str.argtypes = [i32]
     lib.spec_verify_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -245,6 +252,35 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
     return Verifier(target, draft, tokens, temperature, beta, workspace=workspace,
                     accepted_len=accepted_len, out_tokens=out_tokens, aux=aux, stream=stream,
                     draft_len=draft_len)(seed)
+
+
+def spec_verify_noalloc(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor,
+                        seed: int, temperature: torch.Tensor, beta: float, accepted_len: torch.Tensor,
+                        out_tokens: torch.Tensor, *, aux: dict | None = None, stream=None) -> None:
+    """The verify step through spec_verify_noalloc: no workspace, the
+    library's static scratch instead, for callers that cannot allocate device
+    memory.  Every buffer is the caller's: target [B, K+1, V], draft [B, K, V]
+    or None, tokens [B, K] int32, temperature [B] float32, accepted_len [B]
+    and out_tokens [B, K+1] int32 (written), and optionally aux, a dict of
+    p_target [B, K], p_draft [B, K], residual_mass [B], draft_conf [B, K]
+    (float32) and error_word [1] (int32, OR-ed into) tensors.  Nothing is
+    allocated here; calls on one GPU must not overlap in time."""
+    B, K1, V = target.shape
+    a = None
+    if aux is not None:
+        a = _Aux()
+        for key in ("p_target", "p_draft", "residual_mass", "error_word", "draft_conf"):
+            if aux.get(key) is not None:
+                setattr(a, key, aux[key].data_ptr())
+    _check(load_library().spec_verify_noalloc(
+        _ptr(target), _ptr(draft), _ptr(tokens), B, K1 - 1, V, _dtype_code(target),
+        int(seed) & (2**64 - 1), _ptr(temperature), ctypes.c_float(float(beta)), _ptr(accepted_len),
+        _ptr(out_tokens), ctypes.byref(a) if a is not None else None, _stream(stream)))
+
+
+def noalloc_max_scratch() -> int:
+    """Bytes of spec_verify_noalloc's static scratch."""
+    return int(load_library().spec_verify_noalloc_max_scratch())
 
 
 def row_stats(logits: torch.Tensor, temperature, *, stream=None):

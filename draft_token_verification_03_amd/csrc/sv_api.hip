@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sv_internal.h"
 
@@ -200,6 +201,31 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+// Scratch of spec_verify_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never passes the array's name to a kernel -- on the host it is a stand-in,
+// not a device address -- but the address hipGetSymbolAddress returns for the
+// current device, taken once per device and kept here.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static void *g_scratch[kMaxDevices];
+static std::mutex g_scratch_mutex;
+
+// This device's copy of scratch, or nullptr when HIP reports an error.
+static void *device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -232,6 +258,26 @@ int32_t spec_verify_ragged(const void *target_logits, const void *draft_logits,
     return sv::verify(target_logits, draft_logits, draft_tokens, draft_len, B, K, V, dtype, seed,
                       temperature, beta, accepted_len, out_tokens, workspace, workspace_bytes, aux,
                       stream);
+}
+
+size_t spec_verify_noalloc_max_scratch(void) { return sv::kScratchBytes; }
+
+int32_t spec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                            const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                            uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
+                            int32_t *out_tokens, const sv_aux *aux, void *stream)
+{
+    const int32_t v = sv::validate(target_logits, draft_logits, draft_tokens, B, K, V, dtype, temperature,
+                                   beta, accepted_len, out_tokens);
+    if (v != SV_OK || B == 0) return v;
+    // the plans of both streaming kernels must fit the static scratch
+    const size_t need = spec_verify_workspace_size(B, K, V, dtype);
+    if (need == 0) return SV_EINVAL;
+    if (need > sv::kScratchBytes) return SV_ESCRATCH;
+    void *ws = sv::device_scratch();
+    if (!ws) return SV_EHIP;
+    return sv::verify(target_logits, draft_logits, draft_tokens, nullptr, B, K, V, dtype, seed, temperature,
+                      beta, accepted_len, out_tokens, ws, sv::kScratchBytes, aux, stream);
 }
 
 size_t spec_verify_outcomes_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype, int32_t F)
@@ -412,6 +458,9 @@ const char *spec_verify_status_str(int32_t status)
     case SV_EINVAL: return "SV_EINVAL: invalid argument (nothing enqueued)";
     case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
     case SV_EHIP: return "SV_EHIP: HIP runtime error on launch";
+    case SV_ESCRATCH:
+        return "SV_ESCRATCH: these sizes need more scratch than spec_verify_noalloc's static buffer "
+               "holds (spec_verify_noalloc_max_scratch() bytes); call spec_verify with a workspace";
     default: return "unknown status";
     }
 }

@@ -74,6 +74,7 @@ extern "C" {
 #define SV_EINVAL (-1)      /* an argument is invalid; nothing was enqueued     */
 #define SV_EWORKSPACE (-2)  /* workspace NULL, misaligned or too small         */
 #define SV_EHIP (-3)        /* the HIP runtime reported an error on launch     */
+#define SV_ESCRATCH (-4)    /* spec_verify_noalloc: sizes beyond its static scratch */
 
 /* Bits of the device-side error word (see sv_aux.error_word). */
 #define SV_ERR_TOKEN 1          /* a draft token outside [0, V): treated as rejected    */
@@ -127,6 +128,30 @@ int32_t spec_verify(const void *target_logits, const void *draft_logits,
                     uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_aux *aux, void *stream);
+
+/*
+ * The verify step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * spec_verify without the workspace arguments.  Its scratch is a static
+ * device array of spec_verify_noalloc_max_scratch() bytes (32 MiB) inside the
+ * library, one per GPU, held until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  The caller
+ * passes inputs and outputs exactly as for spec_verify and gets the same
+ * results, bit for bit.  Sizes whose workspace (spec_verify_workspace_size)
+ * exceeds the static scratch return SV_ESCRATCH before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (other streams, other host threads) race and give
+ * undefined results; serialise them, or use spec_verify with distinct
+ * workspaces.  The scratch's contents before a call do not matter.  The
+ * first call on a device looks up that device's copy (hipGetSymbolAddress;
+ * SV_EHIP if that fails).
+ */
+size_t spec_verify_noalloc_max_scratch(void);
+
+int32_t spec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                            const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V, int32_t dtype,
+                            uint64_t seed, const float *temperature, float beta, int32_t *accepted_len,
+                            int32_t *out_tokens, const sv_aux *aux, void *stream);
 
 /*
  * The verify step with ragged draft lengths ("Kangaroo: Self-Speculative

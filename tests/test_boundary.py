@@ -186,3 +186,27 @@ def test_tree_validation(lib):
                 dict(t=P(A + 1)), dict(d=P(A + 0x100001)), dict(V=1 << 25)):
         assert call(**bad) == sv.SV_EINVAL, bad
     assert call(B=0, t=None, temp=None, acc=None, out=None, par=None, tok=None, path=None) == sv.SV_OK
+
+
+def test_noalloc_validation(lib):
+    """spec_verify_noalloc validates like spec_verify and rejects sizes whose
+    workspace exceeds its static scratch with SV_ESCRATCH, all before any
+    pointer is used or anything is enqueued (no device call is made here)."""
+    import draft_token_verification_03_amd as sv
+    f = lib.spec_verify_noalloc
+    assert lib.spec_verify_noalloc_max_scratch() == 32 << 20
+    # B == 0: a no-op even with NULL buffers
+    assert f(None, None, None, 0, 4, 100, sv.SV_F32, 0, None, 1.0, None, None, None, None) == sv.SV_OK
+    fake = 1 << 20
+    args = dict(t=fake, d=fake, tok=fake, B=4, K=3, V=1000, dt=sv.SV_F32, T=fake, beta=1.0, acc=fake, out=fake)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["t"], a["d"], a["tok"], a["B"], a["K"], a["V"], a["dt"], 0, a["T"], a["beta"], a["acc"],
+                 a["out"], None, None)
+
+    for bad in (dict(B=-1), dict(K=129), dict(V=0), dict(dt=5), dict(beta=2.0), dict(t=None), dict(acc=None),
+                dict(t=fake + 2)):
+        assert call(**bad) == sv.SV_EINVAL, bad
+    assert call(B=8192, K=128, V=152064, dt=sv.SV_BF16) == sv.SV_ESCRATCH
+    assert sv.status_str(sv.SV_ESCRATCH).startswith("SV_ESCRATCH")
