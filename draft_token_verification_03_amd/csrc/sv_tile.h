@@ -109,41 +109,47 @@ __device__ __forceinline__ void run_raise_lazy(RowRun &run, float lm, const ExpS
     if (__ballot(lm > run.m) != 0ull) run_raise(run, wave_max(lm), e);
 }
 
+// Pairwise fp32 sum of the exponentials of one raw vector.
+template <int DT>
+__device__ __forceinline__ float vec_sum_exp(uint4 r, float o, const ExpScale &e)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    float x[VEC], ev[VEC];
+    Elt<DT>::unpack(r, x);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], o, e);
+#pragma unroll
+    for (int w = VEC / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
+    return ev[0];
+}
+
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_tile(const uint4 (&r)[U], const ExpScale &e, RowRun &run)
 {
-    constexpr int VEC = Elt<DT>::kVec;
     run_raise_lazy(run, tile_lane_max<DT, U>(r), e);
     if (run.m == -INFINITY) return;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float x[VEC], ev[VEC];
-        Elt<DT>::unpack(r[u], x);
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.o, e);
-#pragma unroll
-        for (int w = VEC / 2; w > 0; w >>= 1)
-#pragma unroll
-            for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
-        run.s += (double)ev[0];
-    }
+    for (int u = 0; u < U; ++u) run.s += (double)vec_sum_exp<DT>(r[u], run.o, e);
 }
 
 // Beta-weighted draft row: as run_sum_tile, and each wave keeps the top-4
 // of the elements it has seen, by (value desc, index asc), in a list that
 // every lane holds alike, out of its sums; at the end of the chunk the four
 // waves' lists give the chunk's top-4 and their other entries join the sum
-// (run_finish_top).  The 4th entry is a floor that most later tiles do not
-// reach (after t tiles, a wave's next tile holds a new entry with probability
-// ~4/t), so most tiles take the plain sum.  Elements that beat the floor
-// when their tile arrives are inserted one at a time -- lanes in order, each
-// lane's in token order -- or, when a tile holds many (the first tile,
-// rising rows), through per-lane lists and the wave's top-4 of them.  An
-// entry pushed out of the list, or a candidate that no longer makes it, has
-// its mass added by a lane that the wave's own data fixes.  Every element
-// thus reaches the sum, or the chunk's top-4, along a path and in an order
-// that do not depend on how the waves are timed against each other: a call
-// gives the same bits every time.
+// (run_finish_top).  The list's 4th entry is a floor that most later tiles
+// do not reach (after t tiles a wave's next tile holds a new entry with
+// probability ~4/t), so most vectors take the plain sum.  Elements that beat
+// the floor when their vector is reached are inserted one at a time, in a
+// fixed order (element position in the vector, then lane); when many lanes
+// of a tile beat it (a wave's first tile, rising rows) the tile's floor is
+// first raised to the 4th best of the lanes' best elements, below which no
+// element of the tile can be in the top-4.  An entry pushed out of the
+// list, or a candidate that no longer makes it, has its mass added by lane
+// 0.  Every element thus reaches the sum, or the chunk's top-4, along a path
+// and in an order that depend only on the data: a call gives the same bits
+// every time.
 
 // Key of (v, i), i in [0, INT_MAX): larger keys are better entries; -0 counts
 // as +0, as in `better`.  Key 0 is an empty slot.  (Used by the outcome pass.)
@@ -165,15 +171,6 @@ __device__ __forceinline__ float key_value(uint64_t k)
 __device__ __forceinline__ int key_index(uint64_t k)
 {
     return k == 0 ? INT_MAX : 0x7fffffff - (int)(uint32_t)k;
-}
-
-__device__ __forceinline__ bool top_insert_out(Top4 &t, float v, int i, float &out_v, int &out_i)
-{
-    if (!better(v, i, t.v[3], t.i[3])) return false;
-    out_v = t.v[3];
-    out_i = t.i[3];
-    top_insert(t, v, i);
-    return true;
 }
 
 constexpr int kSerialCandidates = 16;
@@ -211,40 +208,95 @@ __device__ __forceinline__ bool wtop_has(const WaveTop &w, uint64_t k)
     return k != 0 && (w.k0 == k || w.k1 == k || w.k2 == k || w.k3 == k);
 }
 
-// One round of the wave merge: the best head of the lanes' lists (every
-// lane gets it), popped from the list that holds it.
-__device__ __forceinline__ uint64_t wtop_pop_best(WaveTop &t)
+// A floor decoded for `better`: elements (v, i) that beat it.
+struct Floor {
+    uint64_t key;
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ Floor make_floor(uint64_t key)
 {
-    // keys order as (value desc, index asc) pairs do: the wave argmax of the
-    // decoded heads (DPP butterflies) finds the best key
-    float v = key_value(t.k0);
-    int i = key_index(t.k0);
-    wave_argmax(v, i);
-    const uint64_t best = i == INT_MAX ? 0 : top_key(v, i);
-    if (best != 0 && t.k0 == best) {
-        t.k0 = t.k1;
-        t.k1 = t.k2;
-        t.k2 = t.k3;
-        t.k3 = 0;
+    Floor f;
+    f.key = key;
+    f.v = key_value(key);
+    f.i = key_index(key);
+    return f;
+}
+
+// A value the same in every lane of the wave, held as such.
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t k)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)k);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(k >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// The key just below the 4th best of the lanes' best elements (value mx at
+// the lane's lowest index bi; bi = INT_MAX for a lane without elements), or
+// 0 when fewer than four lanes hold one.  Every element of the tile with a
+// smaller key has four better ones in the tile.
+__device__ __forceinline__ uint64_t seed_floor(float mx, int bi)
+{
+    float v = mx;
+    int i = bi;
+    uint64_t k4 = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float bv = v;
+        int bj = i;
+        wave_argmax(bv, bj);
+        bj = __builtin_amdgcn_readfirstlane(bj);
+        bv = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
+        if (bj == INT_MAX) return 0;
+        if (i == bj) {  // indices are unique: the lane that held it drops out
+            v = -INFINITY;
+            i = INT_MAX;
+        }
+        k4 = top_key(bv, bj);
     }
-    return best;
+    return k4 - 1;  // the low word is 0x7fffffff - bj > 0
 }
 
-// The wave's top-4 of the lanes' lists (every lane gets it).
-__device__ __forceinline__ WaveTop wtop_wave_merge(WaveTop t)
+// Per-vector lane maxima of a tile.
+template <int DT, int U>
+__device__ __forceinline__ void tile_vec_max(const uint4 (&r)[U], float (&vm)[U])
 {
-    WaveTop out;
-    out.k0 = wtop_pop_best(t);
-    out.k1 = wtop_pop_best(t);
-    out.k2 = wtop_pop_best(t);
-    out.k3 = wtop_pop_best(t);
-    return out;
+    constexpr int VEC = Elt<DT>::kVec;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float x[VEC];
+        Elt<DT>::unpack(r[u], x);
+        float m = x[0];
+#pragma unroll
+        for (int k = 1; k < VEC; ++k) m = fmaxf(m, x[k]);
+        vm[u] = m;
+    }
 }
 
-// The floor a tile's elements must beat: the wave's 4th key, or the block's
-// floor from the last exchange of the waves' lists when that is higher (an
-// element below the block's 4th best of what all waves had seen then cannot
-// be in the chunk's top-4).
+// The lane's lowest token index (< V) holding value mx, INT_MAX if none.
+template <int DT, int U>
+__device__ __forceinline__ int lane_first_index(const uint4 (&r)[U], int q0, int V, float mx)
+{
+    constexpr int VEC = Elt<DT>::kVec;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int u = U - 1; u >= 0; --u) {
+        float x[VEC];
+        Elt<DT>::unpack(r[u], x);
+#pragma unroll
+        for (int k = VEC - 1; k >= 0; --k) {
+            const int idx = elem_index(q0, u, k, VEC);
+            if (x[k] == mx && idx < V) bi = idx;
+        }
+    }
+    return bi;
+}
+
+// The floor a tile's elements must beat is the wave's 4th key, or the
+// block's floor from the last exchange of the waves' lists when that is
+// higher (an element below the block's 4th best of what all waves had seen
+// then cannot be in the chunk's top-4).
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
                                                  const ExpScale &e, RowRun &run, WaveTop &wt,
@@ -252,43 +304,43 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
 {
     constexpr int VEC = Elt<DT>::kVec;
     const int lane = threadIdx.x & 63;
-    const uint64_t floor_key = wt.k3 > block_floor ? wt.k3 : block_floor;
-    const float fv = key_value(floor_key);
-    const int fi = key_index(floor_key);
-    const float mx = tile_lane_max<DT, U>(r);
+    float vm[U];
+    tile_vec_max<DT, U>(r, vm);
+    float mx = vm[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mx = fmaxf(mx, vm[u]);
     run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
-    // the lane's first token of the tile is its lowest
-    const bool maybe = mx > fv || (mx == fv && elem_index(q0, 0, 0, VEC) < fi);
-    if (__ballot(maybe) == 0ull) {  // no element can enter the list
+    Floor f = make_floor(wt.k3 > block_floor ? wt.k3 : block_floor);
+    // lanes that may hold an element beating the floor (equal values are
+    // told apart by index, element by element)
+    const uint64_t lanes = __ballot(!(mx < f.v));
+    if (lanes == 0ull) {
         if (!have_m) return;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[VEC], ev[VEC];
-            Elt<DT>::unpack(r[u], x);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) ev[k] = exp_scaled(x[k], run.o, e);
-#pragma unroll
-            for (int w = VEC / 2; w > 0; w >>= 1)
-#pragma unroll
-                for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
-            run.s += (double)ev[0];
-        }
+        for (int u = 0; u < U; ++u) run.s += (double)vec_sum_exp<DT>(r[u], run.o, e);
         return;
     }
-    // candidates: elements that beat the floor; the others join the sum
-    uint32_t cmask = 0;  // bit u * VEC + k
-    int ncand = 0;
+    if (__popcll(lanes) > 4) {
+        const uint64_t s = seed_floor(mx, lane_first_index<DT, U>(r, q0, V, mx));
+        if (s > f.key) f = make_floor(s);
+    }
+    const int wbase = __builtin_amdgcn_readfirstlane((int)threadIdx.x) & ~63;
+    double ulost = 0.0;  // masses leaving the list, alike in every lane
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+        if (__ballot(!(vm[u] < f.v)) == 0ull) {
+            if (have_m) run.s += (double)vec_sum_exp<DT>(r[u], run.o, e);
+            continue;
+        }
         float x[VEC], ev[VEC];
         Elt<DT>::unpack(r[u], x);
+        uint32_t cm = 0;  // bit k: element k beats the floor
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int idx = elem_index(q0, u, k, VEC);
-            const bool c = idx < V && better(x[k], idx, fv, fi);
-            cmask |= (c ? 1u : 0u) << (u * VEC + k);
-            ncand += c ? 1 : 0;
+            const bool c = idx < V && better(x[k], idx, f.v, f.i);
+            cm |= (c ? 1u : 0u) << k;
             ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.o, e);
         }
 #pragma unroll
@@ -296,70 +348,21 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
 #pragma unroll
             for (int k = 0; k < w; ++k) ev[k] += ev[k + w];
         run.s += (double)ev[0];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            uint64_t m = __ballot((cm >> k) & 1u);
+            while (m != 0ull) {
+                const int L = __ffsll((unsigned long long)m) - 1;
+                m &= m - 1ull;
+                const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), L));
+                const int i = (q0 + u * kBlock + wbase + L) * VEC + k;
+                const uint64_t out = wtop_insert(wt, top_key(v, i));
+                if (out != 0 && have_m) ulost += (double)exp_scaled(key_value(out), run.o, e);
+            }
+        }
+        if (wt.k3 > f.key) f = make_floor(wt.k3);  // later vectors face the risen floor
     }
-    double lost = 0.0;  // masses leaving the list that this lane adds
-    if (wave_sum_int(ncand) <= kSerialCandidates) {
-        // one candidate at a time, in a fixed order: element position of the
-        // tile, then lane (the lists and every mass that leaves them are
-        // alike in every lane; lane 0 adds those masses)
-        double ulost = 0.0;
-        const int wbase = (int)threadIdx.x & ~63;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (__ballot((cmask >> (u * VEC)) & ((1u << VEC) - 1u)) == 0ull) continue;
-            float x[VEC];
-            Elt<DT>::unpack(r[u], x);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                uint64_t m = __ballot((cmask >> (u * VEC + k)) & 1u);
-                while (m != 0ull) {
-                    const int L = __ffsll((unsigned long long)m) - 1;
-                    m &= m - 1ull;
-                    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), L));
-                    const int i = (q0 + u * kBlock + wbase + L) * VEC + k;
-                    const uint64_t out = wtop_insert(wt, top_key(v, i));
-                    if (out != 0 && have_m) ulost += (double)exp_scaled(key_value(out), run.o, e);
-                }
-            }
-        }
-        if (lane == 0) lost += ulost;
-    } else {
-        // many: each lane's candidates into its own list in token order, the
-        // wave's top-4 of those lists merged with the wave list
-        WaveTop t;
-        wtop_clear(t);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[VEC];
-            Elt<DT>::unpack(r[u], x);
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                if (!((cmask >> (u * VEC + k)) & 1u)) continue;
-                const uint64_t out = wtop_insert(t, top_key(x[k], elem_index(q0, u, k, VEC)));
-                if (out != 0 && have_m) lost += (double)exp_scaled(key_value(out), run.o, e);
-            }
-        }
-        const WaveTop nw = wtop_wave_merge(t);
-        WaveTop m = wt;
-        wtop_insert(m, nw.k0);
-        wtop_insert(m, nw.k1);
-        wtop_insert(m, nw.k2);
-        wtop_insert(m, nw.k3);
-        if (have_m) {
-            if (t.k0 != 0 && !wtop_has(m, t.k0)) lost += (double)exp_scaled(key_value(t.k0), run.o, e);
-            if (t.k1 != 0 && !wtop_has(m, t.k1)) lost += (double)exp_scaled(key_value(t.k1), run.o, e);
-            if (t.k2 != 0 && !wtop_has(m, t.k2)) lost += (double)exp_scaled(key_value(t.k2), run.o, e);
-            if (t.k3 != 0 && !wtop_has(m, t.k3)) lost += (double)exp_scaled(key_value(t.k3), run.o, e);
-            if (lane == 0) {
-                if (wt.k0 != 0 && !wtop_has(m, wt.k0)) lost += (double)exp_scaled(key_value(wt.k0), run.o, e);
-                if (wt.k1 != 0 && !wtop_has(m, wt.k1)) lost += (double)exp_scaled(key_value(wt.k1), run.o, e);
-                if (wt.k2 != 0 && !wtop_has(m, wt.k2)) lost += (double)exp_scaled(key_value(wt.k2), run.o, e);
-                if (wt.k3 != 0 && !wtop_has(m, wt.k3)) lost += (double)exp_scaled(key_value(wt.k3), run.o, e);
-            }
-        }
-        wt = m;
-    }
-    run.s += lost;
+    if (lane == 0) run.s += ulost;
 }
 
 // Greedy row: the lane's (max, lowest index).
@@ -418,7 +421,7 @@ __device__ __forceinline__ uint64_t block_floor_of(const WaveTop &wt, double *ld
 #pragma unroll
     for (int j = 0; j < 4 * kWaves; ++j) wtop_insert(c, all[j]);
     __syncthreads();  // lds_keys free again
-    return c.k3;
+    return wave_uniform(c.k3);
 }
 
 // Weighted draft row chunk: block max M, the chunk's top-4 from the waves'
