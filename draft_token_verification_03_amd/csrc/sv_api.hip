@@ -11,7 +11,7 @@ namespace sv {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only)
+bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only, bool weighted)
 {
     if (B < 0 || K < 0 || K > kMaxK || V < 1 || (dtype != SV_F32 && dtype != SV_BF16)) return false;
     *p = Plan{};
@@ -39,7 +39,14 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool gre
     // long rows in a batch that fills the grid by itself: two chunks a row
     // halve the size of the grid's workgroups, so its last round leaves less
     // of the chip idle
-    if (nc == 1 && p->row_bytes >= kSplitRowBytes) nc = 2;
+    if (nc == 1 && p->row_bytes >= kSplitRowBytes) {
+        nc = 2;
+        // beta-weighted draft rows keep top-4 lists per chunk, whose upkeep
+        // grows with the number of chunks: one chunk a row unless that leaves
+        // a larger share of the last round idle
+        auto idle = [](int64_t w) { return (kFillBlocks - w % kFillBlocks) % kFillBlocks; };
+        if (weighted && 2 * idle(rows) <= idle(2 * rows)) nc = 1;
+    }
     const int64_t nc_max = std::max<int64_t>(1, p->nvec / kBlock);
     const int64_t nc_stage =
         kStageBytes / ((int64_t)sizeof(RowPart) * p->R + (int64_t)sizeof(Top4) * K);
@@ -165,7 +172,8 @@ static int32_t verify(const void *target_logits, const void *draft_logits,
                                temperature, beta, accepted_len, out_tokens);
     if (v != SV_OK || B == 0) return v;
     Plan p;
-    if (!make_plan(B, K, V, dtype, &p, !draft_logits && K > 0 && !draft_len)) return SV_EINVAL;
+    if (!make_plan(B, K, V, dtype, &p, !draft_logits && K > 0 && !draft_len, beta < 1.f && K > 0))
+        return SV_EINVAL;
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < p.bytes)
         return SV_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);

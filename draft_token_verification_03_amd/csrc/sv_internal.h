@@ -67,7 +67,8 @@ struct Plan {
 
 // greedy_only: a call without draft rows (and K > 0, no ragged lengths),
 // whose streaming pass launches only target rows 0..K (argmax_kernel)
-bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only = false);
+bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool greedy_only = false,
+               bool weighted = false);
 
 struct Args {
     const char *target;     // the sub-batch's first target row

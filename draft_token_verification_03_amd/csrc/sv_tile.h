@@ -236,7 +236,7 @@ __device__ __forceinline__ uint64_t wave_uniform(uint64_t k)
 // the lane's lowest index bi; bi = INT_MAX for a lane without elements), or
 // 0 when fewer than four lanes hold one.  Every element of the tile with a
 // smaller key has four better ones in the tile.
-__device__ __forceinline__ uint64_t seed_floor(float mx, int bi)
+__device__ __forceinline__ uint64_t seed_floor_keys(float mx, int bi)
 {
     float v = mx;
     int i = bi;
@@ -256,6 +256,25 @@ __device__ __forceinline__ uint64_t seed_floor(float mx, int bi)
         k4 = top_key(bv, bj);
     }
     return k4 - 1;  // the low word is 0x7fffffff - bj > 0
+}
+
+// The 4th largest of the lanes' maxima by value (one lane dropping out per
+// round), -inf when fewer than four lanes hold a finite one; `ties` tells
+// whether another lane's maximum equals it.
+__device__ __forceinline__ float seed_floor_value(float mx, bool &ties)
+{
+    const int lane = threadIdx.x & 63;
+    float v = mx;
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        M = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(v))));
+        if (M == -INFINITY) break;
+        const uint64_t at = __ballot(v == M);
+        if (lane == __ffsll((unsigned long long)at) - 1) v = -INFINITY;
+    }
+    ties = __ballot(v == M) != 0ull;
+    return M;
 }
 
 // Per-vector lane maxima of a tile.
@@ -296,7 +315,11 @@ __device__ __forceinline__ int lane_first_index(const uint4 (&r)[U], int q0, int
 // The floor a tile's elements must beat is the wave's 4th key, or the
 // block's floor from the last exchange of the waves' lists when that is
 // higher (an element below the block's 4th best of what all waves had seen
-// then cannot be in the chunk's top-4).
+// then cannot be in the chunk's top-4).  Such a floor comes from lower token
+// indices than any element of the tile, so an element beats it exactly when
+// its value is larger; so does a list key taken after the tile's vectors up
+// to u, for the vectors after u.  A floor seeded from the tile itself, or an
+// empty one, is tested with indices (`full`).
 template <int DT, int U>
 __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, int V,
                                                  const ExpScale &e, RowRun &run, WaveTop &wt,
@@ -312,9 +335,8 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
     run_raise_lazy(run, mx, e);
     const bool have_m = run.m != -INFINITY;
     Floor f = make_floor(wt.k3 > block_floor ? wt.k3 : block_floor);
-    // lanes that may hold an element beating the floor (equal values are
-    // told apart by index, element by element)
-    const uint64_t lanes = __ballot(!(mx < f.v));
+    bool full = f.key == 0;
+    const uint64_t lanes = __ballot(full ? !(mx < f.v) : mx > f.v);
     if (lanes == 0ull) {
         if (!have_m) return;
 #pragma unroll
@@ -322,25 +344,34 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
         return;
     }
     if (__popcll(lanes) > 4) {
-        const uint64_t s = seed_floor(mx, lane_first_index<DT, U>(r, q0, V, mx));
-        if (s > f.key) f = make_floor(s);
+        // many lanes: first raise this tile's floor from its lanes' maxima
+        bool ties;
+        const float v4 = seed_floor_value(mx, ties);
+        // every element below v4 has four larger ones; elements equal to it
+        // all stay candidates
+        uint64_t s = v4 == -INFINITY ? 0 : top_key(v4, 0x7fffffff);
+        if (ties) s = seed_floor_keys(mx, lane_first_index<DT, U>(r, q0, V, mx));
+        if (s > f.key) {
+            f = make_floor(s);
+            full = true;
+        }
     }
     const int wbase = __builtin_amdgcn_readfirstlane((int)threadIdx.x) & ~63;
     double ulost = 0.0;  // masses leaving the list, alike in every lane
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (__ballot(!(vm[u] < f.v)) == 0ull) {
+        if (__ballot(full ? !(vm[u] < f.v) : vm[u] > f.v) == 0ull) {
             if (have_m) run.s += (double)vec_sum_exp<DT>(r[u], run.o, e);
             continue;
         }
         float x[VEC], ev[VEC];
         Elt<DT>::unpack(r[u], x);
-        uint32_t cm = 0;  // bit k: element k beats the floor
+        uint64_t cm[VEC];  // lanes whose element k beats the floor
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int idx = elem_index(q0, u, k, VEC);
-            const bool c = idx < V && better(x[k], idx, f.v, f.i);
-            cm |= (c ? 1u : 0u) << k;
+            const bool c = full ? idx < V && better(x[k], idx, f.v, f.i) : x[k] > f.v;
+            cm[k] = __ballot(c);
             ev[k] = (c || !have_m) ? 0.f : exp_scaled(x[k], run.o, e);
         }
 #pragma unroll
@@ -350,7 +381,7 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
         run.s += (double)ev[0];
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            uint64_t m = __ballot((cm >> k) & 1u);
+            uint64_t m = cm[k];
             while (m != 0ull) {
                 const int L = __ffsll((unsigned long long)m) - 1;
                 m &= m - 1ull;
@@ -360,7 +391,10 @@ __device__ __forceinline__ void run_sum_top_tile(const uint4 (&r)[U], int q0, in
                 if (out != 0 && have_m) ulost += (double)exp_scaled(key_value(out), run.o, e);
             }
         }
-        if (wt.k3 > f.key) f = make_floor(wt.k3);  // later vectors face the risen floor
+        if (wt.k3 > f.key) {  // later vectors face the risen floor
+            f = make_floor(wt.k3);
+            full = false;
+        }
     }
     if (lane == 0) run.s += ulost;
 }

@@ -226,10 +226,10 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
             int tiles = 0;
             stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
                 run_sum_top_tile<DT, kLoads>(t, qb, a.V, e, run, wt, block_floor);
-                ++tiles;
-                // the waves share their lists after 1, 2 and 4 tiles: the block's
-                // floor rises with four waves' data instead of one's
-                if (tiles == 1 || tiles == 2 || tiles == 4) block_floor = block_floor_of(wt, lds_keys);
+                // the waves share their lists after the first tile: the block's
+                // floor rises with four waves' data instead of one's (later
+                // exchanges measured slower than the candidates they save)
+                if (++tiles == 1) block_floor = block_floor_of(wt, lds_keys);
             });
             run_finish_top(run, wt, e, lds_f, lds_keys, lds_d, part.m, part.s, ct);
             if (threadIdx.x < 4) {
