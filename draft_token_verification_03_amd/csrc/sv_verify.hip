@@ -16,7 +16,11 @@
 //   3. bonus_kernel  one workgroup per sequence: inverse CDF over the slot
 //                    masses, then over the elements of the selected slot.
 //
-// The three launches are stream-ordered; every kernel reads only what earlier
+// Calls without draft rows (only greedy sequences can verify there) replace
+// steps 2 and 3 by accept_kernel: the accept scan alone, one workgroup per
+// sequence.
+//
+// The launches are stream-ordered; every kernel reads only what earlier
 // launches wrote, so no workgroup ever waits for another.
 #include <algorithm>
 
@@ -924,6 +928,17 @@ __global__ __launch_bounds__(kBlock) void residual_kernel(const Args a)
         residual_slots<DT, TOP, kWaves, 2>(trow, drow, a.V, a.nvec, s0, s1, a.gs, st, e, rs, slot);
 }
 
+// The accept scan alone, one workgroup per sequence: it writes the outputs
+// (all but a sampling sequence's bonus token) and the sequence's outcome.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void accept_kernel(const Args a)
+{
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    AcceptLds L;
+    accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, dyn_lds, &L);
+    accept_sequence<DT>(a, blockIdx.x, L, true);
+}
+
 // ---------------------------------------------------------------------------
 // 4. Bonus draw by inverse CDF in ascending token id: the smallest v with
 // C(v) >= u * Z, Z the total residual mass, first over the slot masses, then
@@ -1160,9 +1175,14 @@ static void launch_all(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_
         stats_kernel<DT, TOP><<<grid, kBlock, 0, s>>>(a);
     }
     const size_t lds = accept_lds_layout(a.R, a.K, a.nc, a.weighted != 0, nullptr, nullptr);
+    if (greedy_only) {
+        // every sequence is greedy or fails: the accept scan alone finishes
+        // them, one workgroup per sequence, with no residual pass or bonus draw
+        accept_kernel<DT><<<(unsigned)a.B, kBlock, lds, s>>>(a);
+        return;
+    }
     residual_kernel<DT, TOP><<<(unsigned)((int64_t)a.B * a.ng), kBlock, lds, s>>>(a);
-    // without draft logits (K > 0) every sequence is greedy or fails: no bonus draw
-    if (a.draft || a.K == 0 || a.draft_len) bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
+    bonus_kernel<DT, TOP><<<(unsigned)a.B, kBlock, 0, s>>>(a);
 }
 
 void launch_verify(const Args &a, hipStream_t s, hipEvent_t begin, hipEvent_t end)
