@@ -87,24 +87,34 @@ __device__ __forceinline__ void fix_tile(int qb, int q1, int V, uint4 (&r)[kLoad
 // `ra` holds the (already requested) tile at q0.  The row's alignment is a
 // template parameter so that no loaded register passes a branch join (a
 // join copies registers, and a copy waits for its load).
+//
+// The steady state issues its loads unconditionally: a load issued under a
+// condition leaves its registers "loaded or not" at the join, and a consumer
+// with branches of its own (the beta-weighted rows) then gets register
+// copies there, which wait for the loads just issued -- one tile in flight
+// instead of two.  The last one or two tiles are peeled.
 template <int DT, bool ALIGNED, class Consume>
 __device__ __forceinline__ void stream_chunk(const char *row, int q0, int q1, int V,
                                              uint4 (&ra)[kLoads], Consume &&consume)
 {
     constexpr int kStep = kBlock * kLoads;
+    const int nt = (q1 - q0 + kStep - 1) / kStep;  // tiles in the chunk, >= 1
     uint4 rb[kLoads];
-    for (int qb = q0;;) {
-        const int qn = qb + kStep;
-        if (qn < q1) issue_tile<DT, ALIGNED>(row, qn, q1, V, rb);
-        if (qn >= q1) fix_tile<DT>(qb, q1, V, ra);
+    int qb = q0;
+    for (int t = 0; t + 2 < nt; t += 2, qb += 2 * kStep) {
+        issue_tile<DT, ALIGNED>(row, qb + kStep, q1, V, rb);
         consume(ra, qb);
-        if (qn >= q1) return;
-        const int qn2 = qn + kStep;
-        if (qn2 < q1) issue_tile<DT, ALIGNED>(row, qn2, q1, V, ra);
-        if (qn2 >= q1) fix_tile<DT>(qn, q1, V, rb);
-        consume(rb, qn);
-        if (qn2 >= q1) return;
-        qb = qn2;
+        issue_tile<DT, ALIGNED>(row, qb + 2 * kStep, q1, V, ra);
+        consume(rb, qb + kStep);
+    }
+    if (qb + kStep < q1) {  // two tiles left
+        issue_tile<DT, ALIGNED>(row, qb + kStep, q1, V, rb);
+        consume(ra, qb);
+        fix_tile<DT>(qb + kStep, q1, V, rb);
+        consume(rb, qb + kStep);
+    } else {
+        fix_tile<DT>(qb, q1, V, ra);
+        consume(ra, qb);
     }
 }
 
