@@ -1,5 +1,5 @@
-// sv_tile.h -- per-thread reductions of the streaming pass, shared by the
-// two-launch and the four-launch paths.
+// sv_tile.h -- per-thread tile reductions of the streaming pass, shared by
+// the verify step, the outcome distribution and the tree walk.
 //
 // A tile is U 16-byte vectors per thread: vector u of thread t is row vector
 // q0 + u * kBlock + t, so element k of it is token (q0 + u*kBlock + t)*VEC + k

@@ -303,10 +303,13 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(const Args a)
 
 // Calls without draft rows and with K > 0 drafts for every sequence (no
 // ragged lengths): only greedy sequences can verify (a sampling sequence
-// fails without its draft rows), so only the argmax of target rows 0..K is
-// needed.  The kernel holds none of the sampling code's registers.
+// fails without its draft rows, in the accept scan), so only the argmax of
+// target rows 0..K is needed, and every row is streamed without waiting for
+// its sequence's temperature (the wait held back the second tile of every
+// workgroup of a one-round grid).  The kernel holds none of the sampling
+// code's registers.
 template <int DT, bool ALIGNED>
-__device__ __forceinline__ void argmax_chunk(const Args &a, const char *row, int b, int slot_row, int chunk)
+__device__ __forceinline__ void argmax_chunk(const Args &a, const char *row, int slot_row, int chunk)
 {
     __shared__ float lds_f[4 + kWaves * 4];
     __shared__ int lds_i[4 + kWaves * 4];
@@ -314,7 +317,6 @@ __device__ __forceinline__ void argmax_chunk(const Args &a, const char *row, int
     const int q1 = min(a.nvec, q0 + a.cvec);
     uint4 r[kLoads];
     issue_tile<DT, ALIGNED>(row, q0, q1, a.V, r);
-    if (a.temperature[b] != 0.f) return;  // checked while the first tile is in flight
     float best = -INFINITY;
     int bi = INT_MAX;
     stream_chunk<DT, ALIGNED>(row, q0, q1, a.V, r, [&](uint4 (&t)[kLoads], int qb) {
@@ -337,8 +339,8 @@ __global__ __launch_bounds__(kBlock) void argmax_kernel(const Args a)
     const int b = (blockIdx.x / a.nc) / (a.K + 1);
     const int j = blockIdx.x / a.nc - b * (a.K + 1);
     const char *row = target_row(a, b, j);
-    if (((uintptr_t)row & 15) == 0) argmax_chunk<DT, true>(a, row, b, b * a.R + j, chunk);
-    else argmax_chunk<DT, false>(a, row, b, b * a.R + j, chunk);
+    if (((uintptr_t)row & 15) == 0) argmax_chunk<DT, true>(a, row, b * a.R + j, chunk);
+    else argmax_chunk<DT, false>(a, row, b * a.R + j, chunk);
 }
 
 // ---------------------------------------------------------------------------
