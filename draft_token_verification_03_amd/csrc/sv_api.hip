@@ -63,7 +63,10 @@ bool make_plan(int32_t B, int32_t K, int32_t V, int32_t dtype, Plan *p, bool gre
     gs = std::max<int64_t>(gs, (units + kMaxResSlots - 1) / kMaxResSlots);
     p->gs = (int32_t)gs;
     p->nslot = (int32_t)((units + gs - 1) / gs);
-    p->ng = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ng_fill, p->nslot));
+    // at least one slot per wave: a workgroup's waves take its slots in turn,
+    // and one with fewer slots than waves still pays the whole accept scan
+    const int64_t ng_max = (p->nslot + kWaves - 1) / kWaves;
+    p->ng = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ng_fill, ng_max));
     p->spg = (p->nslot + p->ng - 1) / p->ng;
     p->ng = (p->nslot + p->spg - 1) / p->spg;
     if ((int64_t)p->sB * p->R * p->nc >= ((int64_t)1 << 31) || (int64_t)p->sB * p->ng >= ((int64_t)1 << 31))
