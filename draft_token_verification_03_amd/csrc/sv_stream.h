@@ -76,25 +76,32 @@ __device__ __forceinline__ void fix_pair(int qb, int q1, int V, PairTileU<U> &r)
 }
 
 // Stream [q0, q1) through consume(tile, qb) with two tiles in flight; `ra`
-// holds the already requested tile at q0.
+// holds the already requested tile at q0.  As the streaming pass's loop: the
+// steady state issues unconditionally (a load issued under a condition
+// leaves its registers "loaded or not" at the join, where copies would wait
+// for it), and the last one or two tiles are peeled.
 template <int DT, bool ALIGNED, bool PAIR, int BLK = kBlock, int U, class Consume>
 __device__ __forceinline__ void stream_pair(const char *trow, const char *drow, int q0, int q1, int V,
                                             PairTileU<U> &ra, Consume &&consume)
 {
     constexpr int kStep = BLK * U;
+    const int nt = (q1 - q0 + kStep - 1) / kStep;  // tiles, >= 1
     PairTileU<U> rb;
-    for (int qb = q0;;) {
-        const int qn = qb + kStep;
-        if (qn < q1) issue_pair<DT, ALIGNED, PAIR, BLK>(trow, drow, qn, q1, V, rb);
-        if (qn >= q1) fix_pair<DT, PAIR, BLK>(qb, q1, V, ra);
+    int qb = q0;
+    for (int t = 0; t + 2 < nt; t += 2, qb += 2 * kStep) {
+        issue_pair<DT, ALIGNED, PAIR, BLK>(trow, drow, qb + kStep, q1, V, rb);
         consume(ra, qb);
-        if (qn >= q1) return;
-        const int qn2 = qn + kStep;
-        if (qn2 < q1) issue_pair<DT, ALIGNED, PAIR, BLK>(trow, drow, qn2, q1, V, ra);
-        if (qn2 >= q1) fix_pair<DT, PAIR, BLK>(qn, q1, V, rb);
-        consume(rb, qn);
-        if (qn2 >= q1) return;
-        qb = qn2;
+        issue_pair<DT, ALIGNED, PAIR, BLK>(trow, drow, qb + 2 * kStep, q1, V, ra);
+        consume(rb, qb + kStep);
+    }
+    if (qb + kStep < q1) {  // two tiles left
+        issue_pair<DT, ALIGNED, PAIR, BLK>(trow, drow, qb + kStep, q1, V, rb);
+        consume(ra, qb);
+        fix_pair<DT, PAIR, BLK>(qb + kStep, q1, V, rb);
+        consume(rb, qb + kStep);
+    } else {
+        fix_pair<DT, PAIR, BLK>(qb, q1, V, ra);
+        consume(ra, qb);
     }
 }
 
