@@ -56,6 +56,7 @@ static_assert(kTreeBlock * kTreeLoads == kTreeStepVecs, "tile step of the tree w
 // the fp32 kappa split into hi + lo parts so that one fma rounds it once.
 // A pass of kLawTarget forms w = exp2(z_t c - o_t) = S_t p(v) (A = 0).
 constexpr int kLawTarget = 0, kLawResidual = 1;
+constexpr int kWaveSteps = 64;  // tile steps a row may have for the barrier-free law pass
 
 struct Law {
     ExpScale e;
@@ -115,22 +116,49 @@ __device__ __forceinline__ void row_pass(const char *trow, const char *drow, int
 }
 
 // Mass of a law per tile step into ssum[] (fp64 step sums of the threads'
-// fp32 vector sums); returns the total.
+// fp32 vector sums, the waves' sums added in wave order); returns the total
+// (the step sums added in step order).  Rows of at most kWaveSteps steps keep
+// each wave's step sums in wsum[] and add them up after the pass, so the waves
+// stream without a barrier per step; longer rows reduce every step at once.
 template <int DT, int MODE>
 __device__ __forceinline__ double law_pass(const char *trow, const char *drow, int nvec, int V, const Law &w,
-                                           double *ssum, double *lds_d)
+                                           double *ssum, double *wsum, double *lds_d)
 {
     constexpr int VEC = Elt<DT>::kVec;
     constexpr int kStep = kTreeBlock * kTreeLoads;
-    double total = 0.0;
-    auto consume = [&](TreeTile &tl, int qb) {
+    const int nsteps = (nvec + kStep - 1) / kStep;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    auto part_of = [&](TreeTile &tl) {
         double part = 0.0;
 #pragma unroll
         for (int u = 0; u < kTreeLoads; ++u) {
             float m[VEC];
             part += (double)law_vec<DT, MODE>(tl.t[u], tl.d[u], w, m);
         }
-        const double s = block_sum<kTreeWaves>(part, lds_d);
+        return part;
+    };
+    if (nsteps <= kWaveSteps) {
+        auto consume = [&](TreeTile &tl, int qb) {
+            const double ws = wave_sum(part_of(tl));
+            if (lane == 0) wsum[(qb / kStep) * kTreeWaves + wave] = ws;
+        };
+        if (MODE == kLawTarget) row_pass<DT, false>(trow, nullptr, nvec, V, consume);
+        else row_pass<DT, true>(trow, drow, nvec, V, consume);
+        __syncthreads();
+        for (int k = threadIdx.x; k < nsteps; k += kTreeBlock) {
+            double v = wsum[k * kTreeWaves];
+#pragma unroll
+            for (int x = 1; x < kTreeWaves; ++x) v += wsum[k * kTreeWaves + x];
+            ssum[k] = v;
+        }
+        __syncthreads();
+        double total = 0.0;
+        for (int k = 0; k < nsteps; ++k) total += ssum[k];
+        return total;
+    }
+    double total = 0.0;
+    auto consume = [&](TreeTile &tl, int qb) {
+        const double s = block_sum<kTreeWaves>(part_of(tl), lds_d);
         if (threadIdx.x == 0) ssum[qb / kStep] = s;
         total += s;
     };
@@ -274,6 +302,7 @@ __device__ __forceinline__ int law_draw(const char *trow, const char *drow, int 
 struct TreeShared {
     int32_t par[kMaxK], tok[kMaxK];
     int32_t path[kMaxK], out[kMaxK + 1];
+    double wsum[kWaveSteps * kTreeWaves];      // the waves' step sums of a law pass
     double ssum[kMaxTreeSteps];
     int32_t next, err;
 };
@@ -413,7 +442,7 @@ __global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
             // step for the bonus; its pass sums S_t P z, z the residual's mass
             const double A2 = A + P;
             law_kappa(w, k0 + log2(A2));
-            const double sw = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            const double sw = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, sh.wsum, lds_d);
             if (sw > 0.0) {
                 A = A2;
                 P = sw / St;  // P z
@@ -435,12 +464,12 @@ __global__ __launch_bounds__(kTreeBlock) void tree_kernel(const TreeArgs t)
         // no child left: the bonus from the current law
         const float uB = philox_uniform(t.seed, (uint32_t)(t.b0 + b), (uint32_t)d, kPurposeBonus);
         if (A == 0.0) {
-            const double tot = law_pass<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, lds_d);
+            const double tot = law_pass<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, sh.wsum, lds_d);
             bonus = law_draw<DT, kLawTarget>(trow, nullptr, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
         } else {
             law_kappa(w, k0 + log2(A));
             double tot = ssum_total;
-            if (!ssum_ready) tot = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, lds_d);
+            if (!ssum_ready) tot = law_pass<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, sh.wsum, lds_d);
             bonus = law_draw<DT, kLawResidual>(trow, drow, t.nvec, V, w, sh.ssum, (double)uB * tot, lds_d, lds_i);
         }
         break;
