@@ -435,53 +435,69 @@ __device__ __forceinline__ void run_finish(const RowRun &run, const ExpScale &e,
     S = block_sum(sc, lds_d);
 }
 
-// Exchange of the waves' lists after a fixed number of tiles (the same in
-// every wave, so the result is too): the 4th best of the four lists' keys.
-// lds_keys holds 4 * kWaves 8-byte words.
-__device__ __forceinline__ uint64_t block_floor_of(const WaveTop &wt, double *lds_keys)
+// Lanes 0..3 of each wave store its list in lds_keys (a fixed field per
+// lane: a select between fields by lane would become an indexed access that
+// keeps the list out of registers); the four words after the waves' are
+// cleared for top4_ranked.  lds_keys holds 4 * kWaves + 4 8-byte words.
+__device__ __forceinline__ void store_wave_list(const WaveTop &wt, double *lds_keys)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint64_t *keys = reinterpret_cast<uint64_t *>(lds_keys) + wave * 4;
-    // a fixed field per lane (a select between fields by lane would become an
-    // indexed access that keeps the list out of registers)
     if (lane == 0) keys[0] = wt.k0;
     if (lane == 1) keys[1] = wt.k1;
     if (lane == 2) keys[2] = wt.k2;
     if (lane == 3) keys[3] = wt.k3;
+    if (threadIdx.x < 4) reinterpret_cast<uint64_t *>(lds_keys)[4 * kWaves + threadIdx.x] = 0;
+}
+
+// The best four of the waves' 16 keys (stored, then a barrier): thread j < 16
+// counts the keys above key j -- non-empty keys are distinct, so that is its
+// place -- and the four best land in the cleared words after the lists.
+// Every thread gets them after a second barrier.
+__device__ __forceinline__ WaveTop top4_ranked(double *lds_keys)
+{
+    uint64_t *all = reinterpret_cast<uint64_t *>(lds_keys);
+    const int tid = threadIdx.x;
+    if (tid < 4 * kWaves) {
+        const uint64_t k = all[tid];
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < 4 * kWaves; ++i) rank += all[i] > k ? 1 : 0;
+        if (k != 0 && rank < 4) all[4 * kWaves + rank] = k;
+    }
     __syncthreads();
     WaveTop c;
-    wtop_clear(c);
-    const uint64_t *all = reinterpret_cast<const uint64_t *>(lds_keys);
-#pragma unroll
-    for (int j = 0; j < 4 * kWaves; ++j) wtop_insert(c, all[j]);
+    c.k0 = all[4 * kWaves];
+    c.k1 = all[4 * kWaves + 1];
+    c.k2 = all[4 * kWaves + 2];
+    c.k3 = all[4 * kWaves + 3];
+    return c;
+}
+
+// Exchange of the waves' lists after a fixed number of tiles (the same in
+// every wave, so the result is too): the 4th best of the four lists' keys.
+__device__ __forceinline__ uint64_t block_floor_of(const WaveTop &wt, double *lds_keys)
+{
+    store_wave_list(wt, lds_keys);
+    __syncthreads();
+    const WaveTop c = top4_ranked(lds_keys);
     __syncthreads();  // lds_keys free again
     return wave_uniform(c.k3);
 }
 
 // Weighted draft row chunk: block max M, the chunk's top-4 from the waves'
-// lists (merged in wave order), and the mass outside it: the lanes' sums and
-// the wave-list entries the chunk's top-4 does not keep.  lds_f holds kWaves
-// entries, lds_keys 4 * kWaves 8-byte words.
+// lists, and the mass outside it: the lanes' sums and the wave-list entries
+// the chunk's top-4 does not keep (lanes 0..3 of each wave take one entry
+// each, added as a quad).  lds_f holds kWaves entries, lds_keys 4 * kWaves +
+// 4 8-byte words.
 __device__ __forceinline__ void run_finish_top(const RowRun &run, const WaveTop &wt, const ExpScale &e,
                                                float *lds_f, double *lds_keys, double *lds_d, float &M,
                                                double &S_excl, Top4 &ct)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    store_wave_list(wt, lds_keys);
     M = block_max(run.m, lds_f);  // uses entries 0..kWaves-1, ends with a barrier
-    // each of lanes 0..3 stores one key of its wave's list (a fixed field
-    // per lane: a select between fields by lane would become an indexed
-    // access that keeps the list out of registers)
-    uint64_t *keys = reinterpret_cast<uint64_t *>(lds_keys) + wave * 4;
-    if (lane == 0) keys[0] = wt.k0;
-    if (lane == 1) keys[1] = wt.k1;
-    if (lane == 2) keys[2] = wt.k2;
-    if (lane == 3) keys[3] = wt.k3;
-    __syncthreads();
-    WaveTop c;
-    wtop_clear(c);
-    const uint64_t *all = reinterpret_cast<const uint64_t *>(lds_keys);
-#pragma unroll
-    for (int j = 0; j < 4 * kWaves; ++j) wtop_insert(c, all[j]);
+    const WaveTop c = top4_ranked(lds_keys);
     const uint64_t ck[4] = {c.k0, c.k1, c.k2, c.k3};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -490,13 +506,14 @@ __device__ __forceinline__ void run_finish_top(const RowRun &run, const WaveTop 
     }
     const double oM = (double)row_offset(M, e);
     double sc = (run.m == -INFINITY) ? 0.0 : run.s * exp2((double)run.o - oM);
-    if (lane == 0) {
-        const uint64_t wk[4] = {wt.k0, wt.k1, wt.k2, wt.k3};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (wk[j] != 0 && key_value(wk[j]) != -INFINITY && !wtop_has(c, wk[j]))
-                sc += exp_scaled64(key_value(wk[j]), oM, e.c64);
+    double out = 0.0;
+    if (lane < 4) {
+        const uint64_t k = reinterpret_cast<const uint64_t *>(lds_keys)[wave * 4 + lane];
+        if (k != 0 && key_value(k) != -INFINITY && !wtop_has(c, k)) out = exp_scaled64(key_value(k), oM, e.c64);
     }
+    out += dpp_double<kDppQuadXor1>(out);
+    out += dpp_double<kDppQuadXor2>(out);
+    if (lane == 0) sc += out;
     S_excl = block_sum(sc, lds_d);
 }
 

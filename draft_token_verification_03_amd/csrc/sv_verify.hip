@@ -233,7 +233,7 @@ __device__ __forceinline__ void stats_chunk(const Args &a, const char *row, int 
         RowRun run;
         run_clear(run);
         if (track_top) {
-            __shared__ double lds_keys[kWaves * 4];  // the waves' lists, exchanged
+            __shared__ double lds_keys[kWaves * 4 + 4];  // the waves' lists, exchanged, and their best four
             WaveTop wt;  // this wave's top-4 so far, alike in every lane
             wtop_clear(wt);
             uint64_t block_floor = 0;
