@@ -1,0 +1,143 @@
+"""The output law of the HIP path, tested directly (no oracle).
+
+Losslessness ("Kangaroo: Self-Speculative Decoding via Shallow
+Sub-Networks", "3. Lossless Speculative Verification"; glossary
+"speculative decoding llm", "Why It Produces Identical Outputs"): with drafts
+drawn from the draft law q' (beta-weighted as in "Speculative Speculative
+Decoding", "Method"), the tokens the verify step emits follow the target law
+at every position reached, and the draft at position i is accepted with
+probability sum_v min(p_i, q'_i).  The joint law of (n, y_0..y_n) is the
+product of min(p_j, q'_j)(y_j) over the accepted positions times the clamped
+residual max(p_n - q'_n, 0)(y_n), or p_K(y_K) after K acceptances.
+
+Each case runs 10^6 sequences of one fixed set of rows in a single call of
+the library (sub-batches of launches), every sequence drafting its own
+tokens from q' on the host and drawing its own Philox streams on the GPU.
+The laws are formed in double precision from the exact input values
+(tests/pins.py); counts are compared by Pearson chi-square (p > 0.01, cells
+expecting fewer than 5 pooled) and the accept counts by a binomial test.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from pins import (binom_pvalue, chi2_pvalue, draft_law, exact_values, sample_categorical, softmax,
+                  to_bf16_bits)
+
+pytestmark = pytest.mark.gpu
+
+_SKIP = not torch.cuda.is_available()
+TRIALS = 1_000_000
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if _SKIP:
+        pytest.skip("no GPU")
+    import draft_token_verification_03_amd as sv
+    sv.load_library()
+    return sv
+
+
+def _rows(rng, V, K, spread, noise):
+    base = rng.normal(size=(K + 1, V)) * spread
+    tgt = (base + noise * rng.normal(size=(K + 1, V))).astype(np.float32)
+    drf = base[:K].astype(np.float32)
+    return tgt, drf
+
+
+def _run(sv, tgt, drf, T, beta, dtype, seed, rng):
+    """10^6 sequences of the rows (tgt [K+1, V], drf [K, V]) through the
+    library; returns (accepted_len, out_tokens, drafted tokens, p, q)."""
+    K1, V = tgt.shape
+    K = K1 - 1
+    if dtype == "bf16":
+        traw, draw_ = to_bf16_bits(tgt), to_bf16_bits(drf)
+        tt = torch.from_numpy(traw.view(np.int16)).view(torch.bfloat16)
+        dt = torch.from_numpy(draw_.view(np.int16)).view(torch.bfloat16)
+    else:
+        traw, draw_ = tgt, drf
+        tt, dt = torch.from_numpy(tgt), torch.from_numpy(drf)
+    tz, dz = exact_values(traw), exact_values(draw_)
+    Tq = float(np.float32(T))
+    p = [softmax(tz[i], Tq) for i in range(K + 1)]
+    q = [draft_law(dz[i], Tq, beta) for i in range(K)]
+    tokens = np.stack([sample_categorical(rng, q[i], TRIALS) for i in range(K)], axis=1).astype(np.int32)
+    dev = torch.device("cuda:0")
+    target = tt.to(dev).unsqueeze(0).expand(TRIALS, K1, V).contiguous()
+    draft = dt.to(dev).unsqueeze(0).expand(TRIALS, K, V).contiguous()
+    temp = torch.full((TRIALS,), Tq, dtype=torch.float32, device=dev)
+    acc, out = sv.spec_verify(target, draft, torch.from_numpy(tokens).to(dev), seed, temp, beta)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.cpu().numpy(), tokens, p, q
+
+
+LAW_CASES = [
+    # V, K, T, beta, dtype
+    (8, 2, 1.0, 1.0, "fp32"),
+    (16, 2, 0.5, 0.5, "fp32"),
+    (12, 1, 2.0, 0.0, "bf16"),
+    (6, 2, 0.7, 0.5, "bf16"),
+]
+
+
+@pytest.mark.parametrize("V,K,T,beta,dtype", LAW_CASES)
+def test_emitted_tokens_follow_the_target_law(sv, V, K, T, beta, dtype):
+    """At every position i the emitted token follows p_i, and the draft at i
+    is accepted with probability sum_v min(p_i, q'_i)."""
+    rng = np.random.default_rng(5000 + V * 10 + K)
+    tgt, drf = _rows(rng, V, K, spread=1.5, noise=0.9)
+    n, out, tokens, p, q = _run(sv, tgt, drf, T, beta, dtype, 313, rng)
+    assert n.min() >= 0 and n.max() <= K
+    for i in range(K + 1):
+        reached = n >= i
+        y = out[reached, i]
+        assert np.all((y >= 0) & (y < V))
+        assert chi2_pvalue(np.bincount(y, minlength=V), p[i]) > 0.01, f"position {i}"
+        if i < K:
+            alpha = np.minimum(p[i], q[i]).sum()
+            assert binom_pvalue(int((n[reached] > i).sum()), int(reached.sum()), alpha) > 0.01, i
+    # the accepted prefix is the drafts, then the bonus, then padding
+    idx = np.arange(0, TRIALS, 997)
+    for b in idx:
+        k = n[b]
+        assert np.array_equal(out[b, :k], tokens[b, :k])
+        assert np.all(out[b, k + 1:] == -1)
+
+
+@pytest.mark.parametrize("beta", [1.0, 0.5])
+def test_joint_law_of_the_outcome(sv, beta):
+    """The joint law of (n, y_0..y_n) over all 4 + 16 + 64 cells (V=4, K=2)."""
+    rng = np.random.default_rng(4242)
+    V, K, T = 4, 2, 0.9
+    tgt, drf = _rows(rng, V, K, spread=1.0, noise=1.0)
+    n, out, _, p, q = _run(sv, tgt, drf, T, beta, "fp32", 29, rng)
+    cells = {}
+    for k in range(K + 1):
+        for ys in np.ndindex(*([V] * (k + 1))):
+            pr = 1.0
+            for j in range(k):
+                pr *= min(p[j][ys[j]], q[j][ys[j]])
+            last = ys[k]
+            pr *= max(p[k][last] - q[k][last], 0.0) if k < K else p[K][last]
+            cells[(k,) + ys] = pr
+    assert abs(sum(cells.values()) - 1.0) < 1e-12
+    # cell index of every sequence: (n, y_0..y_n) in base V with an offset per n
+    offs = np.cumsum([0] + [V ** (k + 1) for k in range(K + 1)])
+    code = np.zeros(TRIALS, dtype=np.int64)
+    for j in range(K + 1):
+        use = n >= j
+        code[use] = code[use] * V + out[use, j]
+    code += offs[n]
+    counts = np.bincount(code, minlength=offs[-1])
+    probs = np.zeros(offs[-1])
+    for key, pr in cells.items():
+        k = key[0]
+        c = 0
+        for y in key[1:]:
+            c = c * V + y
+        probs[offs[k] + c] = pr
+    assert counts.sum() == TRIALS
+    assert chi2_pvalue(counts, probs) > 0.01
