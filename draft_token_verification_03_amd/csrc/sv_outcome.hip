@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t x, int k)
 struct PosConst {
     ExpScale e;
     float ot, od;     // offsets of the target and draft row maxima
-    float delta;      // fp32(log2(D / S_t))
+    float nad;        // fp32(delta - o_t), delta = log2(D / S_t): a + delta in one fma
     float lbeta;      // log2(beta) (-inf for beta == 0)
     float z4;         // a weighted draft row's 4th largest logit
     Top4 top;         // and its top-4
@@ -129,7 +129,7 @@ __device__ __forceinline__ void pair_tile(const PairTile &tl, int qb, int V, con
         Elt<DT>::unpack(tl.d[u], y);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float A = __builtin_fmaf(x[k], pc.e.c, -pc.ot) + pc.delta;
+            const float A = __builtin_fmaf(x[k], pc.e.c, pc.nad);
             const float B = __builtin_fmaf(y[k], pc.e.c, -pc.od);
             const float ea = __builtin_amdgcn_exp2f(A), eb = __builtin_amdgcn_exp2f(B);
             ev[k] = fminf(ea, eb);
@@ -157,7 +157,7 @@ __device__ __forceinline__ void pair_tile(const PairTile &tl, int qb, int V, con
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const int idx = elem_index(qb, u, k, VEC);
-            const float A = __builtin_fmaf(x[k], pc.e.c, -pc.ot) + pc.delta;
+            const float A = __builtin_fmaf(x[k], pc.e.c, pc.nad);
             const float B = __builtin_fmaf(y[k], pc.e.c, -pc.od);
             const bool mem = TOP && y[k] >= pc.z4 && top_has(pc.top, idx);
             if (mem) {  // replace the unweighted term summed above by the weighted one
@@ -189,7 +189,7 @@ __device__ __forceinline__ void pair_tile(const PairTile &tl, int qb, int V, con
         Elt<DT>::unpack(tl.d[u], y);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float A = __builtin_fmaf(x[k], pc.e.c, -pc.ot) + pc.delta;
+            const float A = __builtin_fmaf(x[k], pc.e.c, pc.nad);
             if (!(A != -INFINITY && A >= lf)) continue;
             const int idx = elem_index(qb, u, k, VEC);
             const float B = __builtin_fmaf(y[k], pc.e.c, -pc.od);
@@ -340,7 +340,7 @@ __device__ __forceinline__ void outcome_position(const OutArgs &o, const char *t
         pc.e = e;
         pc.ot = row_offset(mt, e);
         pc.od = row_offset(md, e);
-        pc.delta = (float)(log2(D) - log2(St));
+        pc.nad = (float)((log2(D) - log2(St)) - (double)pc.ot);
         pc.lbeta = (float)a.log2_beta;
         pc.top = ps.top;
         pc.z4 = TOP ? pc.top.v[3] : INFINITY;
