@@ -180,10 +180,12 @@ __device__ __forceinline__ ResidualScale make_residual_scale(const SeqState &st,
     return r;
 }
 
-// 1 - 2^d for d < 0, to ~2e-7 relative: -d * P(d) on [-1, 0), with P a
-// degree-5 fit of (2^d - 1)/d on that interval (fit error 1e-8, fp32 Horner
-// rounding ~1e-7), and 1 - exp2(d) below -1, where 2^d <= 1/2 keeps the
-// subtraction well conditioned.  d >= 0 gives a value <= 0 (callers clamp).
+// 1 - 2^d for d < 0, to ~2e-7 relative, clamped to [0, 1]: -d * P(d) on
+// [-1, 0), with P a degree-5 fit of (2^d - 1)/d on that interval (fit error
+// 1e-8, fp32 Horner rounding ~1e-7), and 1 - exp2(d) below -1, where
+// 2^d <= 1/2 keeps the subtraction well conditioned.  d >= 0, and the NaN of
+// a token masked in both rows, give 0: the clamp is the output modifier of
+// the two producing operations (NaN clamps to 0).
 __device__ __forceinline__ float one_minus_exp2(float d)
 {
     float p = __builtin_fmaf(d, 1.145800052e-04f, 1.290776301e-03f);
@@ -191,14 +193,13 @@ __device__ __forceinline__ float one_minus_exp2(float d)
     p = __builtin_fmaf(d, p, 5.549895018e-02f);
     p = __builtin_fmaf(d, p, 2.402260602e-01f);
     p = __builtin_fmaf(d, p, 6.931471825e-01f);
-    const float poly = -d * p;
-    const float direct = 1.f - __builtin_amdgcn_exp2f(d);
+    const float poly = __builtin_amdgcn_fmed3f(-d * p, 0.f, 1.f);
+    const float direct = __builtin_amdgcn_fmed3f(1.f - __builtin_amdgcn_exp2f(d), 0.f, 1.f);
     return d >= -1.f ? poly : direct;
 }
 
 // MODE 1: max(p_t - q', 0) * S_t with the offset (k_hi, k_lo) of the token's
-// draft weight; MODE 2: p_t * S_t.  The clamp is fmaxf, which returns 0 for
-// the NaN of a token masked in both rows (p_t = 0 there).
+// draft weight; MODE 2: p_t * S_t.
 template <int MODE>
 __device__ __forceinline__ float residual_at(float zt, float zd, const SeqState &st, const ExpScale &e,
                                              const ResidualScale &rs, float khi, float klo)
@@ -207,7 +208,7 @@ __device__ __forceinline__ float residual_at(float zt, float zd, const SeqState 
     if (MODE == 2) return pt;
     const float delta = zd - zt;
     const float d = __builtin_fmaf(delta, rs.c, khi) + klo;
-    return pt * fmaxf(one_minus_exp2(d), 0.f);  // q' >= p_t: no mass
+    return pt * one_minus_exp2(d);  // q' >= p_t: no mass
 }
 
 }  // namespace sv

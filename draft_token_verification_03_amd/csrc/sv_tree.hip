@@ -70,7 +70,7 @@ __device__ __forceinline__ float law_mass(float zt, float zd, const Law &w)
     const float pt = exp_scaled(zt, w.ot, w.e);
     if (MODE == kLawTarget) return pt;
     const float d = __builtin_fmaf(zd - zt, w.e.c, w.k_hi) + w.k_lo;
-    return pt * fmaxf(one_minus_exp2(d), 0.f);  // q A >= p (or a NaN of masked tokens): no mass
+    return pt * one_minus_exp2(d);  // q A >= p (or a NaN of masked tokens): no mass
 }
 
 __device__ __forceinline__ void law_kappa(Law &w, double kappa)
