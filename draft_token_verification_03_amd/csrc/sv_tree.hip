@@ -31,14 +31,15 @@
 
 namespace sv {
 
-// One workgroup streams a sequence's rows on its own: 1024 threads (four
-// waves per SIMD to hide each other's latencies) with two tiles of one
-// vector of each row in flight per thread.  Two vectors a row per tile need
-// more than the 128 registers a thread of a 1024-thread group has, and the
-// spills cost more than the extra loads gain.
-constexpr int kTreeBlock = 1024;
+// One workgroup streams a sequence's rows on its own, so its rate is set by
+// the bytes it has in flight.  512 threads (two waves per SIMD, up to 256
+// registers a thread: the walk's decision and law state fit without spills,
+// which a 1024-thread group's 128 registers do not) each take two vectors of
+// each row per tile, and aligned rows stream through an LDS ring three tiles
+// deep (below), ~96 KB of both rows in flight per workgroup.
+constexpr int kTreeBlock = 512;
 constexpr int kTreeWaves = kTreeBlock / 64;
-constexpr int kTreeLoads = 1;
+constexpr int kTreeLoads = 2;
 using TreeTile = PairTileU<kTreeLoads>;
 static_assert(kTreeBlock * kTreeLoads == kTreeStepVecs, "tile step of the tree walk");
 
@@ -99,17 +100,94 @@ __device__ __forceinline__ float law_vec(uint4 rt, uint4 rd, const Law &w, float
     return s[0];
 }
 
-// A whole-row pass of the workgroup, with the row pair's alignment as a
-// template parameter of the streaming.
+// Aligned rows stream through a ring in LDS: each wave owns kRingStages
+// stages of kTreeLoads 16-byte vectors per lane of the target row and of the
+// draft row, filled by gfx950's 16-byte global-to-LDS loads, so that a
+// thread has kRingStages - 1 tiles of both rows in flight without holding
+// them in registers (register tiles reach two in flight).  The loads of a
+// wave complete in order, so waiting until at most (kRingStages - 1) tiles'
+// loads are outstanding leaves the oldest stage complete; the wave then reads
+// its stage back, the only reader of its own stages, so no barrier is needed.
+// The compiler's own wait before an LDS read of a global-to-LDS target is
+// for every outstanding load, which would drain the ring each tile, so the
+// ring is read by an assembly read that waits for itself, and the tile waits
+// are explicit.  Past the row's last tile the loads repeat that tile's
+// (in-bounds) addresses, which keeps the outstanding count the same on every
+// tile; every load has landed before the pass returns.
+constexpr int kRingStages = 4;
+static_assert((kRingStages & (kRingStages - 1)) == 0, "ring stages: a power of two");
+
+struct TreeRing {
+    uint4 v[kTreeWaves][kRingStages][2][kTreeLoads][64];  // [wave][stage][target, draft][u][lane]
+};
+__shared__ TreeRing tree_ring;
+
+template <int N>
+__device__ __forceinline__ void wait_vmem()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// A stage's vectors, read back by the lane that requested them.
+__device__ __forceinline__ void ring_read2(const uint4 *p0, const uint4 *p1, uint4 &a, uint4 &b)
+{
+    const uint32_t a0 = (uint32_t)(uintptr_t)p0, a1 = (uint32_t)(uintptr_t)p1;
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b)
+                 : "v"(a0), "v"(a1)
+                 : "memory");
+}
+
+template <int DT, bool PAIR, class Consume>
+__device__ __forceinline__ void ring_pass(const char *trow, const char *drow, int nvec, int V, Consume &&consume)
+{
+    static_assert(kTreeLoads == 2, "the ring reads two vectors a row per thread and tile");
+    constexpr int kStep = kTreeBlock * kTreeLoads;
+    constexpr int kPerTile = kTreeLoads * (PAIR ? 2 : 1);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nt = (nvec + kStep - 1) / kStep;  // >= 1
+    const int own = wave * 64 + lane;
+    auto issue = [&](int t) {
+        const int st = t & (kRingStages - 1);
+        const int qb = min(t, nt - 1) * kStep + own;
+#pragma unroll
+        for (int u = 0; u < kTreeLoads; ++u) {
+            const int q = min(qb + u * kTreeBlock, nvec - 1);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(trow) + q,
+                                             &tree_ring.v[wave][st][0][u][0], 16, 0, 0);
+            if (PAIR)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(drow) + q,
+                                                 &tree_ring.v[wave][st][1][u][0], 16, 0, 0);
+        }
+    };
+    // the first kRingStages - 1 rounds only fill the ring
+    for (int t = 1 - kRingStages; t < nt; ++t) {
+        issue(t + kRingStages - 1);
+        if (t < 0) continue;
+        wait_vmem<kPerTile * (kRingStages - 1)>();
+        const int st = t & (kRingStages - 1);
+        TreeTile tl;
+        ring_read2(&tree_ring.v[wave][st][0][0][lane], &tree_ring.v[wave][st][0][1][lane], tl.t[0], tl.t[1]);
+        if (PAIR)
+            ring_read2(&tree_ring.v[wave][st][1][0][lane], &tree_ring.v[wave][st][1][1][lane], tl.d[0], tl.d[1]);
+        else
+            tl.d[0] = tl.d[1] = tl.t[0];
+        if (t == nt - 1) fix_pair<DT, PAIR, kTreeBlock>(t * kStep, nvec, V, tl);
+        consume(tl, t * kStep);
+    }
+    wait_vmem<0>();
+}
+
+// A whole-row pass of the workgroup: aligned rows through the LDS ring,
+// others through register tiles with funnel-shifted loads.
 template <int DT, bool PAIR, class Consume>
 __device__ __forceinline__ void row_pass(const char *trow, const char *drow, int nvec, int V, Consume &&consume)
 {
     const bool aligned = ((uintptr_t)trow & 15) == 0 && (!PAIR || ((uintptr_t)drow & 15) == 0);
-    TreeTile ra;
     if (aligned) {
-        issue_pair<DT, true, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra);
-        stream_pair<DT, true, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra, consume);
+        ring_pass<DT, PAIR>(trow, drow, nvec, V, consume);
     } else {
+        TreeTile ra;
         issue_pair<DT, false, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra);
         stream_pair<DT, false, PAIR, kTreeBlock>(trow, drow, 0, nvec, V, ra, consume);
     }
