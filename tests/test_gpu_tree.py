@@ -138,6 +138,24 @@ def test_tiny_and_odd_vocabularies(sv, oracle_mod, dtype, V):
     check(oracle_mod, g, inp, 1)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("tiles", [1, 2, 3, 4])
+def test_aligned_rows_of_few_tiles(sv, oracle_mod, dtype, tiles):
+    """Aligned rows (V a multiple of the 16-byte vector) stream through the
+    walk's LDS ring: rows of one to four tile steps (1024 vectors each), the
+    last one full or holding a single vector, so that the ring's fill loads
+    repeat the last tile's addresses and the final tile's lanes past the row
+    are masked."""
+    vec = 4 if dtype == "fp32" else 8
+    for last in (1024, 1):
+        V = ((tiles - 1) * 1024 + last) * vec
+        w = WORKLOADS["C5" if dtype == "fp32" else "C2"].sized(B=12, V=V, beta=1.0)
+        _say(f"tree aligned rows dtype={dtype} tiles={tiles} V={V}")
+        inp = make_tree_inputs(w, (3, 2, 1), seed=V + tiles, device="cuda")
+        g = run_gpu(sv, inp, seed=3)
+        check(oracle_mod, g, inp, 3)
+
+
 def test_tree_error_paths(sv, oracle_mod):
     w = WORKLOADS["C5"].sized(B=6, V=3001, beta=1.0)
     inp = make_tree_inputs(w, (2, 2), seed=5, device="cuda")
