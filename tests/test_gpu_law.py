@@ -10,6 +10,9 @@ probability sum_v min(p_i, q'_i).  The joint law of (n, y_0..y_n) is the
 product of min(p_j, q'_j)(y_j) over the accepted positions times the clamped
 residual max(p_n - q'_n, 0)(y_n), or p_K(y_K) after K acceptances.
 
+Ragged draft lengths (spec_verify_ragged) are tested the same way, per
+group of sequences with the same K_b.
+
 Each case runs 10^6 sequences of one fixed set of rows in a single call of
 the library (sub-batches of launches), every sequence drafting its own
 tokens from q' on the host and drawing its own Philox streams on the GPU.
@@ -141,3 +144,49 @@ def test_joint_law_of_the_outcome(sv, beta):
         probs[offs[k] + c] = pr
     assert counts.sum() == TRIALS
     assert chi2_pvalue(counts, probs) > 0.01
+
+
+@pytest.mark.parametrize("dtype,beta", [("fp32", 1.0), ("bf16", 0.5)])
+def test_ragged_lengths_follow_the_target_law(sv, dtype, beta):
+    """Per-sequence draft lengths K_b <= K (spec_verify_ragged; a drafter
+    that stops early, "Kangaroo ...", "3. Lossless Speculative
+    Verification"): each sequence verifies its own K_b drafts, so n <= K_b,
+    every reached position i emits a token following p_i, and after K_b
+    acceptances the bonus follows p_{K_b} (target row K_b)."""
+    rng = np.random.default_rng(6100)
+    V, K, T = 9, 3, 0.8
+    tgt, drf = _rows(rng, V, K, spread=1.4, noise=0.8)
+    if dtype == "bf16":
+        traw, draw_ = to_bf16_bits(tgt), to_bf16_bits(drf)
+        tt = torch.from_numpy(traw.view(np.int16)).view(torch.bfloat16)
+        dt = torch.from_numpy(draw_.view(np.int16)).view(torch.bfloat16)
+    else:
+        traw, draw_ = tgt, drf
+        tt, dt = torch.from_numpy(tgt), torch.from_numpy(drf)
+    tz, dz = exact_values(traw), exact_values(draw_)
+    Tq = float(np.float32(T))
+    p = [softmax(tz[i], Tq) for i in range(K + 1)]
+    q = [draft_law(dz[i], Tq, beta) for i in range(K)]
+    kb = rng.integers(0, K + 1, size=TRIALS).astype(np.int32)
+    tokens = np.stack([sample_categorical(rng, q[i], TRIALS) for i in range(K)], axis=1).astype(np.int32)
+    dev = torch.device("cuda:0")
+    target = tt.to(dev).unsqueeze(0).expand(TRIALS, K + 1, V).contiguous()
+    draft = dt.to(dev).unsqueeze(0).expand(TRIALS, K, V).contiguous()
+    temp = torch.full((TRIALS,), Tq, dtype=torch.float32, device=dev)
+    acc, out = sv.spec_verify(target, draft, torch.from_numpy(tokens).to(dev), 77, temp, beta,
+                              draft_len=torch.from_numpy(kb).to(dev))
+    torch.cuda.synchronize()
+    n, out = acc.cpu().numpy(), out.cpu().numpy()
+    assert np.all(n <= kb)
+    for k in range(K + 1):
+        grp = kb == k
+        for i in range(k + 1):
+            reached = grp & (n >= i)
+            y = out[reached, i]
+            assert np.all((y >= 0) & (y < V))
+            assert chi2_pvalue(np.bincount(y, minlength=V), p[i]) > 0.01, (k, i)
+            if i < k:
+                alpha = np.minimum(p[i], q[i]).sum()
+                assert binom_pvalue(int((n[reached] > i).sum()), int(reached.sum()), alpha) > 0.01, (k, i)
+        # slots past the sequence's own drafts stay padding
+        assert np.all(out[grp][:, k + 1:] == -1)
